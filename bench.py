@@ -1,0 +1,273 @@
+"""Benchmark of the row-major GEMM library on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-extra]
+
+One step is one SGEMM of 4096x4096x1024 (fp32) followed by one HGEMM of
+4096x4096x4096 (fp16 inputs, fp32 accumulation and output), alpha = 1 and
+beta = 0, on seeded uniform[-1,1) inputs already resident in HBM.  The value is
+the step's throughput, (2*4096*4096*1024 + 2*4096^3) / step time, in TFLOPS;
+the per-kernel TFLOPS and fraction of the MI355X peak for its dtype are
+reported beside it, with the roofline of the dominant (longest) kernel taken
+from HIP events recorded on the stream the kernels run on.  The CPU oracle is
+timed on a bounded sample of the same workload as a baseline.  The other
+benchmark configurations (SGEMM 512^3, the 1001x777x513 and 1024x1024x512
+SGEMMs, HGEMM 2048^3 and 16 batched 1024^3 HGEMMs with beta = 1) are timed
+after the main run and reported under "extra" (not part of the value).
+
+Prints exactly one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "TFLOPS (2MNK/t) + % of dtype peak: SGEMM 4096x4096x1024, HGEMM 4096^3"
+# MI355X peaks: 256 CUs x 2.4 GHz; fp32 matrix/vector 256 flop/clk/CU, fp16 dense MFMA 4096 flop/clk/CU.
+PEAK_F32_TFLOPS = 157.3
+PEAK_F16_TFLOPS = 2516.6
+PEAK_HBM_GBS = 8000.0
+KERNEL_SOURCES = {
+    "sgemm": "dense_gemm_optimisation_f32_amd/csrc/sgemm_mfma.hip",
+    "hgemm": "dense_gemm_optimisation_f32_amd/csrc/hgemm_mfma.hip",
+}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+
+
+def source_digest(kind: str) -> str:
+    with open(os.path.join(ROOT, KERNEL_SOURCES[kind]), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(kind: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or None
+    when it is missing or was taken on a different version of the kernel source."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))[kind]
+    except (OSError, KeyError, ValueError):
+        return None
+    if rec.get("source_sha") != source_digest(kind) or rec.get("workload") != workload:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    ap.add_argument("--no-extra", action="store_true", help="skip the other configurations")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU-oracle time budget")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: this library has no multi-GPU path "
+              "(--gpus must be 1).", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import dense_gemm_optimisation_f32_amd as dg
+    import seeded_inputs as si
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    dg.load_library()    # raises if the HIP library is not built: there is no fallback
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+
+    def upload(buf):
+        return torch.from_numpy(np.ascontiguousarray(buf)).to(dev)
+
+    # ---- inputs (resident in HBM before timing)
+    Ms, Ns, Ks = 4096, 4096, 1024
+    ps = si.gemm_problem(Ms, Ns, Ks, seed=42, with_c=False)
+    sA, sB = upload(ps["A"]), upload(ps["B"])
+    sC = torch.empty(Ms * Ns, dtype=torch.float32, device=dev)
+    Mh = Nh = Kh = 4096
+    ph = si.gemm_problem(Mh, Nh, Kh, in_dtype=np.float16, seed=42, with_c=False)
+    hA, hB = upload(ph["A"]), upload(ph["B"])
+    hC = torch.empty(Mh * Nh, dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    def sgemm():
+        dg.gemm_f32(Ms, Ns, Ks, 1.0, sA, Ks, sB, Ns, 0.0, sC, Ns, stream)
+
+    def hgemm():
+        dg.gemm_f16_f32acc(Mh, Nh, Kh, 1.0, hA, Kh, hB, Nh, 0.0, hC, Nh, stream)
+
+    for _ in range(args.warmup):
+        sgemm()
+        hgemm()
+    torch.cuda.synchronize()
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        sgemm()
+        ev[i][1].record(stream)
+        hgemm()
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    t_s = [e[0].elapsed_time(e[1]) * 1e-3 for e in ev]
+    t_h = [e[1].elapsed_time(e[2]) * 1e-3 for e in ev]
+    flop_s = 2.0 * Ms * Ns * Ks
+    flop_h = 2.0 * Mh * Nh * Kh
+    step_s = wall / args.steps
+    value = (flop_s + flop_h) / step_s / 1e12
+
+    def kernel_record(name, ts, flop, peak, workload, bytes_alg):
+        avg = statistics.fmean(ts)
+        return {
+            "workload": workload,
+            "avg_ms": avg * 1e3, "median_ms": statistics.median(ts) * 1e3, "min_ms": min(ts) * 1e3,
+            "tflops": flop / avg / 1e12, "peak_tflops": peak, "frac_of_peak": flop / avg / 1e12 / peak,
+            "algorithmic_flop": flop, "algorithmic_bytes": bytes_alg,
+        }
+
+    w_s = "SGEMM fp32 row-major 4096x4096x1024 alpha=1 beta=0"
+    w_h = "HGEMM fp16->fp32 row-major 4096x4096x4096 alpha=1 beta=0"
+    bytes_s = 4 * (Ms * Ks + Ks * Ns + Ms * Ns)
+    bytes_h = 2 * (Mh * Kh + Kh * Nh) + 4 * Mh * Nh
+    per_kernel = {
+        "sgemm": kernel_record("sgemm", t_s, flop_s, PEAK_F32_TFLOPS, w_s, bytes_s),
+        "hgemm": kernel_record("hgemm", t_h, flop_h, PEAK_F16_TFLOPS, w_h, bytes_h),
+    }
+    dom = max(per_kernel, key=lambda k: per_kernel[k]["avg_ms"])
+    dk = per_kernel[dom]
+    roofline = {
+        "kernel": dom, "bound": "mfma", "achieved": dk["tflops"], "peak": dk["peak_tflops"],
+        "unit": "TFLOP/s", "frac": dk["frac_of_peak"], "traffic": measured_traffic(dom, dk["workload"]),
+        "algorithmic_flop_per_launch": dk["algorithmic_flop"],
+    }
+    other = "hgemm" if dom == "sgemm" else "sgemm"
+    ok = per_kernel[other]
+    roofline_other = {
+        "kernel": other, "bound": "mfma", "achieved": ok["tflops"], "peak": ok["peak_tflops"],
+        "unit": "TFLOP/s", "frac": ok["frac_of_peak"], "traffic": measured_traffic(other, ok["workload"]),
+    }
+
+    extra = {} if args.no_extra else run_extra(dg, si, np, torch, dev, stream)
+
+    cpu = None if args.no_cpu else cpu_baseline(si, np, ps, ph, args.cpu_seconds)
+
+    line = {
+        "metric": METRIC, "value": value, "unit": "TFLOPS", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": step_s * 1e3, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32+f16(f32acc)", "data": "synthetic",
+        "config": {"workload": "one SGEMM 4096x4096x1024 (fp32) + one HGEMM 4096^3 (fp16 in, fp32 "
+                               "accumulate/out) per step, row-major, alpha=1 beta=0, seeded uniform[-1,1)",
+                   "parallelism": "single GPU"},
+        "per_kernel": per_kernel,
+        "roofline": roofline,
+        "roofline_other": roofline_other,
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def time_calls(fn, torch, stream, warmup=3, reps=20):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in evs:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    ts = sorted(a.elapsed_time(b) * 1e-3 for a, b in evs)
+    return ts[len(ts) // 2], ts[0]
+
+
+def run_extra(dg, si, np, torch, dev, stream):
+    out = {}
+
+    def up(buf):
+        return torch.from_numpy(np.ascontiguousarray(buf)).to(dev)
+
+    def sg(M, N, K, alpha, beta, name):
+        p = si.gemm_problem(M, N, K, seed=42, with_c=beta != 0)
+        A, B = up(p["A"]), up(p["B"])
+        C = up(p["C"]) if beta != 0 else torch.empty(M * N, dtype=torch.float32, device=dev)
+        med, mn = time_calls(lambda: dg.gemm_f32(M, N, K, alpha, A, K, B, N, beta, C, N, stream), torch, stream)
+        fl = 2.0 * M * N * K
+        out[name] = {"median_ms": med * 1e3, "tflops": fl / med / 1e12, "frac_of_peak": fl / med / 1e12 / PEAK_F32_TFLOPS}
+
+    sg(512, 512, 512, 1.0, 0.0, "sgemm_512^3")
+    sg(1001, 777, 513, 1.5, -0.5, "sgemm_1001x777x513_a1.5_b-0.5")
+    sg(1024, 1024, 512, 1.5, -0.5, "sgemm_1024x1024x512_a1.5_b-0.5")
+    for n in (1024, 2048, 8192):
+        sg(n, n, 1024, 1.0, 0.0, f"sgemm_{n}x{n}x1024")
+
+    p = si.gemm_problem(2048, 2048, 2048, in_dtype=np.float16, seed=42, with_c=False)
+    A, B = up(p["A"]), up(p["B"])
+    C = torch.empty(2048 * 2048, dtype=torch.float32, device=dev)
+    med, _ = time_calls(lambda: dg.gemm_f16_f32acc(2048, 2048, 2048, 1.0, A, 2048, B, 2048, 0.0, C, 2048, stream),
+                        torch, stream)
+    fl = 2.0 * 2048 ** 3
+    out["hgemm_2048^3"] = {"median_ms": med * 1e3, "tflops": fl / med / 1e12,
+                           "frac_of_peak": fl / med / 1e12 / PEAK_F16_TFLOPS}
+
+    # 16 x 1024^3 batched, beta = 1 (C is read and written: HBM-bound, ridge below the fp16 peak)
+    nb, n = 16, 1024
+    A = torch.empty(nb * n * n, dtype=torch.float16, device=dev).uniform_(-1, 1)
+    B = torch.empty(nb * n * n, dtype=torch.float16, device=dev).uniform_(-1, 1)
+    C = torch.empty(nb * n * n, dtype=torch.float32, device=dev).uniform_(-1, 1)
+    med, _ = time_calls(lambda: dg.gemm_batched_f16_f32acc(n, n, n, 1.0, A, n, n * n, B, n, n * n, 1.0, C, n, n * n,
+                                                           nb, stream), torch, stream)
+    fl = 2.0 * nb * n ** 3
+    bytes_alg = nb * n * n * (2 + 2 + 4 + 4)
+    out["batched_hgemm_16x1024^3_b1"] = {
+        "median_ms": med * 1e3, "tflops": fl / med / 1e12, "frac_of_peak": fl / med / 1e12 / PEAK_F16_TFLOPS,
+        "hbm_roofline_tflops": min(PEAK_F16_TFLOPS, fl / bytes_alg * PEAK_HBM_GBS / 1e3),
+        "warm_buffers": True}
+    return out
+
+
+def cpu_baseline(si, np, ps, ph, budget_s):
+    """The oracle, as it stands, on row blocks of both workloads until the time budget is spent."""
+    import oracle
+
+    threads = oracle.default_threads()
+    flops = 0.0
+    rows_s = rows_h = 0
+    t0 = time.perf_counter()
+    block = 128
+    while time.perf_counter() - t0 < budget_s and (rows_s < 4096 or rows_h < 4096):
+        if rows_s < 4096:
+            rows = np.arange(rows_s, rows_s + block, dtype=np.int32)
+            oracle.gemm_ref(4096, 4096, 1024, 1.0, ps["A"], 1024, ps["B"], 4096, 0.0, None, 4096,
+                            rows=rows, threads=threads)
+            rows_s += block
+            flops += 2.0 * block * 4096 * 1024
+        if rows_h < 4096 and time.perf_counter() - t0 < budget_s:
+            rows = np.arange(rows_h, rows_h + block, dtype=np.int32)
+            oracle.gemm_ref(4096, 4096, 4096, 1.0, ph["A"], 4096, ph["B"], 4096, 0.0, None, 4096,
+                            rows=rows, threads=threads)
+            rows_h += block
+            flops += 2.0 * block * 4096 * 4096
+    dt = time.perf_counter() - t0
+    return {"value": flops / dt / 1e12, "unit": "TFLOPS", "cores": threads, "kind": "oracle",
+            "sample": f"first {rows_s} rows of the SGEMM 4096x4096x1024 and first {rows_h} rows of the "
+                      f"HGEMM 4096^3 (fp64 triple loop), {dt:.1f} s"}
+
+
+if __name__ == "__main__":
+    sys.exit(main())

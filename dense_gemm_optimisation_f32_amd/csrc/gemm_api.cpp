@@ -1,0 +1,132 @@
+// gemm_api.cpp -- the exported C ABI (include/mi355gemm.h): argument checks,
+// the BLAS-style quick returns, and dispatch to the kernel launchers.
+// Argument checks run before any HIP call, so they work on a host with no GPU.
+#include <limits.h>
+#include <stdint.h>
+
+#include "../../include/mi355gemm.h"
+#include "gemm_internal.h"
+
+namespace {
+
+using mi355gemm::GemmProblem;
+
+constexpr int kMaxGridZ = 65535;  // batch members per launch
+
+bool misaligned(const void *p, uintptr_t align)
+{
+    return p != nullptr && (reinterpret_cast<uintptr_t>(p) % align) != 0;
+}
+
+// Overflow-checked (rows-1)*ld + cols, the element extent of a row-major matrix.
+bool extent(long long rows, long long cols, long long ld, long long *out)
+{
+    if (rows == 0 || cols == 0) {
+        *out = 0;
+        return true;
+    }
+    if ((rows - 1) > 0 && ld > (LLONG_MAX - cols) / (rows - 1)) return false;
+    *out = (rows - 1) * ld + cols;
+    return true;
+}
+
+int check(const GemmProblem &p, size_t elem_in)
+{
+    if (p.M < 0 || p.N < 0 || p.K < 0 || p.batch < 0) return GEMM_ERR_SIZE;
+    const long long K1 = p.K > 1 ? p.K : 1, N1 = p.N > 1 ? p.N : 1;
+    if (p.lda < K1 || p.ldb < N1 || p.ldc < N1) return GEMM_ERR_LD;
+    if (p.strideA < 0 || p.strideB < 0 || p.strideC < 0) return GEMM_ERR_LD;
+    long long ea, eb, ec;
+    if (!extent(p.M, p.K, p.lda, &ea) || !extent(p.K, p.N, p.ldb, &eb) || !extent(p.M, p.N, p.ldc, &ec))
+        return GEMM_ERR_SIZE;
+    if (p.batch > 1 && ec > 0 && p.strideC < ec) return GEMM_ERR_LD;
+    if (p.batch > 1) {
+        const long long nb = p.batch - 1;
+        if ((p.strideA > 0 && nb > (LLONG_MAX - ea) / p.strideA) ||
+            (p.strideB > 0 && nb > (LLONG_MAX - eb) / p.strideB) ||
+            (p.strideC > 0 && nb > (LLONG_MAX - ec) / p.strideC))
+            return GEMM_ERR_SIZE;
+    }
+    if (p.M == 0 || p.N == 0 || p.batch == 0) return GEMM_OK;
+    const bool reads_ab = p.K > 0 && p.alpha != 0.f;
+    if (!p.C) return GEMM_ERR_NULL;
+    if (reads_ab && (!p.A || !p.B)) return GEMM_ERR_NULL;
+    if (misaligned(p.C, sizeof(float))) return GEMM_ERR_ALIGN;
+    if (reads_ab && (misaligned(p.A, elem_in) || misaligned(p.B, elem_in))) return GEMM_ERR_ALIGN;
+    return GEMM_OK;
+}
+
+template <class Launch>
+int run(GemmProblem p, size_t elem_in, hipStream_t stream, Launch launch)
+{
+    const int rc = check(p, elem_in);
+    if (rc != GEMM_OK) return rc;
+    if (p.M == 0 || p.N == 0 || p.batch == 0) return GEMM_OK;
+    const bool product = p.K > 0 && p.alpha != 0.f;
+    const int total = p.batch;
+    for (int b0 = 0; b0 < total; b0 += kMaxGridZ) {
+        GemmProblem q = p;
+        q.batch = (total - b0) < kMaxGridZ ? (total - b0) : kMaxGridZ;
+        q.C = p.C + (long long)b0 * p.strideC;
+        if (product) {
+            q.A = static_cast<const char *>(p.A) + (long long)b0 * p.strideA * (long long)elem_in;
+            q.B = static_cast<const char *>(p.B) + (long long)b0 * p.strideB * (long long)elem_in;
+        }
+        const hipError_t e = product ? launch(q, stream) : mi355gemm::launch_scale_c(q, stream);
+        if (e != hipSuccess) return GEMM_ERR_LAUNCH;
+    }
+    return GEMM_OK;
+}
+
+GemmProblem make(int M, int N, int K, float alpha, const void *A, int lda, long long sA, const void *B, int ldb,
+                 long long sB, float beta, float *C, int ldc, long long sC, int batch)
+{
+    GemmProblem p;
+    p.M = M; p.N = N; p.K = K; p.batch = batch;
+    p.alpha = alpha; p.beta = beta;
+    p.A = A; p.lda = lda; p.strideA = sA;
+    p.B = B; p.ldb = ldb; p.strideB = sB;
+    p.C = C; p.ldc = ldc; p.strideC = sC;
+    return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gemm_f32(int M, int N, int K, float alpha, const float *A, int lda, const float *B, int ldb, float beta,
+             float *C, int ldc, hipStream_t stream)
+{
+    return run(make(M, N, K, alpha, A, lda, 0, B, ldb, 0, beta, C, ldc, 0, 1), sizeof(float), stream,
+               mi355gemm::launch_sgemm);
+}
+
+int gemm_f16_f32acc(int M, int N, int K, float alpha, const uint16_t *A, int lda, const uint16_t *B, int ldb,
+                    float beta, float *C, int ldc, hipStream_t stream)
+{
+    return run(make(M, N, K, alpha, A, lda, 0, B, ldb, 0, beta, C, ldc, 0, 1), sizeof(uint16_t), stream,
+               mi355gemm::launch_hgemm);
+}
+
+int gemm_batched_f16_f32acc(int M, int N, int K, float alpha, const uint16_t *A, int lda, long long strideA,
+                            const uint16_t *B, int ldb, long long strideB, float beta, float *C, int ldc,
+                            long long strideC, int batch_count, hipStream_t stream)
+{
+    return run(make(M, N, K, alpha, A, lda, strideA, B, ldb, strideB, beta, C, ldc, strideC, batch_count),
+               sizeof(uint16_t), stream, mi355gemm::launch_hgemm);
+}
+
+const char *gemm_status_string(int status)
+{
+    switch (status) {
+    case GEMM_OK: return "success";
+    case GEMM_ERR_SIZE: return "invalid size: M, N, K or batch_count negative, or an extent overflows";
+    case GEMM_ERR_LD: return "invalid leading dimension or batch stride";
+    case GEMM_ERR_NULL: return "NULL pointer for an operand the call reads or writes";
+    case GEMM_ERR_ALIGN: return "pointer not aligned to its element size";
+    case GEMM_ERR_LAUNCH: return "the HIP runtime refused a kernel launch";
+    default: return "unknown status";
+    }
+}
+
+}  // extern "C"

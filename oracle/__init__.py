@@ -54,10 +54,16 @@ def _load(path: str = LIB):
 
 
 def default_threads() -> int:
+    """Host threads for the oracle: the CPUs this process may run on, capped by
+    OMP_NUM_THREADS when set and by 16 (a GPU host's per-GPU CPU share)."""
     try:
-        return max(1, len(os.sched_getaffinity(0)))
+        n = len(os.sched_getaffinity(0))
     except AttributeError:  # pragma: no cover
-        return max(1, os.cpu_count() or 1)
+        n = os.cpu_count() or 1
+    omp = os.environ.get("OMP_NUM_THREADS", "")
+    if omp.isdigit() and int(omp) > 0:
+        n = min(n, int(omp))
+    return max(1, min(n, 16))
 
 
 def _as_f32(x) -> np.ndarray:

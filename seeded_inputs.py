@@ -83,12 +83,14 @@ def matrix(seed: int, rows: int, cols: int, ld: int | None = None, kind: str = "
 
 def gemm_problem(M: int, N: int, K: int, *, lda: int | None = None, ldb: int | None = None,
                  ldc: int | None = None, in_dtype=np.float32, kind: str = "pm1",
-                 c_kind: str | None = None, seed: int = 42, batch: int = 0) -> dict:
+                 c_kind: str | None = None, seed: int = 42, batch: int = 0,
+                 with_c: bool = True) -> dict:
     """Operands of one GEMM C = alpha*A*B + beta*C (row-major, see :func:`matrix`).
 
     Returns a dict with flat buffers ``A`` (M x K, lda), ``B`` (K x N, ldb) in
     ``in_dtype`` and ``C`` (M x N, ldc, float32), plus the shape and leading
     dimensions.  ``batch`` selects the seed offset of one member of a batch.
+    ``with_c=False`` leaves ``C`` as None (for beta = 0, where C is never read).
     """
     lda = max(K, 1) if lda is None else lda
     ldb = max(N, 1) if ldb is None else ldb
@@ -99,7 +101,7 @@ def gemm_problem(M: int, N: int, K: int, *, lda: int | None = None, ldb: int | N
         "M": M, "N": N, "K": K, "lda": lda, "ldb": ldb, "ldc": ldc,
         "A": matrix(base + 0, M, K, lda, kind, in_dtype),
         "B": matrix(base + 1, K, N, ldb, kind, in_dtype),
-        "C": matrix(base + 2, M, N, ldc, c_kind, np.float32),
+        "C": matrix(base + 2, M, N, ldc, c_kind, np.float32) if with_c else None,
     }
 
 

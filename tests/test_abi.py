@@ -1,0 +1,123 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/mi355gemm.h declares, rejects bad arguments with the documented status
+codes before any HIP call, and treats empty problems as no-ops."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import dense_gemm_optimisation_f32_amd as dg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mi355gemm.h")
+
+OK, ESIZE, ELD, ENULL, EALIGN, ELAUNCH = 0, -1, -2, -3, -4, -5
+FAKE = 0x10000          # a non-NULL, 16-byte aligned address that is never dereferenced
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)) - {"defined"})
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(dg.LIB_PATH):
+        pytest.fail("libmi355gemm.so is not built; run python -m dense_gemm_optimisation_f32_amd.build")
+    return dg.load_library()
+
+
+def test_exports_every_declared_function(lib):
+    names = declared_functions()
+    assert set(names) == set(dg.EXPORTS), names
+    out = subprocess.run(["nm", "-D", "--defined-only", dg.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if l.strip()}
+    for n in names:
+        assert n in exported, f"{n} declared in mi355gemm.h but not exported"
+        assert getattr(lib, n) is not None
+
+
+def test_status_strings(lib):
+    for code in (OK, ESIZE, ELD, ENULL, EALIGN, ELAUNCH):
+        s = dg.status_string(code)
+        assert s and s != "unknown status"
+    assert dg.status_string(12345) == "unknown status"
+
+
+def f32(lib, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc):
+    return lib.gemm_f32(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, None)
+
+
+def f16(lib, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc):
+    return lib.gemm_f16_f32acc(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, None)
+
+
+def bat(lib, M, N, K, alpha, A, lda, sA, B, ldb, sB, beta, C, ldc, sC, nb):
+    return lib.gemm_batched_f16_f32acc(M, N, K, alpha, A, lda, sA, B, ldb, sB, beta, C, ldc, sC, nb, None)
+
+
+@pytest.mark.parametrize("fn", [f32, f16])
+def test_argument_errors(lib, fn):
+    # negative sizes
+    assert fn(lib, -1, 4, 4, 1.0, FAKE, 4, FAKE, 4, 0.0, FAKE, 4) == ESIZE
+    assert fn(lib, 4, -1, 4, 1.0, FAKE, 4, FAKE, 4, 0.0, FAKE, 4) == ESIZE
+    assert fn(lib, 4, 4, -1, 1.0, FAKE, 4, FAKE, 4, 0.0, FAKE, 4) == ESIZE
+    # leading dimensions below the logical width (or below 1)
+    assert fn(lib, 4, 5, 6, 1.0, FAKE, 5, FAKE, 5, 0.0, FAKE, 5) == ELD      # lda < K
+    assert fn(lib, 4, 5, 6, 1.0, FAKE, 6, FAKE, 4, 0.0, FAKE, 5) == ELD      # ldb < N
+    assert fn(lib, 4, 5, 6, 1.0, FAKE, 6, FAKE, 5, 0.0, FAKE, 4) == ELD      # ldc < N
+    assert fn(lib, 4, 5, 0, 1.0, FAKE, 0, FAKE, 5, 0.0, FAKE, 5) == ELD      # lda < 1
+    # NULL operands that would be read or written
+    assert fn(lib, 4, 5, 6, 1.0, None, 6, FAKE, 5, 0.0, FAKE, 5) == ENULL
+    assert fn(lib, 4, 5, 6, 1.0, FAKE, 6, None, 5, 0.0, FAKE, 5) == ENULL
+    assert fn(lib, 4, 5, 6, 1.0, FAKE, 6, FAKE, 5, 0.0, None, 5) == ENULL
+    assert fn(lib, 4, 5, 0, 1.0, None, 1, None, 5, 1.0, None, 5) == ENULL    # K = 0 still writes C
+    # misaligned pointers
+    assert fn(lib, 4, 5, 6, 1.0, FAKE, 6, FAKE, 5, 0.0, FAKE + 2, 5) == EALIGN
+    assert fn(lib, 4, 5, 6, 1.0, FAKE + 1, 6, FAKE, 5, 0.0, FAKE, 5) == EALIGN
+
+
+def test_f32_alignment_is_four_bytes(lib):
+    assert f32(lib, 4, 5, 6, 1.0, FAKE + 2, 6, FAKE, 5, 0.0, FAKE, 5) == EALIGN
+    assert f32(lib, 4, 5, 6, 1.0, FAKE, 6, FAKE + 2, 5, 0.0, FAKE, 5) == EALIGN
+
+
+def test_batched_argument_errors(lib):
+    M, N, K = 4, 5, 6
+    assert bat(lib, M, N, K, 1.0, FAKE, K, M * K, FAKE, N, K * N, 0.0, FAKE, N, M * N, -1) == ESIZE
+    assert bat(lib, M, N, K, 1.0, FAKE, K, -1, FAKE, N, K * N, 0.0, FAKE, N, M * N, 2) == ELD
+    assert bat(lib, M, N, K, 1.0, FAKE, K, M * K, FAKE, N, -1, 0.0, FAKE, N, M * N, 2) == ELD
+    assert bat(lib, M, N, K, 1.0, FAKE, K, M * K, FAKE, N, K * N, 0.0, FAKE, N, -1, 2) == ELD
+    # C members would overlap
+    assert bat(lib, M, N, K, 1.0, FAKE, K, M * K, FAKE, N, K * N, 0.0, FAKE, N, M * N - 1, 2) == ELD
+    # a single member needs no C stride; operand strides may be 0 (shared operand)
+    assert bat(lib, 0, N, K, 1.0, FAKE, K, 0, FAKE, N, 0, 0.0, FAKE, N, 0, 2) == OK
+    # batch extent overflow
+    assert bat(lib, M, N, K, 1.0, FAKE, K, 2**62, FAKE, N, K * N, 0.0, FAKE, N, M * N, 3) == ESIZE
+
+
+def test_empty_problems_are_noops(lib):
+    # No HIP call happens for these, so they succeed without a GPU.
+    for fn in (f32, f16):
+        assert fn(lib, 0, 5, 6, 1.0, None, 6, None, 5, 0.0, None, 5) == OK
+        assert fn(lib, 4, 0, 6, 1.0, None, 6, None, 1, 0.0, None, 1) == OK
+    assert bat(lib, 4, 5, 6, 1.0, None, 6, 0, None, 5, 0, 0.0, None, 5, 0, 0) == OK
+
+
+def test_binding_refuses_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    a = torch.zeros(16, dtype=torch.float32)
+    with pytest.raises(ValueError):
+        dg.gemm_f32(4, 4, 4, 1.0, a, 4, a, 4, 0.0, a, 4, stream=0)
+
+
+def test_binding_reports_status_as_exception():
+    with pytest.raises(dg.GemmError) as e:
+        dg.gemm_f32(-1, 4, 4, 1.0, FAKE, 4, FAKE, 4, 0.0, FAKE, 4, stream=0)
+    assert e.value.status == ESIZE
