@@ -6,31 +6,42 @@
 // owning a grid of MMA tiles, double-buffered shared-memory staging, padding
 // against bank conflicts, and the larger 128x128 block tile), rebuilt for
 // gfx950 rather than translated:
-//   * matrix-core op: v_mfma_f32_32x32x16_f16 (32x32 fp32 block, 16 k per op,
+//   * matrix-core op: v_mfma_f32_32x32x16_f16 (a 32x32 fp32 block, 16 k per op,
 //     8 fp16 values of A and of B per lane);
-//   * workgroup of 4 waves in a 2x2 grid; each wave owns a (BM/2) x (BN/2) tile
-//     = (BM/64) x (BN/64) MFMA blocks whose accumulators stay in registers for
-//     the whole K loop;
-//   * both operands sit in LDS "K-contiguous": A as [m][k], B transposed as
-//     [n][k], so every MFMA operand is one 16-byte LDS read per lane.  B arrives
-//     row-major ([k][n]); each thread loads an 8(k) x 8(n) block with eight
-//     16-byte loads and transposes it in registers before the LDS write;
-//   * LDS rows are 128 bytes (BK = 64 halves = eight 16-byte chunks); the chunk
-//     index is XOR-swizzled with bits of the row index (the MindNotes page's
-//     swizzling idea applied to 16-byte chunks) so that the eight rows a
-//     group of lanes reads or writes land in distinct banks;
+//   * a workgroup of 4 waves in a 2x2 grid; each wave owns a (BM/2) x (BN/2)
+//     tile of (BM/64) x (BN/64) MFMA blocks whose accumulators stay in
+//     registers for the whole K loop;
+//   * A is staged in LDS as [m][k] (K contiguous, 128-byte rows of eight
+//     16-byte chunks whose chunk index is XOR-swizzled with bits of the row --
+//     the MindNotes page's swizzling idea applied to 16-byte chunks), so an A
+//     operand is one 16-byte LDS read per lane;
+//   * B is staged in LDS in its own row-major [k][n] layout (rows padded so the
+//     four rows a transposed read touches fall in different banks -- the
+//     dandandamowang page's padding).  The K-packed B operand is assembled by
+//     two ds_read_b64_tr_b16 transposed LDS reads: within each 16-lane group,
+//     lane i receives element i%4 of the four-element vectors addressed by
+//     lanes i/4, i/4+4, i/4+8 and i/4+12, so lanes pointing at four
+//     consecutive n of rows k..k+3 hand each lane one column's four k values;
 //   * LDS is double-buffered with one barrier per K step; the next step's
-//     global loads are issued before the current step's MFMAs;
-//   * epilogue C = alpha*acc + beta*C with per-element masks; out-of-range A/B
-//     elements are loaded as zero, so any M, N, K and leading dimension work.
+//     global loads are issued before the current step's MFMAs and written to
+//     the other buffer after them;
+//   * workgroups are mapped to tiles so that the tiles one XCD (one L2) runs
+//     form a compact block of C;
+//   * epilogue C = alpha*acc + beta*C (C not read when beta == 0).
+// Two instantiations per tile shape: MASK = false for problems made of whole
+// tiles with 16-byte aligned rows (no bounds checks anywhere), MASK = true for
+// everything else (out-of-range elements load as zero, stores are masked).
 #include "gemm_internal.h"
+#include "tile_order.h"
 
 namespace mi355gemm {
 namespace {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef short short4v __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) short4v lds_short4;
 
 struct HgemmArgs {
     int M, N, K;
@@ -49,29 +60,23 @@ struct HgCfg {
     static constexpr int BM = BM_, BN = BN_, BK = 64, WM = 2, WN = 2, NT = 256;
     static constexpr int TM = BM / WM, TN = BN / WN;
     static constexpr int FM = TM / 32, FN = TN / 32;
-    static constexpr int CPR = BK / 8;                         // 16-byte chunks per LDS row
-    static constexpr int A_CHUNKS = BM * CPR;                  // chunks in an A tile
-    static constexpr int A_LOADS = A_CHUNKS / NT;
-    static constexpr int B_BLOCKS = (BK / 8) * (BN / 8);       // 8x8 blocks in a B tile
-    static constexpr int B_LOADS = (B_BLOCKS + NT - 1) / NT;
-    static constexpr int LDS_CHUNKS = (BM + BN) * CPR;         // per buffer
-    static_assert(A_CHUNKS % NT == 0, "A tile loads must split evenly");
+    static constexpr int CPR = BK / 8;                 // 16-byte chunks per A row
+    static constexpr int LDB = BN + 32;                // B row pitch in halves (64-byte pad)
+    static constexpr int A_HALVES = BM * BK;
+    static constexpr int B_HALVES = BK * LDB;
+    static constexpr int BUF_HALVES = A_HALVES + B_HALVES;
+    static constexpr int A_LOADS = BM * CPR / NT;      // 16-byte A chunks per thread
+    static constexpr int B_LOADS = BK * (BN / 8) / NT; // 16-byte B chunks per thread
+    static_assert(BM * CPR % NT == 0 && BK * (BN / 8) % NT == 0, "tile loads must split evenly");
     static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be whole MFMA blocks");
 };
 
-// Chunk swizzle: rows r..r+7 (aligned to 8) get distinct chunks for a fixed
-// logical chunk, and so do rows 8 apart.
 __device__ __forceinline__ int swz(int row, int chunk)
 {
     return chunk ^ ((row ^ (row >> 3)) & 7);
 }
 
-__device__ __forceinline__ u32x4 load16(const uint16_t *p)
-{
-    return *reinterpret_cast<const u32x4 *>(p);
-}
-
-// Eight fp16 values at p[0..7] (elements at or beyond `valid` read as zero).
+// Eight fp16 values at p[0..7]; elements at or beyond `valid` read as zero.
 __device__ __forceinline__ u32x4 load8_masked(const uint16_t *p, int valid)
 {
     uint16_t h[8];
@@ -85,24 +90,23 @@ __device__ __forceinline__ u32x4 load8_masked(const uint16_t *p, int valid)
     return v;
 }
 
-template <class Cfg, bool VEC>
+template <class Cfg, bool MASK, bool VEC>
 __global__ __launch_bounds__(256) void hgemm_mfma_kernel(HgemmArgs p)
 {
-    constexpr int BM = Cfg::BM, BK = Cfg::BK, CPR = Cfg::CPR;
-    __shared__ u32x4 lds[2 * Cfg::LDS_CHUNKS];
+    constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, CPR = Cfg::CPR, LDB = Cfg::LDB;
+    __shared__ __attribute__((aligned(16))) uint16_t lds[2 * Cfg::BUF_HALVES];
 
     const int tid = threadIdx.x;
-    const int tile = blockIdx.x;
-    const int tm = tile / p.tiles_n, tn = tile - tm * p.tiles_n;
-    const long long m0 = (long long)tm * BM, n0 = (long long)tn * Cfg::BN;
+    int tm, tn;
+    tile_coords(blockIdx.x, p.tiles_m, p.tiles_n, &tm, &tn);
+    const long long m0 = (long long)tm * BM, n0 = (long long)tn * BN;
     const int M = p.M, N = p.N, K = p.K;
     const uint16_t *A = p.A + (long long)blockIdx.z * p.sA;
     const uint16_t *B = p.B + (long long)blockIdx.z * p.sB;
     float *C = p.C + (long long)blockIdx.z * p.sC;
     const long long lda = p.lda, ldb = p.ldb, ldc = p.ldc;
 
-    u32x4 ra[Cfg::A_LOADS];
-    u32x4 rb[Cfg::B_LOADS][8];
+    u32x4 ra[Cfg::A_LOADS], rb[Cfg::B_LOADS];
 
     auto load_tiles = [&](int k0) {
 #pragma unroll
@@ -112,74 +116,67 @@ __global__ __launch_bounds__(256) void hgemm_mfma_kernel(HgemmArgs p)
             const long long gm = m0 + row;
             const int gk = k0 + kc;
             const uint16_t *src = A + gm * lda + gk;
-            if (gm >= M || gk >= K)
+            if (!MASK) {
+                ra[i] = *reinterpret_cast<const u32x4 *>(src);
+            } else if (gm >= M || gk >= K) {
                 ra[i] = u32x4{0u, 0u, 0u, 0u};
-            else if (VEC && gk + 8 <= K)
-                ra[i] = load16(src);
-            else
+            } else if (VEC && gk + 8 <= K) {
+                ra[i] = *reinterpret_cast<const u32x4 *>(src);
+            } else {
                 ra[i] = load8_masked(src, K - gk);
+            }
         }
 #pragma unroll
         for (int i = 0; i < Cfg::B_LOADS; ++i) {
             const int id = i * Cfg::NT + tid;
-            const int kb = id / (Cfg::BN / 8), nb = id % (Cfg::BN / 8);
-            const long long gn = n0 + nb * 8;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int gk = k0 + kb * 8 + e;
-                const uint16_t *src = B + (long long)gk * ldb + gn;
-                if (id >= Cfg::B_BLOCKS || gk >= K || gn >= N)
-                    rb[i][e] = u32x4{0u, 0u, 0u, 0u};
-                else if (VEC && gn + 8 <= N)
-                    rb[i][e] = load16(src);
-                else
-                    rb[i][e] = load8_masked(src, (int)(N - gn));
+            const int kr = id / (BN / 8), nc = (id % (BN / 8)) * 8;
+            const int gk = k0 + kr;
+            const long long gn = n0 + nc;
+            const uint16_t *src = B + (long long)gk * ldb + gn;
+            if (!MASK) {
+                rb[i] = *reinterpret_cast<const u32x4 *>(src);
+            } else if (gk >= K || gn >= N) {
+                rb[i] = u32x4{0u, 0u, 0u, 0u};
+            } else if (VEC && gn + 8 <= N) {
+                rb[i] = *reinterpret_cast<const u32x4 *>(src);
+            } else {
+                rb[i] = load8_masked(src, (int)(N - gn));
             }
         }
     };
 
     auto store_tiles = [&](int buf) {
-        u32x4 *la = lds + buf * Cfg::LDS_CHUNKS;
-        u32x4 *lb = la + BM * CPR;
+        uint16_t *la = lds + buf * Cfg::BUF_HALVES;
+        uint16_t *lb = la + Cfg::A_HALVES;
 #pragma unroll
         for (int i = 0; i < Cfg::A_LOADS; ++i) {
             const int id = i * Cfg::NT + tid;
             const int row = id / CPR, c = id % CPR;
-            la[row * CPR + swz(row, c)] = ra[i];
+            *reinterpret_cast<u32x4 *>(la + row * BK + 8 * swz(row, c)) = ra[i];
         }
 #pragma unroll
         for (int i = 0; i < Cfg::B_LOADS; ++i) {
             const int id = i * Cfg::NT + tid;
-            if (id >= Cfg::B_BLOCKS) continue;
-            const int kb = id / (Cfg::BN / 8), nb = id % (Cfg::BN / 8);
-            // rb[i][e] holds B[kb*8+e][nb*8 .. nb*8+7] as 4 dwords of 2 halves.
-            // Column n = nb*8 + j becomes one chunk: halves k = kb*8 .. kb*8+7.
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                u32x4 w;
-#pragma unroll
-                for (int d = 0; d < 4; ++d) {
-                    const unsigned lo = rb[i][2 * d][j >> 1];
-                    const unsigned hi = rb[i][2 * d + 1][j >> 1];
-                    w[d] = (j & 1) ? ((lo >> 16) | (hi & 0xFFFF0000u)) : ((lo & 0xFFFFu) | (hi << 16));
-                }
-                const int n = nb * 8 + j;
-                lb[n * CPR + swz(n, kb)] = w;
-            }
+            const int kr = id / (BN / 8), nc = (id % (BN / 8)) * 8;
+            *reinterpret_cast<u32x4 *>(lb + kr * LDB + nc) = rb[i];
         }
     };
 
     const int wave = tid >> 6, lane = tid & 63;
     const int wm = wave / Cfg::WN, wn = wave % Cfg::WN;
     const int lr = lane & 31, lk = lane >> 5;
+    // transposed-read lane roles: group q of 16 lanes, lane j within it
+    const int q = lane >> 4, j = lane & 15;
+    const int tr_row = 8 * (q >> 1) + (j >> 2);                         // + 16*s + 4*h
+    const int tr_col = wn * Cfg::TN + 16 * (q & 1) + 4 * (j & 3);        // + 32*bn
 
     f32x16 acc[Cfg::FM][Cfg::FN];
 #pragma unroll
     for (int i = 0; i < Cfg::FM; ++i)
 #pragma unroll
-        for (int j = 0; j < Cfg::FN; ++j)
+        for (int jj = 0; jj < Cfg::FN; ++jj)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+            for (int r = 0; r < 16; ++r) acc[i][jj][r] = 0.f;
 
     const int nk = (K + BK - 1) / BK;
     load_tiles(0);
@@ -189,27 +186,30 @@ __global__ __launch_bounds__(256) void hgemm_mfma_kernel(HgemmArgs p)
     for (int t = 0; t < nk; ++t) {
         const int buf = t & 1;
         if (t + 1 < nk) load_tiles((t + 1) * BK);
-        const u32x4 *la = lds + buf * Cfg::LDS_CHUNKS;
-        const u32x4 *lb = la + BM * CPR;
+        const uint16_t *la = lds + buf * Cfg::BUF_HALVES;
+        const uint16_t *lb = la + Cfg::A_HALVES;
 #pragma unroll
         for (int s = 0; s < BK / 16; ++s) {
-            const int c = 2 * s + lk;   // logical chunk: halves 16s + 8*lk .. +7
+            const int c = 2 * s + lk;   // A chunk: halves 16s + 8*lk .. +7
             half8 a[Cfg::FM], b[Cfg::FN];
 #pragma unroll
             for (int i = 0; i < Cfg::FM; ++i) {
                 const int row = wm * Cfg::TM + 32 * i + lr;
-                a[i] = __builtin_bit_cast(half8, la[row * CPR + swz(row, c)]);
+                a[i] = *reinterpret_cast<const half8 *>(la + row * BK + 8 * swz(row, c));
             }
 #pragma unroll
-            for (int j = 0; j < Cfg::FN; ++j) {
-                const int n = wn * Cfg::TN + 32 * j + lr;
-                b[j] = __builtin_bit_cast(half8, lb[n * CPR + swz(n, c)]);
+            for (int jj = 0; jj < Cfg::FN; ++jj) {
+                const uint16_t *base = lb + (16 * s + tr_row) * LDB + tr_col + 32 * jj;
+                const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4 *)(base));
+                const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4 *)(base + 4 * LDB));
+                const short4v both[2] = {lo, hi};
+                b[jj] = __builtin_bit_cast(half8, both);
             }
 #pragma unroll
             for (int i = 0; i < Cfg::FM; ++i)
 #pragma unroll
-                for (int j = 0; j < Cfg::FN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], acc[i][j], 0, 0, 0);
+                for (int jj = 0; jj < Cfg::FN; ++jj)
+                    acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[jj], acc[i][jj], 0, 0, 0);
         }
         if (t + 1 < nk) store_tiles(buf ^ 1);
         __syncthreads();
@@ -221,14 +221,14 @@ __global__ __launch_bounds__(256) void hgemm_mfma_kernel(HgemmArgs p)
 #pragma unroll
     for (int i = 0; i < Cfg::FM; ++i) {
 #pragma unroll
-        for (int j = 0; j < Cfg::FN; ++j) {
-            const long long col = n0 + wn * Cfg::TN + 32 * j + lr;
+        for (int jj = 0; jj < Cfg::FN; ++jj) {
+            const long long col = n0 + wn * Cfg::TN + 32 * jj + lr;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const long long row = m0 + wm * Cfg::TM + 32 * i + 8 * (r >> 2) + 4 * lk + (r & 3);
-                if (row < M && col < N) {
+                if (!MASK || (row < M && col < N)) {
                     float *dst = C + row * ldc + col;
-                    float v = alpha * acc[i][j][r];
+                    float v = alpha * acc[i][jj][r];
                     if (beta != 0.f) v += beta * *dst;
                     *dst = v;
                 }
@@ -255,12 +255,15 @@ hipError_t launch_cfg(const GemmProblem &q, hipStream_t stream)
                      (reinterpret_cast<uintptr_t>(q.A) % 16 == 0) &&
                      (reinterpret_cast<uintptr_t>(q.B) % 16 == 0) &&
                      (q.strideA % 8 == 0) && (q.strideB % 8 == 0);
+    const bool whole = vec && q.M % Cfg::BM == 0 && q.N % Cfg::BN == 0 && q.K % Cfg::BK == 0;
     dim3 grid(a.tiles_m * a.tiles_n, 1, q.batch);
     dim3 block(Cfg::NT);
-    if (vec)
-        hipLaunchKernelGGL((hgemm_mfma_kernel<Cfg, true>), grid, block, 0, stream, a);
+    if (whole)
+        hipLaunchKernelGGL((hgemm_mfma_kernel<Cfg, false, true>), grid, block, 0, stream, a);
+    else if (vec)
+        hipLaunchKernelGGL((hgemm_mfma_kernel<Cfg, true, true>), grid, block, 0, stream, a);
     else
-        hipLaunchKernelGGL((hgemm_mfma_kernel<Cfg, false>), grid, block, 0, stream, a);
+        hipLaunchKernelGGL((hgemm_mfma_kernel<Cfg, true, false>), grid, block, 0, stream, a);
     return hipGetLastError();
 }
 

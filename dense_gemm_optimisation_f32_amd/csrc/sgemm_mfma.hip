@@ -21,7 +21,11 @@
 //     out-of-range A/B elements are loaded as zero.
 // Why MFMA and not VALU: fp32 VALU FMA without the packed form reaches half of
 // the chip's fp32 rate; the fp32 MFMA path has the full rate.
+// Two instantiations per tile shape: MASK = false for problems made of whole
+// tiles with 16-byte aligned rows (no bounds checks anywhere), MASK = true for
+// everything else.  Workgroups are mapped to tiles XCD by XCD (tile_order.h).
 #include "gemm_internal.h"
+#include "tile_order.h"
 
 namespace mi355gemm {
 namespace {
@@ -59,7 +63,7 @@ struct SgCfg {
     static_assert(BK % 2 == 0, "MFMA consumes k in pairs");
 };
 
-template <class Cfg, bool VEC>
+template <class Cfg, bool MASK, bool VEC>
 __global__ __launch_bounds__(Cfg::NT) void sgemm_mfma_kernel(SgemmArgs p)
 {
     constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK;
@@ -68,8 +72,8 @@ __global__ __launch_bounds__(Cfg::NT) void sgemm_mfma_kernel(SgemmArgs p)
     __shared__ float lds_b[2 * BK * LDB_S];
 
     const int tid = threadIdx.x;
-    const int tile = blockIdx.x;
-    const int tm = tile / p.tiles_n, tn = tile - tm * p.tiles_n;
+    int tm, tn;
+    tile_coords(blockIdx.x, p.tiles_m, p.tiles_n, &tm, &tn);
     const long long m0 = (long long)tm * BM, n0 = (long long)tn * BN;
     const int M = p.M, N = p.N, K = p.K;
     const float *A = p.A + (long long)blockIdx.z * p.sA;
@@ -87,7 +91,7 @@ __global__ __launch_bounds__(Cfg::NT) void sgemm_mfma_kernel(SgemmArgs p)
             const long long gm = m0 + row;
             const int gk = k0 + kc;
             const float *src = A + gm * lda + gk;
-            if (VEC && gm < M && gk + 3 < K) {
+            if (!MASK || (VEC && gm < M && gk + 3 < K)) {
                 ra[i] = *reinterpret_cast<const float4 *>(src);
             } else {
                 const bool rok = gm < M;
@@ -104,7 +108,7 @@ __global__ __launch_bounds__(Cfg::NT) void sgemm_mfma_kernel(SgemmArgs p)
             const int gk = k0 + krow;
             const long long gn = n0 + nc;
             const float *src = B + (long long)gk * ldb + gn;
-            if (VEC && gk < K && gn + 3 < N) {
+            if (!MASK || (VEC && gk < K && gn + 3 < N)) {
                 rb[i] = *reinterpret_cast<const float4 *>(src);
             } else {
                 const bool kok = gk < K;
@@ -187,7 +191,7 @@ __global__ __launch_bounds__(Cfg::NT) void sgemm_mfma_kernel(SgemmArgs p)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const long long row = m0 + wm * Cfg::TM + 32 * i + 8 * (r >> 2) + 4 * lk + (r & 3);
-                if (row < M && col < N) {
+                if (!MASK || (row < M && col < N)) {
                     float *dst = C + row * ldc + col;
                     float v = alpha * acc[i][j][r];
                     if (beta != 0.f) v += beta * *dst;
@@ -215,12 +219,15 @@ hipError_t launch_cfg(const GemmProblem &q, hipStream_t stream)
                      (reinterpret_cast<uintptr_t>(q.A) % 16 == 0) &&
                      (reinterpret_cast<uintptr_t>(q.B) % 16 == 0) &&
                      (q.strideA % 4 == 0) && (q.strideB % 4 == 0);
+    const bool whole = vec && q.M % Cfg::BM == 0 && q.N % Cfg::BN == 0 && q.K % Cfg::BK == 0;
     dim3 grid(a.tiles_m * a.tiles_n, 1, q.batch);
     dim3 block(Cfg::NT);
-    if (vec)
-        hipLaunchKernelGGL((sgemm_mfma_kernel<Cfg, true>), grid, block, 0, stream, a);
+    if (whole)
+        hipLaunchKernelGGL((sgemm_mfma_kernel<Cfg, false, true>), grid, block, 0, stream, a);
+    else if (vec)
+        hipLaunchKernelGGL((sgemm_mfma_kernel<Cfg, true, true>), grid, block, 0, stream, a);
     else
-        hipLaunchKernelGGL((sgemm_mfma_kernel<Cfg, false>), grid, block, 0, stream, a);
+        hipLaunchKernelGGL((sgemm_mfma_kernel<Cfg, true, false>), grid, block, 0, stream, a);
     return hipGetLastError();
 }
 
