@@ -34,6 +34,8 @@
 #include "gemm_internal.h"
 #include "tile_order.h"
 
+#include <type_traits>
+
 namespace mi355gemm {
 namespace {
 
@@ -108,40 +110,52 @@ __global__ __launch_bounds__(256) void hgemm_mfma_kernel(HgemmArgs p)
 
     u32x4 ra[Cfg::A_LOADS], rb[Cfg::B_LOADS];
 
+    // Lane parts of the global addresses (bytes, fixed for the whole K loop);
+    // the rest of each address is uniform across the workgroup and lives in
+    // scalar registers.
+    const unsigned a_lane_off = (unsigned)((tid / CPR) * lda + (tid % CPR) * 8) * 2u;
+    const unsigned b_lane_off = (unsigned)((tid / (BN / 8)) * ldb + (tid % (BN / 8)) * 8) * 2u;
+    constexpr int A_ROWS_PER_LOAD = Cfg::NT / CPR;       // rows covered by one load of all threads
+    constexpr int B_ROWS_PER_LOAD = Cfg::NT / (BN / 8);
+
     auto load_tiles = [&](int k0) {
 #pragma unroll
         for (int i = 0; i < Cfg::A_LOADS; ++i) {
+            if (!MASK) {
+                const char *base = reinterpret_cast<const char *>(A + (m0 + i * A_ROWS_PER_LOAD) * lda + k0);
+                ra[i] = *reinterpret_cast<const u32x4 *>(base + a_lane_off);
+                continue;
+            }
             const int id = i * Cfg::NT + tid;
             const int row = id / CPR, kc = (id % CPR) * 8;
             const long long gm = m0 + row;
             const int gk = k0 + kc;
             const uint16_t *src = A + gm * lda + gk;
-            if (!MASK) {
-                ra[i] = *reinterpret_cast<const u32x4 *>(src);
-            } else if (gm >= M || gk >= K) {
+            if (gm >= M || gk >= K)
                 ra[i] = u32x4{0u, 0u, 0u, 0u};
-            } else if (VEC && gk + 8 <= K) {
+            else if (VEC && gk + 8 <= K)
                 ra[i] = *reinterpret_cast<const u32x4 *>(src);
-            } else {
+            else
                 ra[i] = load8_masked(src, K - gk);
-            }
         }
 #pragma unroll
         for (int i = 0; i < Cfg::B_LOADS; ++i) {
+            if (!MASK) {
+                const char *base = reinterpret_cast<const char *>(B + (long long)(k0 + i * B_ROWS_PER_LOAD) * ldb + n0);
+                rb[i] = *reinterpret_cast<const u32x4 *>(base + b_lane_off);
+                continue;
+            }
             const int id = i * Cfg::NT + tid;
             const int kr = id / (BN / 8), nc = (id % (BN / 8)) * 8;
             const int gk = k0 + kr;
             const long long gn = n0 + nc;
             const uint16_t *src = B + (long long)gk * ldb + gn;
-            if (!MASK) {
-                rb[i] = *reinterpret_cast<const u32x4 *>(src);
-            } else if (gk >= K || gn >= N) {
+            if (gk >= K || gn >= N)
                 rb[i] = u32x4{0u, 0u, 0u, 0u};
-            } else if (VEC && gn + 8 <= N) {
+            else if (VEC && gn + 8 <= N)
                 rb[i] = *reinterpret_cast<const u32x4 *>(src);
-            } else {
+            else
                 rb[i] = load8_masked(src, (int)(N - gn));
-            }
         }
     };
 
@@ -178,63 +192,326 @@ __global__ __launch_bounds__(256) void hgemm_mfma_kernel(HgemmArgs p)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][jj][r] = 0.f;
 
-    const int nk = (K + BK - 1) / BK;
-    load_tiles(0);
-    store_tiles(0);
-    __syncthreads();
-
-    for (int t = 0; t < nk; ++t) {
-        const int buf = t & 1;
-        if (t + 1 < nk) load_tiles((t + 1) * BK);
+    // Operand fragments of one 16-wide k substep, double-buffered in registers:
+    // the fragments of substep s+1 are read from LDS while the MFMAs of
+    // substep s run.
+    half8 fa[2][Cfg::FM], fb[2][Cfg::FN];
+    auto read_frags = [&](int buf, int s, half8 *a, half8 *b) {
         const uint16_t *la = lds + buf * Cfg::BUF_HALVES;
         const uint16_t *lb = la + Cfg::A_HALVES;
+        const int c = 2 * s + lk;   // A chunk: halves 16s + 8*lk .. +7
 #pragma unroll
-        for (int s = 0; s < BK / 16; ++s) {
-            const int c = 2 * s + lk;   // A chunk: halves 16s + 8*lk .. +7
-            half8 a[Cfg::FM], b[Cfg::FN];
-#pragma unroll
-            for (int i = 0; i < Cfg::FM; ++i) {
-                const int row = wm * Cfg::TM + 32 * i + lr;
-                a[i] = *reinterpret_cast<const half8 *>(la + row * BK + 8 * swz(row, c));
-            }
-#pragma unroll
-            for (int jj = 0; jj < Cfg::FN; ++jj) {
-                const uint16_t *base = lb + (16 * s + tr_row) * LDB + tr_col + 32 * jj;
-                const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4 *)(base));
-                const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4 *)(base + 4 * LDB));
-                const short4v both[2] = {lo, hi};
-                b[jj] = __builtin_bit_cast(half8, both);
-            }
-#pragma unroll
-            for (int i = 0; i < Cfg::FM; ++i)
-#pragma unroll
-                for (int jj = 0; jj < Cfg::FN; ++jj)
-                    acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[jj], acc[i][jj], 0, 0, 0);
+        for (int i = 0; i < Cfg::FM; ++i) {
+            const int row = wm * Cfg::TM + 32 * i + lr;
+            a[i] = *reinterpret_cast<const half8 *>(la + row * BK + 8 * swz(row, c));
         }
-        if (t + 1 < nk) store_tiles(buf ^ 1);
-        __syncthreads();
+#pragma unroll
+        for (int jj = 0; jj < Cfg::FN; ++jj) {
+            const uint16_t *base = lb + (16 * s + tr_row) * LDB + tr_col + 32 * jj;
+            const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4 *)(base));
+            const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4 *)(base + 4 * LDB));
+            const short4v both[2] = {lo, hi};
+            b[jj] = __builtin_bit_cast(half8, both);
+        }
+    };
+    auto mfmas = [&](const half8 *a, const half8 *b) {
+#pragma unroll
+        for (int i = 0; i < Cfg::FM; ++i)
+#pragma unroll
+            for (int jj = 0; jj < Cfg::FN; ++jj)
+                acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[jj], acc[i][jj], 0, 0, 0);
+    };
+
+    constexpr int NS = BK / 16;   // k substeps per K step
+    const int nk = (K + BK - 1) / BK;
+    // Prologue: tile 0 into LDS buffer 0, tile 1 on its way into registers,
+    // fragments of substep 0 in registers.
+    load_tiles(0);
+    store_tiles(0);
+    if (nk > 1) load_tiles(BK);
+    __syncthreads();
+    read_frags(0, 0, fa[0], fb[0]);
+
+    // Step t computes tile t from LDS buffer t%2.  Registers hold tile t+1;
+    // they are written to the other buffer during step t (that buffer was last
+    // read in step t-1, before its closing barrier) and refilled with tile t+2.
+    for (int t = 0; t < nk; ++t) {
+        const int buf = t & 1;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            const int cur = s & 1, nxt = cur ^ 1;
+            if (s + 1 < NS) {
+                read_frags(buf, s + 1, fa[nxt], fb[nxt]);
+                if (s + 2 == NS && t + 1 < nk) {
+                    store_tiles(buf ^ 1);
+                    if (t + 2 < nk) load_tiles((t + 2) * BK);
+                }
+            } else if (t + 1 < nk) {
+                __syncthreads();
+                read_frags(buf ^ 1, 0, fa[nxt], fb[nxt]);
+            }
+            mfmas(fa[cur], fb[cur]);
+        }
     }
 
     // Epilogue: register r of lane l in a 32x32 block is row 8*(r/4)+4*(l/32)+r%4,
     // column l%32.
     const float alpha = p.alpha, beta = p.beta;
+    auto epilogue = [&](auto with_c) {
 #pragma unroll
-    for (int i = 0; i < Cfg::FM; ++i) {
+        for (int i = 0; i < Cfg::FM; ++i) {
+#pragma unroll
+            for (int jj = 0; jj < Cfg::FN; ++jj) {
+                const long long col = n0 + wn * Cfg::TN + 32 * jj + lr;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const long long row = m0 + wm * Cfg::TM + 32 * i + 8 * (r >> 2) + 4 * lk + (r & 3);
+                    if (!MASK || (row < M && col < N)) {
+                        float *dst = C + row * ldc + col;
+                        float v = alpha * acc[i][jj][r];
+                        if (decltype(with_c)::value) v += beta * *dst;
+                        *dst = v;
+                    }
+                }
+            }
+        }
+    };
+    if (beta != 0.f)
+        epilogue(std::true_type{});
+    else
+        epilogue(std::false_type{});
+}
+
+// ---------------------------------------------------------------------------
+// Whole-tile kernel fed by direct-to-LDS loads.
+//
+// gfx950's global_load_lds_dwordx4 moves 16 bytes per lane from global memory
+// straight into LDS, lane l's bytes landing at M0 + 16*l, with no trip through
+// vector registers and no LDS-write instruction.  That lets the K loop keep a
+// ring of STAGES BK=32 slices in LDS and issue the loads of slice t+STAGES
+// while slice t is computed, hiding global latency behind several slices of
+// MFMA work.  Because a wave's load fills 1 KB of LDS contiguously, the
+// swizzled layouts are produced by choosing, per lane, which global chunk to
+// fetch for the LDS position the lane owns:
+//   * A slice: BM rows of 64 bytes (four 16-byte k chunks); the chunk at
+//     physical position p of row r holds logical chunk p ^ swz_a(r);
+//   * B slice: 32 rows of BN halves (row-major [k][n]); the chunk at physical
+//     position p of row k holds logical chunk p ^ swz_b(k).
+// swz_a keeps the rows that one LDS cycle serves on distinct banks for the
+// 16-byte A operand reads; swz_b does the same for the four rows a
+// transposed B read touches (for both 128- and 256-byte bank windows).
+// Requires M % BM == 0, N % BN == 0, K % 32 == 0, 16-byte aligned rows and
+// byte offsets within a slice below 2^31.
+template <int BM_, int BN_, int STAGES_>
+struct HgDmaCfg {
+    static constexpr int BM = BM_, BN = BN_, BK = 32, STAGES = STAGES_, WM = 2, WN = 2, NT = 256;
+    static constexpr int TM = BM / WM, TN = BN / WN;
+    static constexpr int FM = TM / 32, FN = TN / 32;
+    static constexpr int A_BYTES = BM * BK * 2;                 // one A slice
+    static constexpr int B_BYTES = BK * BN * 2;                 // one B slice
+    static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+    static constexpr int A_LOADS = A_BYTES / 1024 / 4;          // per wave per slice
+    static constexpr int B_LOADS = B_BYTES / 1024 / 4;
+    static constexpr int B_CPR = BN / 8;                        // 16-byte chunks per B row
+    static constexpr int B_RPL = 64 / B_CPR;                    // B rows per wave load
+    static_assert(A_BYTES % 4096 == 0 && B_BYTES % 4096 == 0, "slices must split over 4 waves");
+    static_assert(STAGES * STAGE_BYTES <= 160 * 1024, "LDS ring too large");
+};
+
+__device__ __forceinline__ int swz_a(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+__device__ __forceinline__ int swz_b(int k)
+{
+    // rows k..k+3 of an aligned group of four map to XOR patterns 0, 6, 10, 12
+    return (0xCA60 >> (4 * (k & 3))) & 15;
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) half8 lds_half8;
+
+__device__ __forceinline__ lds_void *lds_ptr(unsigned byte)
+{
+    return (lds_void *)(uintptr_t)byte;
+}
+
+// One direct-to-LDS load: every lane fetches 16 bytes at sbase + voff and the
+// wave's 1 KB lands contiguously at LDS byte lds_addr (lane l at +16*l).  It is
+// issued through inline asm so that the compiler neither reorders LDS accesses
+// around it (memory clobber) nor adds its own conservative vmcnt(0) before
+// every later LDS read: completion is tracked explicitly with wait_vmcnt.
+__device__ __forceinline__ void dma16(const void *sbase, unsigned voff, unsigned lds_addr)
+{
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(voff), "s"(sbase), "s"(lds_addr)
+                 : "memory", "m0");
+}
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <class Cfg>
+__global__ __launch_bounds__(256) void hgemm_dma_kernel(HgemmArgs p)
+{
+    constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, S = Cfg::STAGES;
+    __shared__ __attribute__((aligned(1024))) unsigned char lds[S * Cfg::STAGE_BYTES];
+    const unsigned lds0 = (unsigned)(uintptr_t)lds;
+
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    int tm, tn;
+    tile_coords(blockIdx.x, p.tiles_m, p.tiles_n, &tm, &tn);
+    const long long m0 = (long long)tm * BM, n0 = (long long)tn * BN;
+    const long long lda = p.lda, ldb = p.ldb, ldc = p.ldc;
+    const char *Ab = reinterpret_cast<const char *>(p.A + (long long)blockIdx.z * p.sA + m0 * lda);
+    const char *Bb = reinterpret_cast<const char *>(p.B + (long long)blockIdx.z * p.sB + n0);
+    float *C = p.C + (long long)blockIdx.z * p.sC;
+
+    // Per-lane byte offsets of the chunks this lane fetches (relative to the
+    // slice's first row and, for B, the tile's first column).
+    unsigned offA[Cfg::A_LOADS], offB[Cfg::B_LOADS];
+#pragma unroll
+    for (int i = 0; i < Cfg::A_LOADS; ++i) {
+        const int g = wave * Cfg::A_LOADS + i;
+        const int r = 16 * g + (lane >> 2);
+        offA[i] = (unsigned)(r * lda + 8 * ((lane & 3) ^ swz_a(r))) * 2u;
+    }
+#pragma unroll
+    for (int i = 0; i < Cfg::B_LOADS; ++i) {
+        const int g = wave * Cfg::B_LOADS + i;
+        const int k = Cfg::B_RPL * g + lane / Cfg::B_CPR;
+        offB[i] = (unsigned)(k * ldb + 8 * ((lane % Cfg::B_CPR) ^ swz_b(k))) * 2u;
+    }
+    const int uwave = __builtin_amdgcn_readfirstlane(wave);
+    auto issue_slice = [&](int kt, int slot) {
+        const char *a = Ab + (long long)kt * BK * 2;
+        const char *b = Bb + (long long)kt * BK * ldb * 2;
+        const unsigned la = lds0 + slot * Cfg::STAGE_BYTES + uwave * Cfg::A_LOADS * 1024;
+        const unsigned lb = lds0 + slot * Cfg::STAGE_BYTES + Cfg::A_BYTES + uwave * Cfg::B_LOADS * 1024;
+#pragma unroll
+        for (int i = 0; i < Cfg::A_LOADS; ++i) dma16(a, offA[i], la + 1024 * i);
+#pragma unroll
+        for (int i = 0; i < Cfg::B_LOADS; ++i) dma16(b, offB[i], lb + 1024 * i);
+    };
+    constexpr int LOADS = Cfg::A_LOADS + Cfg::B_LOADS;   // vector-memory ops per slice per lane
+
+    // Fragment read addresses (bytes, without the slot base).
+    const int wm = wave / Cfg::WN, wn = wave % Cfg::WN;
+    const int lr = lane & 31, lk = lane >> 5, q = lane >> 4, j = lane & 15;
+    unsigned fragA[2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+        const int r = wm * Cfg::TM + lr;
+        fragA[s] = (unsigned)(r * BK * 2 + 16 * ((2 * s + lk) ^ swz_a(r)));
+    }
+    unsigned fragB[Cfg::FN];
+    const int kq = 8 * (q >> 1) + (j >> 2);     // row within a 16-row substep (plus 4*h)
+#pragma unroll
+    for (int jj = 0; jj < Cfg::FN; ++jj) {
+        const int n = wn * Cfg::TN + 32 * jj + 16 * (q & 1) + 4 * (j & 3);
+        fragB[jj] = (unsigned)(Cfg::A_BYTES + kq * BN * 2 + 16 * ((n >> 3) ^ swz_b(kq)) + 2 * (n & 7));
+    }
+
+    f32x16 acc[Cfg::FM][Cfg::FN];
+#pragma unroll
+    for (int i = 0; i < Cfg::FM; ++i)
+#pragma unroll
+        for (int jj = 0; jj < Cfg::FN; ++jj)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][jj][r] = 0.f;
+
+    half8 fa[2][Cfg::FM], fb[2][Cfg::FN];
+    auto read_frags = [&](int slot, int s, half8 *a, half8 *b) {
+        const unsigned base = lds0 + slot * Cfg::STAGE_BYTES;
+#pragma unroll
+        for (int i = 0; i < Cfg::FM; ++i)
+            a[i] = *(const lds_half8 *)(uintptr_t)(base + fragA[s] + i * 32 * BK * 2);
 #pragma unroll
         for (int jj = 0; jj < Cfg::FN; ++jj) {
-            const long long col = n0 + wn * Cfg::TN + 32 * jj + lr;
+            const unsigned bb = base + fragB[jj] + 16 * s * BN * 2;
+            const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4 *)(uintptr_t)bb);
+            const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4 *)(uintptr_t)(bb + 4 * BN * 2));
+            const short4v both[2] = {lo, hi};
+            b[jj] = __builtin_bit_cast(half8, both);
+        }
+    };
+    auto mfmas = [&](const half8 *a, const half8 *b) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const long long row = m0 + wm * Cfg::TM + 32 * i + 8 * (r >> 2) + 4 * lk + (r & 3);
-                if (!MASK || (row < M && col < N)) {
+        for (int i = 0; i < Cfg::FM; ++i)
+#pragma unroll
+            for (int jj = 0; jj < Cfg::FN; ++jj)
+                acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[jj], acc[i][jj], 0, 0, 0);
+    };
+    auto lds_barrier = [&]() {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    };
+    // One step on slice t (slot t % S): substep 1 fragments of slice t are read
+    // while substep 0 is computed; then, once slice t+1 is resident for every
+    // wave (this lane's loads counted down to PENDING outstanding slices, then
+    // the barrier) and every wave holds its slice-t fragments, slot t % S may be
+    // refilled with slice t+S, and the substep 0 fragments of slice t+1 are read
+    // while substep 1 of slice t is computed.
+    auto step = [&](int t, auto pending, auto refill) {
+        const int slot = t % S;
+        read_frags(slot, 1, fa[1], fb[1]);
+        mfmas(fa[0], fb[0]);
+        wait_vmcnt<LOADS * decltype(pending)::value>();
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's slice-t reads are done
+        lds_barrier();
+        if (decltype(refill)::value) issue_slice(t + S, slot);
+        read_frags((t + 1) % S, 0, fa[0], fb[0]);
+        mfmas(fa[1], fb[1]);
+    };
+
+    const int nk = p.K / BK;   // >= S (checked by the launcher)
+    // Prologue: slices 0..S-1 in flight; slice 0 resident; substep 0 fragments read.
+#pragma unroll
+    for (int st = 0; st < S; ++st) issue_slice(st, st);
+    wait_vmcnt<LOADS * (S - 1)>();
+    lds_barrier();
+    read_frags(0, 0, fa[0], fb[0]);
+
+    // Steady state: slices up to t+S-1 issued, slice t+1 needed.
+    for (int t = 0; t + S < nk; ++t) step(t, std::integral_constant<int, S - 2>{}, std::true_type{});
+    // Tail: no more slices to issue; the outstanding count drains to zero.
+    const int t0 = nk - S;
+    step(t0 + 0, std::integral_constant<int, S - 2>{}, std::false_type{});
+    step(t0 + 1, std::integral_constant<int, S - 3>{}, std::false_type{});
+    step(t0 + 2, std::integral_constant<int, S - 4>{}, std::false_type{});
+    static_assert(S == 4, "the tail above is written for a four-slice ring");
+    // Last slice: both substeps from registers/LDS already resident.
+    read_frags((nk - 1) % S, 1, fa[1], fb[1]);
+    mfmas(fa[0], fb[0]);
+    mfmas(fa[1], fb[1]);
+
+    const float alpha = p.alpha, beta = p.beta;
+    auto epilogue = [&](auto with_c) {
+#pragma unroll
+        for (int i = 0; i < Cfg::FM; ++i) {
+#pragma unroll
+            for (int jj = 0; jj < Cfg::FN; ++jj) {
+                const long long col = n0 + wn * Cfg::TN + 32 * jj + lr;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const long long row = m0 + wm * Cfg::TM + 32 * i + 8 * (r >> 2) + 4 * lk + (r & 3);
                     float *dst = C + row * ldc + col;
                     float v = alpha * acc[i][jj][r];
-                    if (beta != 0.f) v += beta * *dst;
+                    if (decltype(with_c)::value) v += beta * *dst;
                     *dst = v;
                 }
             }
         }
-    }
+    };
+    if (beta != 0.f)
+        epilogue(std::true_type{});
+    else
+        epilogue(std::false_type{});
 }
 
 using Hg256 = HgCfg<256, 256>;
@@ -269,10 +546,40 @@ hipError_t launch_cfg(const GemmProblem &q, hipStream_t stream)
 
 }  // namespace
 
+using HgDma256 = HgDmaCfg<256, 256, 4>;
+
+template <class Cfg>
+bool dma_ok(const GemmProblem &q)
+{
+    const bool aligned = (q.lda % 8 == 0) && (q.ldb % 8 == 0) && (q.strideA % 8 == 0) &&
+                         (q.strideB % 8 == 0) && (reinterpret_cast<uintptr_t>(q.A) % 16 == 0) &&
+                         (reinterpret_cast<uintptr_t>(q.B) % 16 == 0);
+    const bool whole = q.M % Cfg::BM == 0 && q.N % Cfg::BN == 0 && q.K % Cfg::BK == 0 &&
+                       q.K >= Cfg::BK * Cfg::STAGES;
+    const bool fits = (long long)Cfg::BM * q.lda * 2 < (1LL << 31) && (long long)Cfg::BK * q.ldb * 2 < (1LL << 31);
+    return aligned && whole && fits;
+}
+
+template <class Cfg>
+hipError_t launch_dma(const GemmProblem &q, hipStream_t stream)
+{
+    HgemmArgs a;
+    a.M = q.M; a.N = q.N; a.K = q.K;
+    a.alpha = q.alpha; a.beta = q.beta;
+    a.A = static_cast<const uint16_t *>(q.A); a.lda = q.lda; a.sA = q.strideA;
+    a.B = static_cast<const uint16_t *>(q.B); a.ldb = q.ldb; a.sB = q.strideB;
+    a.C = q.C; a.ldc = q.ldc; a.sC = q.strideC;
+    a.tiles_m = q.M / Cfg::BM;
+    a.tiles_n = q.N / Cfg::BN;
+    hipLaunchKernelGGL((hgemm_dma_kernel<Cfg>), dim3(a.tiles_m * a.tiles_n, 1, q.batch), dim3(Cfg::NT), 0, stream, a);
+    return hipGetLastError();
+}
+
 hipError_t launch_hgemm(const GemmProblem &q, hipStream_t stream)
 {
     // 256x256 tiles when they give at least one tile per CU, else 128x128.
     const long long t256 = (long long)((q.M + 255) / 256) * ((q.N + 255) / 256) * q.batch;
+    if (t256 >= 256 && dma_ok<HgDma256>(q)) return launch_dma<HgDma256>(q, stream);
     if (t256 >= 256) return launch_cfg<Hg256>(q, stream);
     return launch_cfg<Hg128>(q, stream);
 }
