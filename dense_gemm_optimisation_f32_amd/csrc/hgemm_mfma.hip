@@ -33,6 +33,7 @@
 // everything else (out-of-range elements load as zero, stores are masked).
 #include "gemm_internal.h"
 #include "tile_order.h"
+#include "epilogue.h"
 
 #include <type_traits>
 
@@ -219,7 +220,7 @@ __global__ __launch_bounds__(256) void hgemm_mfma_kernel(HgemmArgs p)
         for (int i = 0; i < Cfg::FM; ++i)
 #pragma unroll
             for (int jj = 0; jj < Cfg::FN; ++jj)
-                acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[jj], acc[i][jj], 0, 0, 0);
+                acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b[jj], a[i], acc[i][jj], 0, 0, 0);
     };
 
     constexpr int NS = BK / 16;   // k substeps per K step
@@ -254,24 +255,22 @@ __global__ __launch_bounds__(256) void hgemm_mfma_kernel(HgemmArgs p)
         }
     }
 
-    // Epilogue: register r of lane l in a 32x32 block is row 8*(r/4)+4*(l/32)+r%4,
-    // column l%32.
+    // Epilogue (operands were swapped, so each lane holds four consecutive
+    // columns of one row per register quad; see epilogue.h).
     const float alpha = p.alpha, beta = p.beta;
+    const bool cvec = (ldc % 4 == 0) && (reinterpret_cast<uintptr_t>(C) % 16 == 0);
     auto epilogue = [&](auto with_c) {
 #pragma unroll
         for (int i = 0; i < Cfg::FM; ++i) {
+            const long long row = m0 + wm * Cfg::TM + 32 * i + lr;
 #pragma unroll
             for (int jj = 0; jj < Cfg::FN; ++jj) {
-                const long long col = n0 + wn * Cfg::TN + 32 * jj + lr;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const long long row = m0 + wm * Cfg::TM + 32 * i + 8 * (r >> 2) + 4 * lk + (r & 3);
-                    if (!MASK || (row < M && col < N)) {
-                        float *dst = C + row * ldc + col;
-                        float v = alpha * acc[i][jj][r];
-                        if (decltype(with_c)::value) v += beta * *dst;
-                        *dst = v;
-                    }
+                for (int g = 0; g < 4; ++g) {
+                    const long long col = n0 + wn * Cfg::TN + 32 * jj + 8 * g + 4 * lk;
+                    const f32x4_t v = {acc[i][jj][4 * g], acc[i][jj][4 * g + 1], acc[i][jj][4 * g + 2],
+                                       acc[i][jj][4 * g + 3]};
+                    store_row4<MASK, decltype(with_c)::value>(C, ldc, row, col, v, alpha, beta, M, N, cvec);
                 }
             }
         }
@@ -444,7 +443,7 @@ __global__ __launch_bounds__(256) void hgemm_dma_kernel(HgemmArgs p)
         for (int i = 0; i < Cfg::FM; ++i)
 #pragma unroll
             for (int jj = 0; jj < Cfg::FN; ++jj)
-                acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[jj], acc[i][jj], 0, 0, 0);
+                acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b[jj], a[i], acc[i][jj], 0, 0, 0);
     };
     auto lds_barrier = [&]() {
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
@@ -490,20 +489,22 @@ __global__ __launch_bounds__(256) void hgemm_dma_kernel(HgemmArgs p)
     mfmas(fa[0], fb[0]);
     mfmas(fa[1], fb[1]);
 
+    // Epilogue (operands were swapped, so each lane holds four consecutive
+    // columns of one row per register quad; see epilogue.h).
     const float alpha = p.alpha, beta = p.beta;
+    const bool cvec = (ldc % 4 == 0) && (reinterpret_cast<uintptr_t>(C) % 16 == 0);
     auto epilogue = [&](auto with_c) {
 #pragma unroll
         for (int i = 0; i < Cfg::FM; ++i) {
+            const long long row = m0 + wm * Cfg::TM + 32 * i + lr;
 #pragma unroll
             for (int jj = 0; jj < Cfg::FN; ++jj) {
-                const long long col = n0 + wn * Cfg::TN + 32 * jj + lr;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const long long row = m0 + wm * Cfg::TM + 32 * i + 8 * (r >> 2) + 4 * lk + (r & 3);
-                    float *dst = C + row * ldc + col;
-                    float v = alpha * acc[i][jj][r];
-                    if (decltype(with_c)::value) v += beta * *dst;
-                    *dst = v;
+                for (int g = 0; g < 4; ++g) {
+                    const long long col = n0 + wn * Cfg::TN + 32 * jj + 8 * g + 4 * lk;
+                    const f32x4_t v = {acc[i][jj][4 * g], acc[i][jj][4 * g + 1], acc[i][jj][4 * g + 2],
+                                       acc[i][jj][4 * g + 3]};
+                    store_row4<false, decltype(with_c)::value>(C, ldc, row, col, v, alpha, beta, 0, 0, cvec);
                 }
             }
         }
@@ -514,7 +515,6 @@ __global__ __launch_bounds__(256) void hgemm_dma_kernel(HgemmArgs p)
         epilogue(std::false_type{});
 }
 
-using Hg256 = HgCfg<256, 256>;
 using Hg128 = HgCfg<128, 128>;
 
 template <class Cfg>
@@ -577,10 +577,11 @@ hipError_t launch_dma(const GemmProblem &q, hipStream_t stream)
 
 hipError_t launch_hgemm(const GemmProblem &q, hipStream_t stream)
 {
-    // 256x256 tiles when they give at least one tile per CU, else 128x128.
+    // Direct-to-LDS 256x256 tiles when the problem is made of whole tiles and
+    // they give at least one tile per CU; 128x128 register-staged tiles (with
+    // bounds checks where needed) otherwise.
     const long long t256 = (long long)((q.M + 255) / 256) * ((q.N + 255) / 256) * q.batch;
     if (t256 >= 256 && dma_ok<HgDma256>(q)) return launch_dma<HgDma256>(q, stream);
-    if (t256 >= 256) return launch_cfg<Hg256>(q, stream);
     return launch_cfg<Hg128>(q, stream);
 }
 

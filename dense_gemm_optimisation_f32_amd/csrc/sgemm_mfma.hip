@@ -26,6 +26,9 @@
 // everything else.  Workgroups are mapped to tiles XCD by XCD (tile_order.h).
 #include "gemm_internal.h"
 #include "tile_order.h"
+#include "epilogue.h"
+
+#include <type_traits>
 
 namespace mi355gemm {
 namespace {
@@ -174,32 +177,251 @@ __global__ __launch_bounds__(Cfg::NT) void sgemm_mfma_kernel(SgemmArgs p)
             for (int i = 0; i < Cfg::FM; ++i)
 #pragma unroll
                 for (int j = 0; j < Cfg::FN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i], b[j], acc[i][j], 0, 0, 0);
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(b[j], a[i], acc[i][j], 0, 0, 0);
         }
         if (t + 1 < nk) store_tiles(buf ^ 1);
         __syncthreads();
     }
 
-    // Epilogue.  In a 32x32 MFMA block, register r of lane l holds row
-    // 8*(r/4) + 4*(l/32) + r%4 and column l%32.
+    // Epilogue (operands were swapped, so each lane holds four consecutive
+    // columns of one row per register quad; see epilogue.h).
     const float alpha = p.alpha, beta = p.beta;
+    const bool cvec = (ldc % 4 == 0) && (reinterpret_cast<uintptr_t>(C) % 16 == 0);
+    auto epilogue = [&](auto with_c) {
 #pragma unroll
-    for (int i = 0; i < Cfg::FM; ++i) {
+        for (int i = 0; i < Cfg::FM; ++i) {
+            const long long row = m0 + wm * Cfg::TM + 32 * i + lr;
 #pragma unroll
-        for (int j = 0; j < Cfg::FN; ++j) {
-            const long long col = n0 + wn * Cfg::TN + 32 * j + lr;
+            for (int jj = 0; jj < Cfg::FN; ++jj) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const long long row = m0 + wm * Cfg::TM + 32 * i + 8 * (r >> 2) + 4 * lk + (r & 3);
-                if (!MASK || (row < M && col < N)) {
-                    float *dst = C + row * ldc + col;
-                    float v = alpha * acc[i][j][r];
-                    if (beta != 0.f) v += beta * *dst;
-                    *dst = v;
+                for (int g = 0; g < 4; ++g) {
+                    const long long col = n0 + wn * Cfg::TN + 32 * jj + 8 * g + 4 * lk;
+                    const f32x4_t v = {acc[i][jj][4 * g], acc[i][jj][4 * g + 1], acc[i][jj][4 * g + 2],
+                                       acc[i][jj][4 * g + 3]};
+                    store_row4<MASK, decltype(with_c)::value>(C, ldc, row, col, v, alpha, beta, M, N, cvec);
                 }
             }
         }
+    };
+    if (beta != 0.f)
+        epilogue(std::true_type{});
+    else
+        epilogue(std::false_type{});
+}
+
+// ---------------------------------------------------------------------------
+// Whole-tile kernel fed by direct-to-LDS loads (global_load_lds_dwordx4: lane
+// l's 16 bytes land at M0 + 16*l, no register staging, no LDS-write
+// instructions).  Two LDS slots of BK = 32 k; slice t+2 is fetched while
+// slice t+1 waits and slice t is computed, which at fp32-MFMA speed (64
+// cycles per 32x32x2 op) leaves a whole slice of compute to hide the fetch.
+//
+// Operand layouts in LDS and the k order:
+//   * A slice: BM rows of 128 bytes (eight 16-byte chunks of four k); the chunk
+//     at physical position p of row r holds logical chunk p ^ ((r ^ r>>3) & 7),
+//     so the sixteen rows one LDS cycle serves fall on distinct banks.  A lane
+//     reads one whole chunk (four consecutive k of its row) per ds_read_b128:
+//     lanes 0-31 the chunk 2u, lanes 32-63 the chunk 2u+1.  Element e of that
+//     read feeds the e-th MFMA of quad u, so that MFMA's k pair is
+//     {8u+e, 8u+4+e} -- a fixed reordering of the sum over k;
+//   * B slice: 32 rows of BN floats, row-major; the chunk at physical
+//     position p of row k holds logical chunk p ^ (8 * ((k >> 2) & 1)), which
+//     puts rows k and k+4 (read by the two half-waves of one MFMA operand) on
+//     different banks.  The B operand of MFMA (u, e) is row 8u+e+4*(lane/32),
+//     column lane%32 -- one ds_read_b32 per lane.
+template <int BM_, int BN_>
+struct SgDmaCfg {
+    static constexpr int BM = BM_, BN = BN_, BK = 32, WM = 2, WN = 2, NT = 256, SLOTS = 2;
+    static constexpr int TM = BM / WM, TN = BN / WN;
+    static constexpr int FM = TM / 32, FN = TN / 32;
+    static constexpr int A_BYTES = BM * BK * 4;
+    static constexpr int B_BYTES = BK * BN * 4;
+    static constexpr int SLOT_BYTES = A_BYTES + B_BYTES;
+    static constexpr int A_LOADS = A_BYTES / 1024 / 4;       // per wave per slice
+    static constexpr int B_LOADS = B_BYTES / 1024 / 4;
+    static constexpr int B_CPR = BN / 4;                     // 16-byte chunks per B row
+    static constexpr int B_RPL = 256 / BN;                   // B rows per wave load
+    static_assert(A_BYTES % 4096 == 0 && B_BYTES % 4096 == 0, "slices must split over 4 waves");
+    static_assert(SLOTS * SLOT_BYTES <= 160 * 1024, "LDS slots too large");
+};
+
+__device__ __forceinline__ int sg_swz_a(int r) { return (r ^ (r >> 3)) & 7; }
+__device__ __forceinline__ int sg_swz_b(int k) { return 8 * ((k >> 2) & 1); }
+
+__device__ __forceinline__ void sg_dma16(const void *sbase, unsigned voff, unsigned lds_addr)
+{
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(voff), "s"(sbase), "s"(lds_addr)
+                 : "memory", "m0");
+}
+
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) f32x4v lds_f32x4;
+typedef __attribute__((address_space(3))) float lds_f32;
+
+template <class Cfg>
+__global__ __launch_bounds__(256) void sgemm_dma_kernel(SgemmArgs p)
+{
+    constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK;
+    __shared__ __attribute__((aligned(1024))) unsigned char lds[Cfg::SLOTS * Cfg::SLOT_BYTES];
+    const unsigned lds0 = (unsigned)(uintptr_t)lds;
+
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int uwave = __builtin_amdgcn_readfirstlane(wave);
+    int tm, tn;
+    tile_coords(blockIdx.x, p.tiles_m, p.tiles_n, &tm, &tn);
+    const long long m0 = (long long)tm * BM, n0 = (long long)tn * BN;
+    const long long lda = p.lda, ldb = p.ldb, ldc = p.ldc;
+    const char *Ab = reinterpret_cast<const char *>(p.A + (long long)blockIdx.z * p.sA + m0 * lda);
+    const char *Bb = reinterpret_cast<const char *>(p.B + (long long)blockIdx.z * p.sB + n0);
+    float *C = p.C + (long long)blockIdx.z * p.sC;
+
+    unsigned offA[Cfg::A_LOADS], offB[Cfg::B_LOADS];
+#pragma unroll
+    for (int i = 0; i < Cfg::A_LOADS; ++i) {
+        const int r = 8 * (uwave * Cfg::A_LOADS + i) + (lane >> 3);
+        offA[i] = (unsigned)(r * lda + 4 * ((lane & 7) ^ sg_swz_a(r))) * 4u;
     }
+#pragma unroll
+    for (int i = 0; i < Cfg::B_LOADS; ++i) {
+        const int k = Cfg::B_RPL * (uwave * Cfg::B_LOADS + i) + lane / Cfg::B_CPR;
+        offB[i] = (unsigned)(k * ldb + 4 * ((lane % Cfg::B_CPR) ^ sg_swz_b(k))) * 4u;
+    }
+    auto issue_slice = [&](int kt, int slot) {
+        const char *a = Ab + (long long)kt * BK * 4;
+        const char *b = Bb + (long long)kt * BK * ldb * 4;
+        const unsigned la = lds0 + slot * Cfg::SLOT_BYTES + uwave * Cfg::A_LOADS * 1024;
+        const unsigned lb = lds0 + slot * Cfg::SLOT_BYTES + Cfg::A_BYTES + uwave * Cfg::B_LOADS * 1024;
+#pragma unroll
+        for (int i = 0; i < Cfg::A_LOADS; ++i) sg_dma16(a, offA[i], la + 1024 * i);
+#pragma unroll
+        for (int i = 0; i < Cfg::B_LOADS; ++i) sg_dma16(b, offB[i], lb + 1024 * i);
+    };
+
+    const int wm = wave / Cfg::WN, wn = wave % Cfg::WN;
+    const int lr = lane & 31, lk = lane >> 5;
+    // A operand rows and the lane part of their chunk index (logical chunk 2u+lk).
+    unsigned rowA[Cfg::FM], tA[Cfg::FM];
+#pragma unroll
+    for (int i = 0; i < Cfg::FM; ++i) {
+        const int r = wm * Cfg::TM + 32 * i + lr;
+        rowA[i] = (unsigned)(r * BK * 4);
+        tA[i] = (unsigned)(lk ^ sg_swz_a(r));
+    }
+    // B operand: row 8u+e+4*lk, logical chunk (wn*TN + 32j + lr)/4, physical
+    // chunk flipped by 8 when lk = 1.
+    unsigned colB[Cfg::FN];
+#pragma unroll
+    for (int j = 0; j < Cfg::FN; ++j) {
+        const int q = ((wn * Cfg::TN + 32 * j) >> 2) + (lr >> 2);
+        colB[j] = (unsigned)(Cfg::A_BYTES + 4 * lk * BN * 4 + 16 * (q ^ (8 * lk)) + 4 * (lr & 3));
+    }
+
+    f32x16 acc[Cfg::FM][Cfg::FN];
+#pragma unroll
+    for (int i = 0; i < Cfg::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < Cfg::FN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+    auto compute_slice = [&](int slot) {
+        const unsigned base = lds0 + slot * Cfg::SLOT_BYTES;
+#pragma unroll
+        for (int u = 0; u < BK / 8; ++u) {
+            f32x4v a[Cfg::FM];
+#pragma unroll
+            for (int i = 0; i < Cfg::FM; ++i)
+                a[i] = *(const lds_f32x4 *)(uintptr_t)(base + rowA[i] + 16 * (tA[i] ^ (2u * u)));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                float b[Cfg::FN];
+#pragma unroll
+                for (int j = 0; j < Cfg::FN; ++j)
+                    b[j] = *(const lds_f32 *)(uintptr_t)(base + colB[j] + (8 * u + e) * BN * 4);
+#pragma unroll
+                for (int i = 0; i < Cfg::FM; ++i)
+#pragma unroll
+                    for (int j = 0; j < Cfg::FN; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(b[j], a[i][e], acc[i][j], 0, 0, 0);
+            }
+        }
+    };
+    auto lds_barrier = [&]() {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    };
+    constexpr int LOADS = Cfg::A_LOADS + Cfg::B_LOADS;
+    static_assert(LOADS < 64, "vmcnt range");
+
+    const int nk = p.K / BK;   // >= 2 (checked by the launcher)
+    issue_slice(0, 0);
+    issue_slice(1, 1);
+    __builtin_amdgcn_s_waitcnt((LOADS & 15) | ((LOADS >> 4) << 14) | (7 << 4) | (15 << 8));   // slice 0 done
+    lds_barrier();
+    for (int t = 0; t < nk; ++t) {
+        compute_slice(t & 1);
+        if (t + 1 < nk) {
+            __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): slice t+1 done for this lane
+            __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's slice-t reads are done
+            lds_barrier();
+            if (t + 2 < nk) issue_slice(t + 2, t & 1);
+        }
+    }
+
+    const float alpha = p.alpha, beta = p.beta;
+    const bool cvec = (ldc % 4 == 0) && (reinterpret_cast<uintptr_t>(C) % 16 == 0);
+    auto epilogue = [&](auto with_c) {
+#pragma unroll
+        for (int i = 0; i < Cfg::FM; ++i) {
+            const long long row = m0 + wm * Cfg::TM + 32 * i + lr;
+#pragma unroll
+            for (int jj = 0; jj < Cfg::FN; ++jj) {
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const long long col = n0 + wn * Cfg::TN + 32 * jj + 8 * g + 4 * lk;
+                    const f32x4_t v = {acc[i][jj][4 * g], acc[i][jj][4 * g + 1], acc[i][jj][4 * g + 2],
+                                       acc[i][jj][4 * g + 3]};
+                    store_row4<false, decltype(with_c)::value>(C, ldc, row, col, v, alpha, beta, 0, 0, cvec);
+                }
+            }
+        }
+    };
+    if (beta != 0.f)
+        epilogue(std::true_type{});
+    else
+        epilogue(std::false_type{});
+}
+
+using SgDma256 = SgDmaCfg<256, 256>;
+using SgDma128 = SgDmaCfg<128, 128>;
+
+template <class Cfg>
+bool sg_dma_ok(const GemmProblem &q)
+{
+    const bool aligned = (q.lda % 4 == 0) && (q.ldb % 4 == 0) && (q.strideA % 4 == 0) &&
+                         (q.strideB % 4 == 0) && (reinterpret_cast<uintptr_t>(q.A) % 16 == 0) &&
+                         (reinterpret_cast<uintptr_t>(q.B) % 16 == 0);
+    const bool whole = q.M % Cfg::BM == 0 && q.N % Cfg::BN == 0 && q.K % Cfg::BK == 0 && q.K >= 2 * Cfg::BK;
+    const bool fits = (long long)Cfg::BM * q.lda * 4 < (1LL << 31) && (long long)Cfg::BK * q.ldb * 4 < (1LL << 31);
+    return aligned && whole && fits;
+}
+
+template <class Cfg>
+hipError_t launch_sg_dma(const GemmProblem &q, hipStream_t stream)
+{
+    SgemmArgs a;
+    a.M = q.M; a.N = q.N; a.K = q.K;
+    a.alpha = q.alpha; a.beta = q.beta;
+    a.A = static_cast<const float *>(q.A); a.lda = q.lda; a.sA = q.strideA;
+    a.B = static_cast<const float *>(q.B); a.ldb = q.ldb; a.sB = q.strideB;
+    a.C = q.C; a.ldc = q.ldc; a.sC = q.strideC;
+    a.tiles_m = q.M / Cfg::BM;
+    a.tiles_n = q.N / Cfg::BN;
+    hipLaunchKernelGGL((sgemm_dma_kernel<Cfg>), dim3(a.tiles_m * a.tiles_n, 1, q.batch), dim3(Cfg::NT), 0, stream, a);
+    return hipGetLastError();
 }
 
 using SgBig = SgCfg<128, 128, 16, 2, 2>;
@@ -235,6 +457,12 @@ hipError_t launch_cfg(const GemmProblem &q, hipStream_t stream)
 
 hipError_t launch_sgemm(const GemmProblem &q, hipStream_t stream)
 {
+    // Direct-to-LDS whole tiles: 256x256 when that still gives one tile per
+    // CU, else 128x128; register-staged 128x128 tiles with bounds checks for
+    // everything else.
+    const long long t256 = (long long)(q.M / 256) * (q.N / 256) * q.batch;
+    if (t256 >= 256 && sg_dma_ok<SgDma256>(q)) return launch_sg_dma<SgDma256>(q, stream);
+    if (sg_dma_ok<SgDma128>(q)) return launch_sg_dma<SgDma128>(q, stream);
     return launch_cfg<SgBig>(q, stream);
 }
 
