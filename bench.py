@@ -38,7 +38,8 @@ KERNEL_SOURCES = {
     "sgemm": "dense_gemm_optimisation_f32_amd/csrc/sgemm_mfma.hip",
     "hgemm": "dense_gemm_optimisation_f32_amd/csrc/hgemm_mfma.hip",
 }
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.md")
+COPY_BYTES = 256 << 20   # size of the calibration copy (read and written)
 
 
 def source_digest(kind: str) -> str:
@@ -46,11 +47,18 @@ def source_digest(kind: str) -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
+def _traffic_records():
+    """The JSON block of the committed counter summary (profiles/hbm_traffic.md)."""
+    text = open(TRAFFIC_FILE).read()
+    start = text.index("```json") + len("```json")
+    return json.loads(text[start:text.index("```", start)])
+
+
 def measured_traffic(kind: str, workload: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary, or None
     when it is missing or was taken on a different version of the kernel source."""
     try:
-        rec = json.load(open(TRAFFIC_FILE))[kind]
+        rec = _traffic_records()[kind]
     except (OSError, KeyError, ValueError):
         return None
     if rec.get("source_sha") != source_digest(kind) or rec.get("workload") != workload:
@@ -66,7 +74,14 @@ def main() -> int:
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--no-extra", action="store_true", help="skip the other configurations")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU-oracle time budget")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run a plain 256 MiB device copy three times (counter calibration)")
+    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="turn two rocprofv3 counter_collection.csv files (FETCH_SIZE, WRITE_SIZE) of a "
+                         "--copy-calibration run into profiles/hbm_traffic.md; uses no GPU")
     args = ap.parse_args()
+    if args.write_traffic:
+        return write_traffic(*args.write_traffic)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: this library has no multi-GPU path "
@@ -99,6 +114,15 @@ def main() -> int:
     hA, hB = upload(ph["A"]), upload(ph["B"])
     hC = torch.empty(Mh * Nh, dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
+
+    if args.copy_calibration:
+        # uninitialised buffers: no fill kernel joins the counted dispatches
+        src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)   # plain elementwise copy: reads and writes COPY_BYTES
+        torch.cuda.synchronize()
+        del src, dst
 
     def sgemm():
         dg.gemm_f32(Ms, Ns, Ks, 1.0, sA, Ks, sB, Ns, 0.0, sC, Ns, stream)
@@ -179,6 +203,68 @@ def main() -> int:
         "extra": extra,
     }
     print(json.dumps(line), flush=True)
+    return 0
+
+
+def write_traffic(fetch_csv: str, write_csv: str) -> int:
+    """Per-launch HBM traffic of the step's kernels from FETCH_SIZE / WRITE_SIZE counter
+    runs, each scaled by the ratio of known bytes to counted bytes for the calibration copy."""
+    import csv
+
+    def per_kernel(path, counter):
+        vals = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            name, value = r["Kernel_Name"], float(r["Counter_Value"]) * 1024.0
+            kind = "sgemm" if "sgemm" in name else "hgemm" if "hgemm" in name else "copy"
+            if kind == "copy" and value < COPY_BYTES / 8:
+                continue   # other small kernels of the run (tensor fills), not the calibration copy
+            vals.setdefault(kind, {}).setdefault(name, []).append(value)
+        return vals
+
+    fetch, write = per_kernel(fetch_csv, "FETCH_SIZE"), per_kernel(write_csv, "WRITE_SIZE")
+
+    def mean(d, kind):
+        (name, v), = d[kind].items()
+        return name, sum(v) / len(v)
+
+    copy_name, copy_f = mean(fetch, "copy")
+    _, copy_w = mean(write, "copy")
+    scale_f, scale_w = COPY_BYTES / copy_f, COPY_BYTES / copy_w
+    workloads = {"sgemm": "SGEMM fp32 row-major 4096x4096x1024 alpha=1 beta=0",
+                 "hgemm": "HGEMM fp16->fp32 row-major 4096x4096x4096 alpha=1 beta=0"}
+    alg = {"sgemm": 4 * (4096 * 1024 * 2 + 4096 * 4096), "hgemm": 2 * (4096 * 4096 * 2) + 4 * 4096 * 4096}
+    recs = {"copy_calibration": {"kernel": copy_name, "bytes": COPY_BYTES, "fetch_counted": copy_f,
+                                 "write_counted": copy_w, "fetch_scale": scale_f, "write_scale": scale_w}}
+    rows = []
+    for kind in ("sgemm", "hgemm"):
+        name, f = mean(fetch, kind)
+        _, w = mean(write, kind)
+        total = f * scale_f + w * scale_w
+        recs[kind] = {"kernel": name, "workload": workloads[kind], "source_sha": source_digest(kind),
+                      "fetch_bytes_per_launch": f * scale_f, "write_bytes_per_launch": w * scale_w,
+                      "hbm_bytes_per_launch": total, "algorithmic_bytes": alg[kind]}
+        rows.append(f"| {kind} | {workloads[kind]} | {f * scale_f / 1e6:.1f} | {w * scale_w / 1e6:.1f} | "
+                    f"{total / 1e6:.1f} | {alg[kind] / 1e6:.1f} | {total / alg[kind]:.2f} |")
+    cmd = ("cd /tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d $R/gpurun_out/traffic_fetch -o t -- "
+           "python3 $R/bench.py --no-cpu --no-extra --steps 3 --warmup 1 --copy-calibration\n"
+           "cd /tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv -d $R/gpurun_out/traffic_write -o t -- "
+           "python3 $R/bench.py --no-cpu --no-extra --steps 3 --warmup 1 --copy-calibration\n"
+           "python3 $R/bench.py --write-traffic $R/gpurun_out/traffic_fetch/t_counter_collection.csv "
+           "$R/gpurun_out/traffic_write/t_counter_collection.csv   # R = repository root")
+    text = ("# HBM traffic per launch: bench step kernels (rocprofv3 FETCH_SIZE / WRITE_SIZE)\n\n"
+            f"Commands (one MI355X):\n\n```\n{cmd}\n```\n\n"
+            f"Calibration: a plain elementwise copy of {COPY_BYTES >> 20} MiB reads and writes {COPY_BYTES} bytes; "
+            f"the counters read {copy_f:.0f} B fetched and {copy_w:.0f} B written, so fetch counts are scaled by "
+            f"{scale_f:.4f} and write counts by {scale_w:.4f}.\n\n"
+            "| kernel | workload | fetched (MB) | written (MB) | total (MB) | algorithmic (MB) | ratio |\n"
+            "|---|---|---|---|---|---|---|\n" + "\n".join(rows) + "\n\n"
+            "Machine-readable copy (bench.py reads it; a record whose source_sha no longer matches the kernel "
+            "source is ignored):\n\n```json\n" + json.dumps(recs, indent=1) + "\n```\n")
+    with open(TRAFFIC_FILE, "w") as f:
+        f.write(text)
+    print(text)
     return 0
 
 
