@@ -286,38 +286,51 @@ __global__ __launch_bounds__(256) void hgemm_mfma_kernel(HgemmArgs p)
 //
 // gfx950's global_load_lds_dwordx4 moves 16 bytes per lane from global memory
 // straight into LDS, lane l's bytes landing at M0 + 16*l, with no trip through
-// vector registers and no LDS-write instruction.  That lets the K loop keep a
-// ring of STAGES BK=32 slices in LDS and issue the loads of slice t+STAGES
-// while slice t is computed, hiding global latency behind several slices of
-// MFMA work.  Because a wave's load fills 1 KB of LDS contiguously, the
+// vector registers and no LDS-write instruction.  The K loop keeps a ring of
+// STAGES slices of BK k in LDS and fetches slice t+STAGES while slice t is
+// computed.  Because a wave's load fills 1 KB of LDS contiguously, the
 // swizzled layouts are produced by choosing, per lane, which global chunk to
 // fetch for the LDS position the lane owns:
-//   * A slice: BM rows of 64 bytes (four 16-byte k chunks); the chunk at
-//     physical position p of row r holds logical chunk p ^ swz_a(r);
-//   * B slice: 32 rows of BN halves (row-major [k][n]); the chunk at physical
+//   * A slice: BM rows of BK halves (four or eight 16-byte k chunks); the
+//     chunk at physical position p of row r holds logical chunk p ^ swz_a(r);
+//   * B slice: BK rows of BN halves (row-major [k][n]); the chunk at physical
 //     position p of row k holds logical chunk p ^ swz_b(k).
-// swz_a keeps the rows that one LDS cycle serves on distinct banks for the
-// 16-byte A operand reads; swz_b does the same for the four rows a
-// transposed B read touches (for both 128- and 256-byte bank windows).
-// Requires M % BM == 0, N % BN == 0, K % 32 == 0, 16-byte aligned rows and
-// byte offsets within a slice below 2^31.
-template <int BM_, int BN_, int STAGES_>
+// swz_a keeps the rows one LDS cycle serves on distinct banks for the 16-byte
+// A operand reads; swz_b does the same for the four rows a transposed B read
+// touches (measured conflict-free on gfx950 for 128- and 256-byte windows).
+// The workgroup runs WM x WN waves; with eight waves two share each SIMD, so
+// one wave's MFMAs cover the other's LDS latency.
+// Requires M % BM == 0, N % BN == 0, K % BK == 0, K >= STAGES*BK, 16-byte
+// aligned rows and byte offsets within a slice below 2^31.
+template <int BM_, int BN_, int STAGES_, int WM_, int WN_, int BK_>
 struct HgDmaCfg {
-    static constexpr int BM = BM_, BN = BN_, BK = 32, STAGES = STAGES_, WM = 2, WN = 2, NT = 256;
+    static constexpr int BM = BM_, BN = BN_, BK = BK_, STAGES = STAGES_, WM = WM_, WN = WN_;
+    static constexpr int NW = WM * WN, NT = 64 * NW;
+    static constexpr int A_CPR = BK / 8;                        // 16-byte chunks per A row
     static constexpr int TM = BM / WM, TN = BN / WN;
     static constexpr int FM = TM / 32, FN = TN / 32;
     static constexpr int A_BYTES = BM * BK * 2;                 // one A slice
     static constexpr int B_BYTES = BK * BN * 2;                 // one B slice
     static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
-    static constexpr int A_LOADS = A_BYTES / 1024 / 4;          // per wave per slice
-    static constexpr int B_LOADS = B_BYTES / 1024 / 4;
+    static constexpr int A_LOADS = A_BYTES / 1024 / NW;         // per wave per slice
+    static constexpr int B_LOADS = B_BYTES / 1024 / NW;
     static constexpr int B_CPR = BN / 8;                        // 16-byte chunks per B row
     static constexpr int B_RPL = 64 / B_CPR;                    // B rows per wave load
-    static_assert(A_BYTES % 4096 == 0 && B_BYTES % 4096 == 0, "slices must split over 4 waves");
+    static_assert(A_BYTES % (1024 * NW) == 0 && B_BYTES % (1024 * NW) == 0, "slices must split over the waves");
+    static_assert(A_CPR == 4 || A_CPR == 8, "A rows of 64 or 128 bytes");
     static_assert(STAGES * STAGE_BYTES <= 160 * 1024, "LDS ring too large");
 };
 
-__device__ __forceinline__ int swz_a(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+// A chunk swizzle.  64-byte rows (four chunks): rows that one LDS cycle
+// serves get distinct (row, chunk) bank groups.  128-byte rows (eight chunks):
+// the chunk is XORed with row bits 0-2 and 3-4, which keeps any aligned 16
+// rows on distinct banks and is unchanged by the 32-row steps between the
+// MFMA blocks of a wave.
+template <int CPR>
+__device__ __forceinline__ int swz_a(int r)
+{
+    return CPR == 8 ? ((r & 7) ^ ((r >> 3) & 3)) : (((r >> 1) ^ (r >> 3)) & 3);
+}
 __device__ __forceinline__ int swz_b(int k)
 {
     // rows k..k+3 of an aligned group of four map to XOR patterns 0, 6, 10, 12
@@ -355,7 +368,7 @@ __device__ __forceinline__ void wait_vmcnt()
 }
 
 template <class Cfg>
-__global__ __launch_bounds__(256) void hgemm_dma_kernel(HgemmArgs p)
+__global__ __launch_bounds__(Cfg::NT) void hgemm_dma_kernel(HgemmArgs p)
 {
     constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, S = Cfg::STAGES;
     __shared__ __attribute__((aligned(1024))) unsigned char lds[S * Cfg::STAGE_BYTES];
@@ -376,8 +389,8 @@ __global__ __launch_bounds__(256) void hgemm_dma_kernel(HgemmArgs p)
 #pragma unroll
     for (int i = 0; i < Cfg::A_LOADS; ++i) {
         const int g = wave * Cfg::A_LOADS + i;
-        const int r = 16 * g + (lane >> 2);
-        offA[i] = (unsigned)(r * lda + 8 * ((lane & 3) ^ swz_a(r))) * 2u;
+        const int r = (64 / Cfg::A_CPR) * g + lane / Cfg::A_CPR;
+        offA[i] = (unsigned)(r * lda + 8 * ((lane % Cfg::A_CPR) ^ swz_a<Cfg::A_CPR>(r))) * 2u;
     }
 #pragma unroll
     for (int i = 0; i < Cfg::B_LOADS; ++i) {
@@ -401,11 +414,11 @@ __global__ __launch_bounds__(256) void hgemm_dma_kernel(HgemmArgs p)
     // Fragment read addresses (bytes, without the slot base).
     const int wm = wave / Cfg::WN, wn = wave % Cfg::WN;
     const int lr = lane & 31, lk = lane >> 5, q = lane >> 4, j = lane & 15;
-    unsigned fragA[2];
+    unsigned fragA[BK / 16];
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
+    for (int s = 0; s < BK / 16; ++s) {
         const int r = wm * Cfg::TM + lr;
-        fragA[s] = (unsigned)(r * BK * 2 + 16 * ((2 * s + lk) ^ swz_a(r)));
+        fragA[s] = (unsigned)(r * BK * 2 + 16 * ((2 * s + lk) ^ swz_a<Cfg::A_CPR>(r)));
     }
     unsigned fragB[Cfg::FN];
     const int kq = 8 * (q >> 1) + (j >> 2);     // row within a 16-row substep (plus 4*h)
@@ -450,22 +463,39 @@ __global__ __launch_bounds__(256) void hgemm_dma_kernel(HgemmArgs p)
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
     };
-    // One step on slice t (slot t % S): substep 1 fragments of slice t are read
-    // while substep 0 is computed; then, once slice t+1 is resident for every
-    // wave (this lane's loads counted down to PENDING outstanding slices, then
-    // the barrier) and every wave holds its slice-t fragments, slot t % S may be
-    // refilled with slice t+S, and the substep 0 fragments of slice t+1 are read
-    // while substep 1 of slice t is computed.
+    // Interleave each substep's MFMAs one-for-one with the LDS reads of the
+    // next substep's fragments.
+    auto interleave = [&]() {
+#pragma unroll
+        for (int i = 0; i < Cfg::FM * Cfg::FN; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+        }
+    };
+    // One step on slice t (slot t % S).  The fragments of substep sub+1 are read
+    // while substep sub is computed; before the last substep, once slice t+1 is
+    // resident for every wave (this lane's loads counted down to PENDING
+    // outstanding slices, then the barrier) and every wave holds its slice-t
+    // fragments, slot t % S is refilled with slice t+S and the first fragments
+    // of slice t+1 are read while the last substep of slice t is computed.
+    constexpr int NS = BK / 16;
     auto step = [&](int t, auto pending, auto refill) {
         const int slot = t % S;
-        read_frags(slot, 1, fa[1], fb[1]);
-        mfmas(fa[0], fb[0]);
-        wait_vmcnt<LOADS * decltype(pending)::value>();
-        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's slice-t reads are done
-        lds_barrier();
-        if (decltype(refill)::value) issue_slice(t + S, slot);
-        read_frags((t + 1) % S, 0, fa[0], fb[0]);
-        mfmas(fa[1], fb[1]);
+#pragma unroll
+        for (int sub = 0; sub < NS; ++sub) {
+            const int cur = sub & 1, nxt = cur ^ 1;
+            if (sub + 1 < NS) {
+                read_frags(slot, sub + 1, fa[nxt], fb[nxt]);
+            } else {
+                wait_vmcnt<LOADS * decltype(pending)::value>();
+                __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's slice-t reads are done
+                lds_barrier();
+                if (decltype(refill)::value) issue_slice(t + S, slot);
+                read_frags((t + 1) % S, 0, fa[nxt], fb[nxt]);
+            }
+            mfmas(fa[cur], fb[cur]);
+            interleave();
+        }
     };
 
     const int nk = p.K / BK;   // >= S (checked by the launcher)
@@ -480,17 +510,24 @@ __global__ __launch_bounds__(256) void hgemm_dma_kernel(HgemmArgs p)
     for (int t = 0; t + S < nk; ++t) step(t, std::integral_constant<int, S - 2>{}, std::true_type{});
     // Tail: no more slices to issue; the outstanding count drains to zero.
     const int t0 = nk - S;
-    step(t0 + 0, std::integral_constant<int, S - 2>{}, std::false_type{});
-    step(t0 + 1, std::integral_constant<int, S - 3>{}, std::false_type{});
-    step(t0 + 2, std::integral_constant<int, S - 4>{}, std::false_type{});
-    static_assert(S == 4, "the tail above is written for a four-slice ring");
-    // Last slice: both substeps from registers/LDS already resident.
-    read_frags((nk - 1) % S, 1, fa[1], fb[1]);
-    mfmas(fa[0], fb[0]);
-    mfmas(fa[1], fb[1]);
+    if constexpr (S == 4) {
+        step(t0 + 0, std::integral_constant<int, 2>{}, std::false_type{});
+        step(t0 + 1, std::integral_constant<int, 1>{}, std::false_type{});
+        step(t0 + 2, std::integral_constant<int, 0>{}, std::false_type{});
+    } else {
+        static_assert(S == 2, "ring of two or four slices");
+        step(t0 + 0, std::integral_constant<int, 0>{}, std::false_type{});
+    }
+    {   // last slice: everything is resident
+        const int slot = (nk - 1) % S;
+#pragma unroll
+        for (int sub = 0; sub < NS; ++sub) {
+            const int cur = sub & 1, nxt = cur ^ 1;
+            if (sub + 1 < NS) read_frags(slot, sub + 1, fa[nxt], fb[nxt]);
+            mfmas(fa[cur], fb[cur]);
+        }
+    }
 
-    // Epilogue (operands were swapped, so each lane holds four consecutive
-    // columns of one row per register quad; see epilogue.h).
     const float alpha = p.alpha, beta = p.beta;
     const bool cvec = (ldc % 4 == 0) && (reinterpret_cast<uintptr_t>(C) % 16 == 0);
     auto epilogue = [&](auto with_c) {
@@ -546,7 +583,8 @@ hipError_t launch_cfg(const GemmProblem &q, hipStream_t stream)
 
 }  // namespace
 
-using HgDma256 = HgDmaCfg<256, 256, 4>;
+// 256x256 tile, 8 waves (2 x 4) of 128x64, BK = 64, two LDS slots of 64 KB.
+using HgDma256 = HgDmaCfg<256, 256, 2, 2, 4, 64>;
 
 template <class Cfg>
 bool dma_ok(const GemmProblem &q)
