@@ -585,6 +585,9 @@ hipError_t launch_cfg(const GemmProblem &q, hipStream_t stream)
 
 // 256x256 tile, 8 waves (2 x 4) of 128x64, BK = 64, two LDS slots of 64 KB.
 using HgDma256 = HgDmaCfg<256, 256, 2, 2, 4, 64>;
+// 128x128 tile, 4 waves of 64x64, BK = 64, four slots of 32 KB: for grids that
+// 256x256 tiles would leave under-filled.
+using HgDma128 = HgDmaCfg<128, 128, 4, 2, 2, 64>;
 
 template <class Cfg>
 bool dma_ok(const GemmProblem &q)
@@ -620,6 +623,7 @@ hipError_t launch_hgemm(const GemmProblem &q, hipStream_t stream)
     // bounds checks where needed) otherwise.
     const long long t256 = (long long)((q.M + 255) / 256) * ((q.N + 255) / 256) * q.batch;
     if (t256 >= 256 && dma_ok<HgDma256>(q)) return launch_dma<HgDma256>(q, stream);
+    if (dma_ok<HgDma128>(q)) return launch_dma<HgDma128>(q, stream);
     return launch_cfg<Hg128>(q, stream);
 }
 

@@ -424,6 +424,169 @@ hipError_t launch_sg_dma(const GemmProblem &q, hipStream_t stream)
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Small / under-filled problems: split K inside the workgroup.
+//
+// When even 128x128 tiles leave most CUs idle (M*N small next to K), one
+// workgroup owns a (32*FM) x (32*FN) tile of C and its four waves split K
+// into four contiguous ranges (multiples of 8).  Each wave streams its
+// operands straight from global memory into registers -- A as 16-byte quads
+// of four consecutive k of a row (element e of quad u feeds k pair
+// {8u+e, 8u+4+e}, as in the whole-tile kernel), B as one float per lane and k
+// -- keeping P steps of eight k in flight, and accumulates its partial tile on
+// the fp32 MFMA.  The four partial tiles meet in LDS and are summed in a fixed
+// order (wave 0 + wave 1 + wave 2 + wave 3), so results are deterministic; each
+// wave then finishes one quarter of the tile (its register quad) through the
+// alpha/beta epilogue.  Out-of-range rows, columns and k load as zero.
+template <int FM_, int FN_>
+struct SgSmallCfg {
+    static constexpr int FM = FM_, FN = FN_, KW = 4, NT = 64 * KW, P = 4;
+    static constexpr int TM = 32 * FM, TN = 32 * FN;
+};
+
+template <class Cfg, bool VECA>
+__global__ __launch_bounds__(256) void sgemm_small_kernel(SgemmArgs p)
+{
+    constexpr int FM = Cfg::FM, FN = Cfg::FN, KW = Cfg::KW, P = Cfg::P;
+    __shared__ f32x4_t part[KW * FM * FN * 4 * 64];
+
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+    const int lr = lane & 31, lk = lane >> 5;
+    int tm, tn;
+    tile_coords(blockIdx.x, p.tiles_m, p.tiles_n, &tm, &tn);
+    const long long m0 = (long long)tm * Cfg::TM, n0 = (long long)tn * Cfg::TN;
+    const int M = p.M, N = p.N, K = p.K;
+    const float *A = p.A + (long long)blockIdx.z * p.sA;
+    const float *B = p.B + (long long)blockIdx.z * p.sB;
+    float *C = p.C + (long long)blockIdx.z * p.sC;
+    const long long lda = p.lda, ldb = p.ldb, ldc = p.ldc;
+
+    // this wave's k range
+    const int kc = (((K + KW - 1) / KW) + 7) & ~7;
+    const int kb = w * kc;
+    const int ke = (kb + kc < K) ? kb + kc : K;
+
+    bool rowok[FM], colok[FN];
+    const float *arow[FM];
+    const float *bcol[FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+        const long long r = m0 + 32 * i + lr;
+        rowok[i] = r < M;
+        arow[i] = A + (rowok[i] ? r : 0) * lda;
+    }
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+        const long long c = n0 + 32 * j + lr;
+        colok[j] = c < N;
+        bcol[j] = B + (colok[j] ? c : 0);
+    }
+
+    f32x4_t ra[P][FM];
+    float rb[P][FN][4];
+    auto load_step = [&](int k, f32x4_t *a, float (*b)[4]) {
+        const int ka = k + 4 * lk;   // this lane's A quad starts here
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            if (VECA && rowok[i] && ka + 3 < ke) {
+                a[i] = *reinterpret_cast<const f32x4_t *>(arow[i] + ka);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) a[i][e] = (rowok[i] && ka + e < ke) ? arow[i][ka + e] : 0.f;
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int kk = k + e + 4 * lk;
+                b[j][e] = (colok[j] && kk < ke) ? bcol[j][(long long)kk * ldb] : 0.f;
+            }
+    };
+
+    f32x16 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+    const int nsteps = (ke > kb) ? (ke - kb + 7) / 8 : 0;
+#pragma unroll
+    for (int s = 0; s < P; ++s)
+        if (s < nsteps) load_step(kb + 8 * s, ra[s], rb[s]);
+    for (int s0 = 0; s0 < nsteps; s0 += P) {
+#pragma unroll
+        for (int s = 0; s < P; ++s) {
+            if (s0 + s < nsteps) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+#pragma unroll
+                    for (int i = 0; i < FM; ++i)
+#pragma unroll
+                        for (int j = 0; j < FN; ++j)
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(rb[s][j][e], ra[s][i][e], acc[i][j], 0, 0, 0);
+                if (s0 + s + P < nsteps) load_step(kb + 8 * (s0 + s + P), ra[s], rb[s]);
+            }
+        }
+    }
+
+    // Partial tiles to LDS: quad g of block (i, j) of wave w at
+    // part[(((w*FM + i)*FN + j)*4 + g)*64 + lane].
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+                part[(((w * FM + i) * FN + j) * 4 + g) * 64 + lane] =
+                    f32x4_t{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+    __syncthreads();
+
+    // Wave w reduces quad g = w of every block and writes it.
+    const float alpha = p.alpha, beta = p.beta;
+    const bool cvec = (ldc % 4 == 0) && (reinterpret_cast<uintptr_t>(C) % 16 == 0);
+    const int g = w;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            f32x4_t sum = part[((i * FN + j) * 4 + g) * 64 + lane];
+#pragma unroll
+            for (int ww = 1; ww < KW; ++ww) sum += part[(((ww * FM + i) * FN + j) * 4 + g) * 64 + lane];
+            const long long row = m0 + 32 * i + lr;
+            const long long col = n0 + 32 * j + 8 * g + 4 * lk;
+            if (beta != 0.f)
+                store_row4<true, true>(C, ldc, row, col, sum, alpha, beta, M, N, cvec);
+            else
+                store_row4<true, false>(C, ldc, row, col, sum, alpha, beta, M, N, cvec);
+        }
+}
+
+template <class Cfg>
+hipError_t launch_small(const GemmProblem &q, hipStream_t stream)
+{
+    SgemmArgs a;
+    a.M = q.M; a.N = q.N; a.K = q.K;
+    a.alpha = q.alpha; a.beta = q.beta;
+    a.A = static_cast<const float *>(q.A); a.lda = q.lda; a.sA = q.strideA;
+    a.B = static_cast<const float *>(q.B); a.ldb = q.ldb; a.sB = q.strideB;
+    a.C = q.C; a.ldc = q.ldc; a.sC = q.strideC;
+    a.tiles_m = (q.M + Cfg::TM - 1) / Cfg::TM;
+    a.tiles_n = (q.N + Cfg::TN - 1) / Cfg::TN;
+    const bool veca = (q.lda % 4 == 0) && (reinterpret_cast<uintptr_t>(q.A) % 16 == 0) && (q.strideA % 4 == 0);
+    dim3 grid(a.tiles_m * a.tiles_n, 1, q.batch);
+    if (veca)
+        hipLaunchKernelGGL((sgemm_small_kernel<Cfg, true>), grid, dim3(Cfg::NT), 0, stream, a);
+    else
+        hipLaunchKernelGGL((sgemm_small_kernel<Cfg, false>), grid, dim3(Cfg::NT), 0, stream, a);
+    return hipGetLastError();
+}
+
+using SgSmall64 = SgSmallCfg<2, 2>;
+using SgSmall32 = SgSmallCfg<1, 1>;
+
 using SgBig = SgCfg<128, 128, 16, 2, 2>;
 
 template <class Cfg>
@@ -461,6 +624,13 @@ hipError_t launch_sgemm(const GemmProblem &q, hipStream_t stream)
     // CU, else 128x128; register-staged 128x128 tiles with bounds checks for
     // everything else.
     const long long t256 = (long long)(q.M / 256) * (q.N / 256) * q.batch;
+    const long long t128 = (long long)((q.M + 127) / 128) * ((q.N + 127) / 128) * q.batch;
+    if (t128 < 256) {
+        // fewer 128x128 tiles than CUs: split K inside smaller workgroup tiles
+        const long long t64 = (long long)((q.M + 63) / 64) * ((q.N + 63) / 64) * q.batch;
+        if (t64 >= 256) return launch_small<SgSmall64>(q, stream);
+        return launch_small<SgSmall32>(q, stream);
+    }
     if (t256 >= 256 && sg_dma_ok<SgDma256>(q)) return launch_sg_dma<SgDma256>(q, stream);
     if (sg_dma_ok<SgDma128>(q)) return launch_sg_dma<SgDma128>(q, stream);
     return launch_cfg<SgBig>(q, stream);

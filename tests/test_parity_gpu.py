@@ -172,6 +172,32 @@ def test_batched_small_full_and_shared_operand():
     batched_check(33, 65, 17, 4, 1.0, 0.0, kind_vals="int4", exact=True, pad=1)
 
 
+@pytest.mark.parametrize("kind", ["f32", "f16"])
+def test_fast_paths_with_padded_leading_dimensions(kind):
+    # whole tiles and 16-byte aligned rows, but every leading dimension larger than
+    # the logical width: the direct-to-LDS kernels must honour lda/ldb/ldc
+    # (SGEMM needs >= 256 tiles of 128x128 before it leaves the split-K small-problem kernel)
+    if kind == "f32":
+        run_and_check(kind, 2048, 2048, 320, 1.5, -0.5, lda=328, ldb=2056, ldc=2060, sample=128)
+    else:
+        run_and_check(kind, 512, 384, 320, 1.5, -0.5, lda=328, ldb=392, ldc=400)
+    run_and_check(kind, 4096, 4096, 256, 1.0, 0.0, lda=264, ldb=4104, ldc=4100, sample=64, c_nan=True)
+
+
+@pytest.mark.parametrize("M,N,K", [(512, 512, 512), (64, 64, 4096), (1000, 100, 3000), (96, 1024, 40)])
+def test_small_problem_split_k(M, N, K):
+    # fewer 128x128 tiles than CUs: the four waves of a workgroup split K and their
+    # partial tiles are summed in a fixed order -- check values, bits and determinism
+    run_and_check("f32", M, N, K, 1.5, -0.5, lda=K + 1)
+    run_and_check("f32", M, N, K, 1.0, 1.0, kind_vals="int4", exact=True, seed=11)
+
+
+def test_batched_whole_tiles_mid_size():
+    # 128x128 whole tiles with K a multiple of 64 (the mid-size direct-to-LDS path), 3 members
+    batched_check(384, 256, 320, 3, 1.5, -0.5)
+    batched_check(256, 384, 512, 2, 1.0, 1.0, kind_vals="int4", exact=True)
+
+
 # ------------------------------------------------------------------ edge cases
 RAGGED = [(1, 1, 1), (1, 7, 3), (3, 1, 5), (2, 3, 1), (33, 65, 17), (127, 129, 63), (129, 127, 65),
           (257, 255, 129), (31, 33, 300), (300, 17, 1000), (17, 300, 8), (65, 64, 9)]
