@@ -229,19 +229,20 @@ __global__ __launch_bounds__(Cfg::NT) void sgemm_mfma_kernel(SgemmArgs p)
 //     puts rows k and k+4 (read by the two half-waves of one MFMA operand) on
 //     different banks.  The B operand of MFMA (u, e) is row 8u+e+4*(lane/32),
 //     column lane%32 -- one ds_read_b32 per lane.
-template <int BM_, int BN_>
+template <int BM_, int BN_, int WM_, int WN_>
 struct SgDmaCfg {
-    static constexpr int BM = BM_, BN = BN_, BK = 32, WM = 2, WN = 2, NT = 256, SLOTS = 2;
+    static constexpr int BM = BM_, BN = BN_, BK = 32, WM = WM_, WN = WN_, SLOTS = 2;
+    static constexpr int NW = WM * WN, NT = 64 * NW;
     static constexpr int TM = BM / WM, TN = BN / WN;
     static constexpr int FM = TM / 32, FN = TN / 32;
     static constexpr int A_BYTES = BM * BK * 4;
     static constexpr int B_BYTES = BK * BN * 4;
     static constexpr int SLOT_BYTES = A_BYTES + B_BYTES;
-    static constexpr int A_LOADS = A_BYTES / 1024 / 4;       // per wave per slice
-    static constexpr int B_LOADS = B_BYTES / 1024 / 4;
+    static constexpr int A_LOADS = A_BYTES / 1024 / NW;      // per wave per slice
+    static constexpr int B_LOADS = B_BYTES / 1024 / NW;
     static constexpr int B_CPR = BN / 4;                     // 16-byte chunks per B row
     static constexpr int B_RPL = 256 / BN;                   // B rows per wave load
-    static_assert(A_BYTES % 4096 == 0 && B_BYTES % 4096 == 0, "slices must split over 4 waves");
+    static_assert(A_BYTES % (1024 * NW) == 0 && B_BYTES % (1024 * NW) == 0, "slices must split over the waves");
     static_assert(SLOTS * SLOT_BYTES <= 160 * 1024, "LDS slots too large");
 };
 
@@ -261,7 +262,7 @@ typedef __attribute__((address_space(3))) f32x4v lds_f32x4;
 typedef __attribute__((address_space(3))) float lds_f32;
 
 template <class Cfg>
-__global__ __launch_bounds__(256) void sgemm_dma_kernel(SgemmArgs p)
+__global__ __launch_bounds__(Cfg::NT) void sgemm_dma_kernel(SgemmArgs p)
 {
     constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK;
     __shared__ __attribute__((aligned(1024))) unsigned char lds[Cfg::SLOTS * Cfg::SLOT_BYTES];
@@ -395,8 +396,10 @@ __global__ __launch_bounds__(256) void sgemm_dma_kernel(SgemmArgs p)
         epilogue(std::false_type{});
 }
 
-using SgDma256 = SgDmaCfg<256, 256>;
-using SgDma128 = SgDmaCfg<128, 128>;
+// 256x256 tiles with eight waves (2 x 4 of 128x64, two per SIMD: one wave's
+// MFMAs cover the other's LDS and barrier latency); 128x128 tiles with four.
+using SgDma256 = SgDmaCfg<256, 256, 2, 4>;
+using SgDma128 = SgDmaCfg<128, 128, 2, 2>;
 
 template <class Cfg>
 bool sg_dma_ok(const GemmProblem &q)
