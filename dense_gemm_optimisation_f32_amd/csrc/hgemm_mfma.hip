@@ -587,7 +587,7 @@ hipError_t launch_cfg(const GemmProblem &q, hipStream_t stream)
 using HgDma256 = HgDmaCfg<256, 256, 2, 2, 4, 64>;
 // 128x128 tile, 4 waves of 64x64, BK = 64, four slots of 32 KB: for grids that
 // 256x256 tiles would leave under-filled.
-using HgDma128 = HgDmaCfg<128, 128, 4, 2, 2, 64>;
+using HgDma128 = HgDmaCfg<128, 128, 4, 2, 4, 64>;
 
 template <class Cfg>
 bool dma_ok(const GemmProblem &q)
