@@ -45,7 +45,7 @@ def _load(path: str = LIB):
         lib = ctypes.CDLL(path)
         fn = lib.oracle_gemm
         fn.restype = ctypes.c_int
-        fn.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_double,
+        fn.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_double,
                        ctypes.c_void_p, ctypes.c_longlong, ctypes.c_void_p, ctypes.c_longlong,
                        ctypes.c_double, ctypes.c_void_p, ctypes.c_longlong,
                        ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
@@ -78,11 +78,12 @@ def _as_f32(x) -> np.ndarray:
 
 def gemm_ref(M: int, N: int, K: int, alpha: float, A, lda: int, B, ldb: int,
              beta: float, C, ldc: int, rows=None, threads: int | None = None,
-             lib_path: str = LIB):
+             lib_path: str = LIB, transA: bool = False, transB: bool = False):
     """(ref, bound) as float64 arrays of shape (len(rows) or M, N).
 
     ``A``, ``B``, ``C`` are flat row-major buffers (see ``seeded_inputs.matrix``);
     ``C`` may be None when ``beta == 0``.  ``rows`` selects output rows.
+    ``transA`` / ``transB``: A is stored K x M / B is stored N x K (op = transpose).
     """
     lib = _load(lib_path)
     a = _as_f32(A) if M * K > 0 else np.zeros(1, np.float32)
@@ -97,7 +98,7 @@ def gemm_ref(M: int, N: int, K: int, alpha: float, A, lda: int, B, ldb: int,
     ref = np.zeros((nrows, N), dtype=np.float64)
     bound = np.zeros((nrows, N), dtype=np.float64)
     rc = lib.oracle_gemm(
-        M, N, K, float(np.float32(alpha)),
+        int(bool(transA)), int(bool(transB)), M, N, K, float(np.float32(alpha)),
         a.ctypes.data, lda, b.ctypes.data, ldb,
         float(np.float32(beta)), c.ctypes.data if c is not None else None, ldc,
         rows_arr.ctypes.data if rows_arr is not None else None, nrows,
@@ -108,7 +109,8 @@ def gemm_ref(M: int, N: int, K: int, alpha: float, A, lda: int, B, ldb: int,
 
 
 def gemm_ref_batched(M, N, K, alpha, A, lda, strideA, B, ldb, strideB, beta, C, ldc,
-                     strideC, batch, rows=None, threads=None, lib_path: str = LIB):
+                     strideC, batch, rows=None, threads=None, lib_path: str = LIB,
+                     transA: bool = False, transB: bool = False):
     """Strided-batched form: member b uses A + b*strideA, B + b*strideB, C + b*strideC.
 
     (MindNotes 'GEMM' page, section "Batched execution and mixed precision":
@@ -120,10 +122,13 @@ def gemm_ref_batched(M, N, K, alpha, A, lda, strideA, B, ldb, strideB, beta, C, 
     c = None if C is None else np.asarray(C).reshape(-1)
     refs, bounds = [], []
     for i in range(batch):
-        ai = a[i * strideA: i * strideA + (M - 1) * lda + K] if M * K else a
-        bi = b[i * strideB: i * strideB + (K - 1) * ldb + N] if K * N else b
+        ar, ac = (K, M) if transA else (M, K)
+        br, bc = (N, K) if transB else (K, N)
+        ai = a[i * strideA: i * strideA + (ar - 1) * lda + ac] if M * K else a
+        bi = b[i * strideB: i * strideB + (br - 1) * ldb + bc] if K * N else b
         ci = None if c is None else c[i * strideC: i * strideC + (M - 1) * ldc + N]
-        r, bd = gemm_ref(M, N, K, alpha, ai, lda, bi, ldb, beta, ci, ldc, rows, threads, lib_path)
+        r, bd = gemm_ref(M, N, K, alpha, ai, lda, bi, ldb, beta, ci, ldc, rows, threads, lib_path,
+                         transA, transB)
         refs.append(r)
         bounds.append(bd)
     return np.stack(refs), np.stack(bounds)

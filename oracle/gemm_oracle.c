@@ -4,12 +4,15 @@
  * check and the benchmark's CPU-baseline leg, never from the product path.
  *
  * What it computes (MindNotes 'GEMM' page, section "core problem and
- * arithmetic characteristics": C = alpha*op(A)op(B) + beta*C with A of size
- * MxK, B of size KxN, C of size MxN, where C[i][j] is the dot product of row i
- * of A with column j of B; op is the identity here):
+ * arithmetic characteristics": C = alpha*op(A)op(B) + beta*C with op(A) of
+ * size MxK, op(B) of size KxN, C of size MxN, where C[i][j] is the dot product
+ * of row i of op(A) with column j of op(B); op is the identity or the
+ * transpose, chosen per operand):
  *
- *     ref[i][j]   = alpha * sum_{k=0}^{K-1} A[i][k]*B[k][j]  + beta * C[i][j]
- *     bound[i][j] = |alpha| * sum_k |A[i][k]|*|B[k][j]|     + |beta| * |C[i][j]|
+ *     ref[i][j]   = alpha * sum_{k=0}^{K-1} a(i,k)*b(k,j)  + beta * C[i][j]
+ *     bound[i][j] = |alpha| * sum_k |a(i,k)|*|b(k,j)|     + |beta| * |C[i][j]|
+ *
+ * with a(i,k) = op(A)[i][k] and b(k,j) = op(B)[k][j].
  *
  * in IEEE double precision.  The loop is the plain triple loop of the ssxxe.cn
  * V100 SGEMM article, section 1.2 (its CPU reference), with the accumulator
@@ -21,8 +24,10 @@
  * product of two of them is exact in double; only the additions round.
  *
  * Storage (MindNotes 'GEMM' page, section "Leading Dimension (lda, ldb, ldc)"):
- * element (i,k) of A is A[i*lda + k], (k,j) of B is B[k*ldb + j], (i,j) of C is
- * C[i*ldc + j]; the ld-width pad at the end of each row is never read.
+ * every matrix is row-major with its own leading dimension.  a(i,k) is
+ * A[i*lda + k], or A[k*lda + i] when A is stored transposed (K x M); b(k,j) is
+ * B[k*ldb + j], or B[j*ldb + k] when B is stored transposed (N x K); (i,j) of C
+ * is C[i*ldc + j].  The ld-width pad at the end of each row is never read.
  *
  * Where the pages say nothing the BLAS reference semantics are taken: C is not
  * read when beta == 0 (so a C full of NaN cannot leak in), A and B are not read
@@ -40,6 +45,7 @@
 #include <stdlib.h>
 
 typedef struct {
+    int transA, transB;
     int M, N, K;
     double alpha, beta;
     const float *A, *B, *C;
@@ -60,13 +66,13 @@ static void oracle_one_row(const oracle_job *jb, int r, double *acc, double *acc
         acc_abs[j] = 0.0;
     }
     if (jb->alpha != 0.0) {
-        const float *arow = jb->A + (size_t)i * (size_t)jb->lda;
         for (int k = 0; k < jb->K; ++k) {
-            const double a = (double)arow[k];
+            const double a = jb->transA ? (double)jb->A[(size_t)k * (size_t)jb->lda + (size_t)i]
+                                        : (double)jb->A[(size_t)i * (size_t)jb->lda + (size_t)k];
             const double a_abs = fabs(a);
-            const float *brow = jb->B + (size_t)k * (size_t)jb->ldb;
             for (int j = 0; j < N; ++j) {
-                const double b = (double)brow[j];
+                const double b = jb->transB ? (double)jb->B[(size_t)j * (size_t)jb->ldb + (size_t)k]
+                                            : (double)jb->B[(size_t)k * (size_t)jb->ldb + (size_t)j];
                 acc[j] += a * b;
                 acc_abs[j] += a_abs * fabs(b);
             }
@@ -108,18 +114,21 @@ static void *oracle_worker(void *arg)
 
 /*
  * oracle_gemm: ref and bound for the rows listed in ``rows`` (or all M rows
- * when rows == NULL, in which case nrows must equal M).  ``C`` may be NULL when
+ * when rows == NULL, in which case nrows must equal M).  transA / transB
+ * (0 or 1) say whether A / B are stored transposed.  ``C`` may be NULL when
  * beta == 0.  Returns 0 on success, -1 on bad arguments, -2 on allocation or
  * thread failure.
  */
-int oracle_gemm(int M, int N, int K, double alpha,
+int oracle_gemm(int transA, int transB, int M, int N, int K, double alpha,
                 const float *A, long long lda, const float *B, long long ldb,
                 double beta, const float *C, long long ldc,
                 const int *rows, int nrows, double *ref, double *bound, int nthreads)
 {
     if (M < 0 || N < 0 || K < 0 || nrows < 0) return -1;
+    if ((transA != 0 && transA != 1) || (transB != 0 && transB != 1)) return -1;
     if (!rows && nrows != M) return -1;
-    if (lda < (K > 1 ? K : 1) || ldb < (N > 1 ? N : 1) || ldc < (N > 1 ? N : 1)) return -1;
+    const int a_cols = transA ? M : K, b_cols = transB ? K : N;
+    if (lda < (a_cols > 1 ? a_cols : 1) || ldb < (b_cols > 1 ? b_cols : 1) || ldc < (N > 1 ? N : 1)) return -1;
     if (beta != 0.0 && !C && nrows > 0 && N > 0) return -1;
     if (rows)
         for (int r = 0; r < nrows; ++r)
@@ -127,6 +136,7 @@ int oracle_gemm(int M, int N, int K, double alpha,
     if (nrows == 0 || N == 0) return 0;
 
     oracle_job jb;
+    jb.transA = transA; jb.transB = transB;
     jb.M = M; jb.N = N; jb.K = K;
     jb.alpha = alpha; jb.beta = beta;
     jb.A = A; jb.B = B; jb.C = C;

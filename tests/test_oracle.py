@@ -206,9 +206,46 @@ def pin_row_subset_and_threads(lib):
     assert np.array_equal(sub, full[rows]) and np.array_equal(sb, fb[rows])
 
 
+def _padded(mat, ld, tail):
+    """Row-major copy of ``mat`` with leading dimension ``ld`` and ``tail`` NaN elements after it."""
+    r, c = mat.shape
+    buf = np.full(r * ld + tail, np.nan, np.float32)
+    buf[: r * ld].reshape(r, ld)[:, :c] = mat
+    return buf
+
+
+def pin_op_storage(lib):
+    """op(A) = A^T and op(B) = B^T (MindNotes definition C = alpha*op(A)op(B) + beta*C): storing
+    the transpose and flagging it gives the same products in the same k order, so all four
+    storage combinations agree bit for bit with the plain problem (which the exact brute force
+    pins).  Buffers carry a NaN tail, so an index that strays past the stored matrix shows."""
+    for (M, N, K) in [(5, 9, 7), (13, 8, 21), (32, 17, 1), (9, 4, 30)]:
+        p = si.gemm_problem(M, N, K, seed=600 + M)
+        A, B = oracle.logical(p["A"], M, K, K), oracle.logical(p["B"], K, N, N)
+        tail = 4 * (M + N + K) * (M + N + K + 8)
+        A_n, A_t = _padded(A, K + 2, tail), _padded(np.ascontiguousarray(A.T), M + 3, tail)
+        B_n, B_t = _padded(B, N + 1, tail), _padded(np.ascontiguousarray(B.T), K + 5, tail)
+        base = None
+        for ta, tb in [(False, False), (True, False), (False, True), (True, True)]:
+            r, b = oracle.gemm_ref(M, N, K, 1.5, A_t if ta else A_n, M + 3 if ta else K + 2,
+                                   B_t if tb else B_n, K + 5 if tb else N + 1, -0.5, p["C"], N,
+                                   lib_path=lib, transA=ta, transB=tb)
+            if base is None:
+                base = (r, b)
+            assert np.array_equal(r, base[0]) and np.array_equal(b, base[1]), f"op {ta},{tb} shape {(M, N, K)}"
+    # The MindNotes row-major trick with op flags: C^T = op(B')op(A') with B' = B stored K x N
+    # read transposed and A' = A stored M x K read transposed gives C^T (N x M).
+    M, K, N = 2, 3, 4
+    p = si.gemm_problem(M, N, K, kind="int4", seed=77)
+    r, _ = oracle.gemm_ref(M, N, K, 1.0, p["A"], K, p["B"], N, 0.0, None, N, lib_path=lib)
+    rt, _ = oracle.gemm_ref(N, M, K, 1.0, p["B"], N, p["A"], K, 0.0, None, M, lib_path=lib,
+                            transA=True, transB=True)
+    assert np.array_equal(rt.T, r)
+
+
 PINS = [pin_identity, pin_permutation, pin_closed_forms, pin_brute_force_exact,
         pin_fp64_rounding_bound, pin_lda_worked_example, pin_transpose_invariant,
-        pin_row_subset_and_threads]
+        pin_row_subset_and_threads, pin_op_storage]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -224,6 +261,11 @@ def test_rejects_bad_arguments():
         oracle.gemm_ref(-1, 4, 4, 1.0, p["A"], 4, p["B"], 4, 0.0, None, 4)
     with pytest.raises(ValueError):
         oracle.gemm_ref(4, 4, 4, 1.0, p["A"], 4, p["B"], 4, 0.0, None, 4, rows=[4])
+    with pytest.raises(ValueError):   # A stored transposed (K x M) needs lda >= M
+        oracle.gemm_ref(5, 4, 3, 1.0, np.zeros(40, np.float32), 4, p["B"], 4, 0.0, None, 4, transA=True)
+    with pytest.raises(ValueError):   # B stored transposed (N x K) needs ldb >= K
+        oracle.gemm_ref(4, 3, 5, 1.0, np.zeros(40, np.float32), 5, np.zeros(40, np.float32), 4, 0.0, None, 3,
+                        transB=True)
 
 
 def test_normalized_error():
@@ -259,19 +301,27 @@ MUTANTS = {
     "alpha_on_c": ("ref[j] = ab + jb->beta * c;", "ref[j] = ab + jb->alpha * c;"),
     "alpha_dropped": ("double ab = jb->alpha != 0.0 ? jb->alpha * acc[j] : 0.0;",
                       "double ab = jb->alpha != 0.0 ? acc[j] : 0.0;"),
-    "b_rows_reversed": ("const float *brow = jb->B + (size_t)k * (size_t)jb->ldb;",
-                        "const float *brow = jb->B + (size_t)(jb->K - 1 - k) * (size_t)jb->ldb;"),
-    "a_index_shifted": ("const double a = (double)arow[k];",
-                        "const double a = (double)arow[(k + 1) % jb->K];"),
-    "b_column_shifted": ("const double b = (double)brow[j];",
-                         "const double b = (double)brow[(j + 1) % N];"),
+    "b_rows_reversed": ("(double)jb->B[(size_t)k * (size_t)jb->ldb + (size_t)j]",
+                        "(double)jb->B[(size_t)(jb->K - 1 - k) * (size_t)jb->ldb + (size_t)j]"),
+    "a_index_shifted": ("(double)jb->A[(size_t)i * (size_t)jb->lda + (size_t)k]",
+                        "(double)jb->A[(size_t)i * (size_t)jb->lda + (size_t)((k + 1) % jb->K)]"),
+    "b_column_shifted": ("(double)jb->B[(size_t)k * (size_t)jb->ldb + (size_t)j]",
+                         "(double)jb->B[(size_t)k * (size_t)jb->ldb + (size_t)((j + 1) % N)]"),
     "bound_signed": ("acc_abs[j] += a_abs * fabs(b);", "acc_abs[j] += a_abs * b;"),
     "c_read_when_beta_zero": ("if (jb->beta != 0.0) {\n            const double c",
                               "if (crow) {\n            const double c"),
-    "a_stride_ignores_lda": ("const float *arow = jb->A + (size_t)i * (size_t)jb->lda;",
-                             "const float *arow = jb->A + (size_t)i * (size_t)jb->K;"),
+    "a_stride_ignores_lda": ("(double)jb->A[(size_t)i * (size_t)jb->lda + (size_t)k]",
+                             "(double)jb->A[(size_t)i * (size_t)jb->K + (size_t)k]"),
     "c_stride_ignores_ldc": ("jb->C + (size_t)i * (size_t)jb->ldc", "jb->C + (size_t)i * (size_t)jb->N"),
     "float_accumulator": ("acc[j] += a * b;", "acc[j] = (double)(float)(acc[j] + a * b);"),
+    "transA_ignored": ("const double a = jb->transA ?", "const double a = 0 ?"),
+    "transB_ignored": ("const double b = jb->transB ?", "const double b = 0 ?"),
+    "transposed_a_ignores_lda": ("(double)jb->A[(size_t)k * (size_t)jb->lda + (size_t)i]",
+                                 "(double)jb->A[(size_t)k * (size_t)jb->M + (size_t)i]"),
+    "transposed_b_ignores_ldb": ("(double)jb->B[(size_t)j * (size_t)jb->ldb + (size_t)k]",
+                                 "(double)jb->B[(size_t)j * (size_t)jb->K + (size_t)k]"),
+    "transposed_a_swapped_index": ("(double)jb->A[(size_t)k * (size_t)jb->lda + (size_t)i]",
+                                   "(double)jb->A[(size_t)i * (size_t)jb->lda + (size_t)k]"),
 }
 
 
