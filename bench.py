@@ -311,6 +311,22 @@ def run_extra(dg, si, np, torch, dev, stream):
     out["hgemm_2048^3"] = {"median_ms": med * 1e3, "tflops": fl / med / 1e12,
                            "frac_of_peak": fl / med / 1e12 / PEAK_F16_TFLOPS}
 
+    # op(A)op(B): the bench shapes with A stored K x M and/or B stored N x K
+    for tA, tB in ((0, 1), (1, 0), (1, 1)):
+        tag = ("T" if tA else "N") + ("T" if tB else "N")
+        for kind, (M, N, K) in (("sgemm", (4096, 4096, 1024)), ("hgemm", (4096, 4096, 4096))):
+            dt = torch.float32 if kind == "sgemm" else torch.float16
+            A = torch.empty(M * K, dtype=dt, device=dev).uniform_(-1, 1)
+            B = torch.empty(K * N, dtype=dt, device=dev).uniform_(-1, 1)
+            C = torch.empty(M * N, dtype=torch.float32, device=dev)
+            lda, ldb = (M if tA else K), (K if tB else N)
+            fn = dg.gemm_f32_ex if kind == "sgemm" else dg.gemm_f16_f32acc_ex
+            med, _ = time_calls(lambda: fn(tA, tB, M, N, K, 1.0, A, lda, B, ldb, 0.0, C, N, stream), torch, stream)
+            fl = 2.0 * M * N * K
+            peak = PEAK_F32_TFLOPS if kind == "sgemm" else PEAK_F16_TFLOPS
+            out[f"{kind}_{tag}_{M}x{N}x{K}"] = {"median_ms": med * 1e3, "tflops": fl / med / 1e12,
+                                                "frac_of_peak": fl / med / 1e12 / peak}
+
     # 16 x 1024^3 batched, beta = 1 (C is read and written: HBM-bound, ridge below the fp16 peak)
     nb, n = 16, 1024
     A = torch.empty(nb * n * n, dtype=torch.float16, device=dev).uniform_(-1, 1)

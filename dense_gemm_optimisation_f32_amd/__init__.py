@@ -1,7 +1,8 @@
 """Python binding of libmi355gemm.so: row-major GEMM on one MI355X.
 
-The three functions take the same arguments as the C ABI in
-``include/mi355gemm.h`` and only marshal them: every step of the computation
+The functions take the same arguments as the C ABI in
+``include/mi355gemm.h`` and only marshal them (the ``_ex`` forms add the
+transA/transB flags of C = alpha*op(A)op(B) + beta*C): every step of the computation
 runs in the library's HIP kernels.  Operands may be torch CUDA tensors (their
 ``data_ptr()`` is passed; dtype, device and storage extent are checked first so
 that a wrong buffer is refused on the host instead of faulting the GPU) or raw
@@ -16,11 +17,13 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["gemm_f32", "gemm_f16_f32acc", "gemm_batched_f16_f32acc", "status_string",
+__all__ = ["gemm_f32", "gemm_f16_f32acc", "gemm_batched_f16_f32acc",
+           "gemm_f32_ex", "gemm_f16_f32acc_ex", "gemm_batched_f16_f32acc_ex", "status_string",
            "GemmError", "GemmLibraryMissing", "LIB_PATH", "load_library", "EXPORTS"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmi355gemm.so")
-EXPORTS = ("gemm_f32", "gemm_f16_f32acc", "gemm_batched_f16_f32acc", "gemm_status_string")
+EXPORTS = ("gemm_f32", "gemm_f16_f32acc", "gemm_batched_f16_f32acc",
+           "gemm_f32_ex", "gemm_f16_f32acc_ex", "gemm_batched_f16_f32acc_ex", "gemm_status_string")
 
 _lib = None
 
@@ -53,6 +56,12 @@ def load_library(path: str = LIB_PATH):
     lib.gemm_f16_f32acc.restype = i
     lib.gemm_batched_f16_f32acc.argtypes = [i, i, i, f, vp, i, ll, vp, i, ll, f, vp, i, ll, i, vp]
     lib.gemm_batched_f16_f32acc.restype = i
+    lib.gemm_f32_ex.argtypes = [i, i] + lib.gemm_f32.argtypes
+    lib.gemm_f32_ex.restype = i
+    lib.gemm_f16_f32acc_ex.argtypes = [i, i] + lib.gemm_f16_f32acc.argtypes
+    lib.gemm_f16_f32acc_ex.restype = i
+    lib.gemm_batched_f16_f32acc_ex.argtypes = [i, i] + lib.gemm_batched_f16_f32acc.argtypes
+    lib.gemm_batched_f16_f32acc_ex.restype = i
     lib.gemm_status_string.argtypes = [i]
     lib.gemm_status_string.restype = ctypes.c_char_p
     if path == LIB_PATH:
@@ -101,11 +110,13 @@ def _stream(stream):
     return stream.cuda_stream
 
 
-def _needs(M, N, K, alpha, lda, ldb, ldc, batch=1, sA=0, sB=0, sC=0):
+def _needs(M, N, K, alpha, lda, ldb, ldc, batch=1, sA=0, sB=0, sC=0, transA=0, transB=0):
     reads_ab = K > 0 and alpha != 0 and M > 0 and N > 0
     nb = max(batch - 1, 0)
-    na = _extent(M, K, lda) + nb * sA if reads_ab else 0
-    nbb = _extent(K, N, ldb) + nb * sB if reads_ab else 0
+    a_rows, a_cols = (K, M) if transA else (M, K)
+    b_rows, b_cols = (N, K) if transB else (K, N)
+    na = _extent(a_rows, a_cols, lda) + nb * sA if reads_ab else 0
+    nbb = _extent(b_rows, b_cols, ldb) + nb * sB if reads_ab else 0
     nc = _extent(M, N, ldc) + nb * sC if batch > 0 else 0
     return na, nbb, nc
 
@@ -143,3 +154,41 @@ def gemm_batched_f16_f32acc(M, N, K, alpha, A, lda, strideA, B, ldb, strideB, be
                                      _stream(stream))
     if rc != 0:
         raise GemmError(rc, "gemm_batched_f16_f32acc")
+
+
+def gemm_f32_ex(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=None) -> None:
+    """C <- alpha*op(A)*op(B) + beta*C, fp32; transA: A stored K x M, transB: B stored N x K."""
+    lib = load_library()
+    tA, tB = int(transA), int(transB)   # values other than 0/1 are refused by the library
+    na, nb, nc = _needs(M, N, K, alpha, lda, ldb, ldc, transA=tA, transB=tB)
+    rc = lib.gemm_f32_ex(tA, tB, M, N, K, alpha, _ptr(A, "A", "torch.float32", na), lda,
+                         _ptr(B, "B", "torch.float32", nb), ldb, beta,
+                         _ptr(C, "C", "torch.float32", nc), ldc, _stream(stream))
+    if rc != 0:
+        raise GemmError(rc, "gemm_f32_ex")
+
+
+def gemm_f16_f32acc_ex(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=None) -> None:
+    """gemm_f16_f32acc with op(A)/op(B) (see gemm_f32_ex)."""
+    lib = load_library()
+    tA, tB = int(transA), int(transB)   # values other than 0/1 are refused by the library
+    na, nb, nc = _needs(M, N, K, alpha, lda, ldb, ldc, transA=tA, transB=tB)
+    rc = lib.gemm_f16_f32acc_ex(tA, tB, M, N, K, alpha, _ptr(A, "A", "torch.float16", na), lda,
+                                _ptr(B, "B", "torch.float16", nb), ldb, beta,
+                                _ptr(C, "C", "torch.float32", nc), ldc, _stream(stream))
+    if rc != 0:
+        raise GemmError(rc, "gemm_f16_f32acc_ex")
+
+
+def gemm_batched_f16_f32acc_ex(transA, transB, M, N, K, alpha, A, lda, strideA, B, ldb, strideB, beta, C, ldc,
+                               strideC, batch_count, stream=None) -> None:
+    """gemm_batched_f16_f32acc with op(A)/op(B) (see gemm_f32_ex)."""
+    lib = load_library()
+    tA, tB = int(transA), int(transB)   # values other than 0/1 are refused by the library
+    na, nb, nc = _needs(M, N, K, alpha, lda, ldb, ldc, batch_count, strideA, strideB, strideC, tA, tB)
+    rc = lib.gemm_batched_f16_f32acc_ex(tA, tB, M, N, K, alpha, _ptr(A, "A", "torch.float16", na), lda, strideA,
+                                        _ptr(B, "B", "torch.float16", nb), ldb, strideB, beta,
+                                        _ptr(C, "C", "torch.float32", nc), ldc, strideC, batch_count,
+                                        _stream(stream))
+    if rc != 0:
+        raise GemmError(rc, "gemm_batched_f16_f32acc_ex")

@@ -32,12 +32,16 @@ bool extent(long long rows, long long cols, long long ld, long long *out)
 
 int check(const GemmProblem &p, size_t elem_in)
 {
+    if ((p.transA != 0 && p.transA != 1) || (p.transB != 0 && p.transB != 1)) return GEMM_ERR_OP;
     if (p.M < 0 || p.N < 0 || p.K < 0 || p.batch < 0) return GEMM_ERR_SIZE;
-    const long long K1 = p.K > 1 ? p.K : 1, N1 = p.N > 1 ? p.N : 1;
-    if (p.lda < K1 || p.ldb < N1 || p.ldc < N1) return GEMM_ERR_LD;
+    // stored shapes: A is M x K (or K x M), B is K x N (or N x K)
+    const long long a_rows = p.transA ? p.K : p.M, a_cols = p.transA ? p.M : p.K;
+    const long long b_rows = p.transB ? p.N : p.K, b_cols = p.transB ? p.K : p.N;
+    const long long N1 = p.N > 1 ? p.N : 1;
+    if (p.lda < (a_cols > 1 ? a_cols : 1) || p.ldb < (b_cols > 1 ? b_cols : 1) || p.ldc < N1) return GEMM_ERR_LD;
     if (p.strideA < 0 || p.strideB < 0 || p.strideC < 0) return GEMM_ERR_LD;
     long long ea, eb, ec;
-    if (!extent(p.M, p.K, p.lda, &ea) || !extent(p.K, p.N, p.ldb, &eb) || !extent(p.M, p.N, p.ldc, &ec))
+    if (!extent(a_rows, a_cols, p.lda, &ea) || !extent(b_rows, b_cols, p.ldb, &eb) || !extent(p.M, p.N, p.ldc, &ec))
         return GEMM_ERR_SIZE;
     if (p.batch > 1 && ec > 0 && p.strideC < ec) return GEMM_ERR_LD;
     if (p.batch > 1) {
@@ -78,10 +82,11 @@ int run(GemmProblem p, size_t elem_in, hipStream_t stream, Launch launch)
     return GEMM_OK;
 }
 
-GemmProblem make(int M, int N, int K, float alpha, const void *A, int lda, long long sA, const void *B, int ldb,
-                 long long sB, float beta, float *C, int ldc, long long sC, int batch)
+GemmProblem make(int tA, int tB, int M, int N, int K, float alpha, const void *A, int lda, long long sA,
+                 const void *B, int ldb, long long sB, float beta, float *C, int ldc, long long sC, int batch)
 {
     GemmProblem p;
+    p.transA = tA; p.transB = tB;
     p.M = M; p.N = N; p.K = K; p.batch = batch;
     p.alpha = alpha; p.beta = beta;
     p.A = A; p.lda = lda; p.strideA = sA;
@@ -94,26 +99,47 @@ GemmProblem make(int M, int N, int K, float alpha, const void *A, int lda, long 
 
 extern "C" {
 
+int gemm_f32_ex(int transA, int transB, int M, int N, int K, float alpha, const float *A, int lda, const float *B,
+                int ldb, float beta, float *C, int ldc, hipStream_t stream)
+{
+    return run(make(transA, transB, M, N, K, alpha, A, lda, 0, B, ldb, 0, beta, C, ldc, 0, 1), sizeof(float),
+               stream, mi355gemm::launch_sgemm);
+}
+
+int gemm_f16_f32acc_ex(int transA, int transB, int M, int N, int K, float alpha, const uint16_t *A, int lda,
+                       const uint16_t *B, int ldb, float beta, float *C, int ldc, hipStream_t stream)
+{
+    return run(make(transA, transB, M, N, K, alpha, A, lda, 0, B, ldb, 0, beta, C, ldc, 0, 1), sizeof(uint16_t),
+               stream, mi355gemm::launch_hgemm);
+}
+
+int gemm_batched_f16_f32acc_ex(int transA, int transB, int M, int N, int K, float alpha, const uint16_t *A, int lda,
+                               long long strideA, const uint16_t *B, int ldb, long long strideB, float beta, float *C,
+                               int ldc, long long strideC, int batch_count, hipStream_t stream)
+{
+    return run(make(transA, transB, M, N, K, alpha, A, lda, strideA, B, ldb, strideB, beta, C, ldc, strideC,
+                    batch_count),
+               sizeof(uint16_t), stream, mi355gemm::launch_hgemm);
+}
+
 int gemm_f32(int M, int N, int K, float alpha, const float *A, int lda, const float *B, int ldb, float beta,
              float *C, int ldc, hipStream_t stream)
 {
-    return run(make(M, N, K, alpha, A, lda, 0, B, ldb, 0, beta, C, ldc, 0, 1), sizeof(float), stream,
-               mi355gemm::launch_sgemm);
+    return gemm_f32_ex(0, 0, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream);
 }
 
 int gemm_f16_f32acc(int M, int N, int K, float alpha, const uint16_t *A, int lda, const uint16_t *B, int ldb,
                     float beta, float *C, int ldc, hipStream_t stream)
 {
-    return run(make(M, N, K, alpha, A, lda, 0, B, ldb, 0, beta, C, ldc, 0, 1), sizeof(uint16_t), stream,
-               mi355gemm::launch_hgemm);
+    return gemm_f16_f32acc_ex(0, 0, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream);
 }
 
 int gemm_batched_f16_f32acc(int M, int N, int K, float alpha, const uint16_t *A, int lda, long long strideA,
                             const uint16_t *B, int ldb, long long strideB, float beta, float *C, int ldc,
                             long long strideC, int batch_count, hipStream_t stream)
 {
-    return run(make(M, N, K, alpha, A, lda, strideA, B, ldb, strideB, beta, C, ldc, strideC, batch_count),
-               sizeof(uint16_t), stream, mi355gemm::launch_hgemm);
+    return gemm_batched_f16_f32acc_ex(0, 0, M, N, K, alpha, A, lda, strideA, B, ldb, strideB, beta, C, ldc, strideC,
+                                      batch_count, stream);
 }
 
 const char *gemm_status_string(int status)
@@ -125,6 +151,7 @@ const char *gemm_status_string(int status)
     case GEMM_ERR_NULL: return "NULL pointer for an operand the call reads or writes";
     case GEMM_ERR_ALIGN: return "pointer not aligned to its element size";
     case GEMM_ERR_LAUNCH: return "the HIP runtime refused a kernel launch";
+    case GEMM_ERR_OP: return "transpose flag is neither 0 nor 1";
     default: return "unknown status";
     }
 }

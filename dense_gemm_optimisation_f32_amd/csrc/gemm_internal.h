@@ -10,6 +10,7 @@ namespace mi355gemm {
 // One (possibly batched) row-major GEMM after argument checking.  Offsets are
 // 64-bit; strides are in elements.
 struct GemmProblem {
+    int transA, transB;   // A stored K x M / B stored N x K
     int M, N, K, batch;
     float alpha, beta;
     const void *A;
@@ -20,7 +21,7 @@ struct GemmProblem {
     long long ldc, strideC;
 };
 
-// fp32 SGEMM on fp32 MFMA (K > 0, alpha != 0, M, N > 0).
+// fp32 SGEMM on fp32 MFMA (K > 0, alpha != 0, M, N > 0; any transA/transB).
 hipError_t launch_sgemm(const GemmProblem &p, hipStream_t stream);
 // fp16-input, fp32-accumulate GEMM on fp16 MFMA (same preconditions).
 hipError_t launch_hgemm(const GemmProblem &p, hipStream_t stream);

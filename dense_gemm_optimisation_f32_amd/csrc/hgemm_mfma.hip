@@ -31,6 +31,18 @@
 // Two instantiations per tile shape: MASK = false for problems made of whole
 // tiles with 16-byte aligned rows (no bounds checks anywhere), MASK = true for
 // everything else (out-of-range elements load as zero, stores are masked).
+//
+// Transposed operands (C = alpha*op(A)op(B) + beta*C, the MindNotes 'GEMM'
+// page, section "core problem and arithmetic characteristics"): each kernel is
+// instantiated for the four storage combinations.  An operand tile is copied
+// to LDS in its stored orientation (16-byte loads along the contiguous
+// dimension), and the operand fragment is read in the way that layout calls
+// for: a K-contiguous operand (A stored M x K, B stored N x K) in swizzled
+// 128-byte rows read with one ds_read_b128 per lane, an MN-contiguous operand
+// (A stored K x M, B stored K x N) in [k][mn] rows read with two
+// ds_read_b64_tr_b16.  Both reads hand lane l the same eight k
+// (8*(l/32) .. +7 of the 16-k substep), so the four combinations add the same
+// products in the same order.
 #include "gemm_internal.h"
 #include "tile_order.h"
 #include "epilogue.h"
@@ -63,15 +75,24 @@ struct HgCfg {
     static constexpr int BM = BM_, BN = BN_, BK = 64, WM = 2, WN = 2, NT = 256;
     static constexpr int TM = BM / WM, TN = BN / WN;
     static constexpr int FM = TM / 32, FN = TN / 32;
-    static constexpr int CPR = BK / 8;                 // 16-byte chunks per A row
-    static constexpr int LDB = BN + 32;                // B row pitch in halves (64-byte pad)
-    static constexpr int A_HALVES = BM * BK;
-    static constexpr int B_HALVES = BK * LDB;
-    static constexpr int BUF_HALVES = A_HALVES + B_HALVES;
-    static constexpr int A_LOADS = BM * CPR / NT;      // 16-byte A chunks per thread
-    static constexpr int B_LOADS = BK * (BN / 8) / NT; // 16-byte B chunks per thread
-    static_assert(BM * CPR % NT == 0 && BK * (BN / 8) % NT == 0, "tile loads must split evenly");
     static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be whole MFMA blocks");
+};
+
+// One operand tile of the register-staged kernel: R rows or columns of the
+// output (BM for A, BN for B) by BK k.  KC: stored K-contiguous, kept in LDS
+// as R rows of BK halves with swizzled 16-byte chunks; otherwise stored
+// MN-contiguous, kept as BK rows of R halves plus a 64-byte pad.
+template <bool KC, int R, int BK, int NT>
+struct HgTile {
+    static constexpr bool KCONTIG = KC;
+    static constexpr int ROWS = KC ? R : BK;         // rows as stored
+    static constexpr int COLS = KC ? BK : R;         // contiguous halves per stored row
+    static constexpr int CPR = COLS / 8;             // 16-byte chunks per stored row
+    static constexpr int LOADS = ROWS * CPR / NT;    // 16-byte chunks per thread
+    static constexpr int PITCH = KC ? BK : R + 32;   // LDS row pitch (halves)
+    static constexpr int HALVES = ROWS * PITCH;
+    static_assert((ROWS * CPR) % NT == 0, "tile loads must split evenly");
+    static_assert(!KC || BK == 64, "K-contiguous LDS rows are eight 16-byte chunks");
 };
 
 __device__ __forceinline__ int swz(int row, int chunk)
@@ -93,11 +114,29 @@ __device__ __forceinline__ u32x4 load8_masked(const uint16_t *p, int valid)
     return v;
 }
 
-template <class Cfg, bool MASK, bool VEC>
+// Eight consecutive halves (r, c..c+7) of a row-major rows x cols matrix X;
+// with MASK, elements outside it read as zero (VEC: one 16-byte load where all
+// eight are inside).
+template <bool MASK, bool VEC>
+__device__ __forceinline__ u32x4 load8(const uint16_t *X, long long ld, long long r, long long c, long long rows,
+                                       long long cols)
+{
+    const uint16_t *src = X + r * ld + c;
+    if (!MASK) return *reinterpret_cast<const u32x4 *>(src);
+    if (r >= rows || c >= cols) return u32x4{0u, 0u, 0u, 0u};
+    if (VEC && c + 8 <= cols) return *reinterpret_cast<const u32x4 *>(src);
+    return load8_masked(src, (int)(cols - c));
+}
+
+// TA: A stored K x M; TB: B stored N x K.
+template <class Cfg, bool MASK, bool VEC, bool TA, bool TB>
 __global__ __launch_bounds__(256) void hgemm_mfma_kernel(HgemmArgs p)
 {
-    constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, CPR = Cfg::CPR, LDB = Cfg::LDB;
-    __shared__ __attribute__((aligned(16))) uint16_t lds[2 * Cfg::BUF_HALVES];
+    constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, NT = Cfg::NT;
+    using TileA = HgTile<!TA, BM, BK, NT>;
+    using TileB = HgTile<TB, BN, BK, NT>;
+    constexpr int BUF_HALVES = TileA::HALVES + TileB::HALVES;
+    __shared__ __attribute__((aligned(16))) uint16_t lds[2 * BUF_HALVES];
 
     const int tid = threadIdx.x;
     int tm, tn;
@@ -109,72 +148,40 @@ __global__ __launch_bounds__(256) void hgemm_mfma_kernel(HgemmArgs p)
     float *C = p.C + (long long)blockIdx.z * p.sC;
     const long long lda = p.lda, ldb = p.ldb, ldc = p.ldc;
 
-    u32x4 ra[Cfg::A_LOADS], rb[Cfg::B_LOADS];
-
-    // Lane parts of the global addresses (bytes, fixed for the whole K loop);
-    // the rest of each address is uniform across the workgroup and lives in
-    // scalar registers.
-    const unsigned a_lane_off = (unsigned)((tid / CPR) * lda + (tid % CPR) * 8) * 2u;
-    const unsigned b_lane_off = (unsigned)((tid / (BN / 8)) * ldb + (tid % (BN / 8)) * 8) * 2u;
-    constexpr int A_ROWS_PER_LOAD = Cfg::NT / CPR;       // rows covered by one load of all threads
-    constexpr int B_ROWS_PER_LOAD = Cfg::NT / (BN / 8);
+    u32x4 ra[TileA::LOADS], rb[TileB::LOADS];
 
     auto load_tiles = [&](int k0) {
 #pragma unroll
-        for (int i = 0; i < Cfg::A_LOADS; ++i) {
-            if (!MASK) {
-                const char *base = reinterpret_cast<const char *>(A + (m0 + i * A_ROWS_PER_LOAD) * lda + k0);
-                ra[i] = *reinterpret_cast<const u32x4 *>(base + a_lane_off);
-                continue;
-            }
-            const int id = i * Cfg::NT + tid;
-            const int row = id / CPR, kc = (id % CPR) * 8;
-            const long long gm = m0 + row;
-            const int gk = k0 + kc;
-            const uint16_t *src = A + gm * lda + gk;
-            if (gm >= M || gk >= K)
-                ra[i] = u32x4{0u, 0u, 0u, 0u};
-            else if (VEC && gk + 8 <= K)
-                ra[i] = *reinterpret_cast<const u32x4 *>(src);
-            else
-                ra[i] = load8_masked(src, K - gk);
+        for (int i = 0; i < TileA::LOADS; ++i) {
+            const int id = i * NT + tid;
+            const int r = id / TileA::CPR, c = (id % TileA::CPR) * 8;
+            ra[i] = TA ? load8<MASK, VEC>(A, lda, k0 + r, m0 + c, K, M) : load8<MASK, VEC>(A, lda, m0 + r, k0 + c, M, K);
         }
 #pragma unroll
-        for (int i = 0; i < Cfg::B_LOADS; ++i) {
-            if (!MASK) {
-                const char *base = reinterpret_cast<const char *>(B + (long long)(k0 + i * B_ROWS_PER_LOAD) * ldb + n0);
-                rb[i] = *reinterpret_cast<const u32x4 *>(base + b_lane_off);
-                continue;
-            }
-            const int id = i * Cfg::NT + tid;
-            const int kr = id / (BN / 8), nc = (id % (BN / 8)) * 8;
-            const int gk = k0 + kr;
-            const long long gn = n0 + nc;
-            const uint16_t *src = B + (long long)gk * ldb + gn;
-            if (gk >= K || gn >= N)
-                rb[i] = u32x4{0u, 0u, 0u, 0u};
-            else if (VEC && gn + 8 <= N)
-                rb[i] = *reinterpret_cast<const u32x4 *>(src);
-            else
-                rb[i] = load8_masked(src, (int)(N - gn));
+        for (int i = 0; i < TileB::LOADS; ++i) {
+            const int id = i * NT + tid;
+            const int r = id / TileB::CPR, c = (id % TileB::CPR) * 8;
+            rb[i] = TB ? load8<MASK, VEC>(B, ldb, n0 + r, k0 + c, N, K) : load8<MASK, VEC>(B, ldb, k0 + r, n0 + c, K, N);
         }
     };
 
+    // K-contiguous rows go to swizzled chunks, MN-contiguous rows to padded rows.
+    auto store_one = [&](auto tile, uint16_t *dst, int i, const u32x4 &v) {
+        using T = decltype(tile);
+        const int id = i * NT + tid;
+        const int r = id / T::CPR, c = id % T::CPR;
+        if constexpr (T::KCONTIG)
+            *reinterpret_cast<u32x4 *>(dst + r * BK + 8 * swz(r, c)) = v;
+        else
+            *reinterpret_cast<u32x4 *>(dst + r * T::PITCH + 8 * c) = v;
+    };
     auto store_tiles = [&](int buf) {
-        uint16_t *la = lds + buf * Cfg::BUF_HALVES;
-        uint16_t *lb = la + Cfg::A_HALVES;
+        uint16_t *la = lds + buf * BUF_HALVES;
+        uint16_t *lb = la + TileA::HALVES;
 #pragma unroll
-        for (int i = 0; i < Cfg::A_LOADS; ++i) {
-            const int id = i * Cfg::NT + tid;
-            const int row = id / CPR, c = id % CPR;
-            *reinterpret_cast<u32x4 *>(la + row * BK + 8 * swz(row, c)) = ra[i];
-        }
+        for (int i = 0; i < TileA::LOADS; ++i) store_one(TileA{}, la, i, ra[i]);
 #pragma unroll
-        for (int i = 0; i < Cfg::B_LOADS; ++i) {
-            const int id = i * Cfg::NT + tid;
-            const int kr = id / (BN / 8), nc = (id % (BN / 8)) * 8;
-            *reinterpret_cast<u32x4 *>(lb + kr * LDB + nc) = rb[i];
-        }
+        for (int i = 0; i < TileB::LOADS; ++i) store_one(TileB{}, lb, i, rb[i]);
     };
 
     const int wave = tid >> 6, lane = tid & 63;
@@ -182,8 +189,8 @@ __global__ __launch_bounds__(256) void hgemm_mfma_kernel(HgemmArgs p)
     const int lr = lane & 31, lk = lane >> 5;
     // transposed-read lane roles: group q of 16 lanes, lane j within it
     const int q = lane >> 4, j = lane & 15;
-    const int tr_row = 8 * (q >> 1) + (j >> 2);                         // + 16*s + 4*h
-    const int tr_col = wn * Cfg::TN + 16 * (q & 1) + 4 * (j & 3);        // + 32*bn
+    const int tr_row = 8 * (q >> 1) + (j >> 2);   // + 16*s + 4*h
+    const int tr_col = 16 * (q & 1) + 4 * (j & 3);  // + wave offset + 32*block
 
     f32x16 acc[Cfg::FM][Cfg::FN];
 #pragma unroll
@@ -193,27 +200,33 @@ __global__ __launch_bounds__(256) void hgemm_mfma_kernel(HgemmArgs p)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][jj][r] = 0.f;
 
+    // Fragment of 32 output rows (or columns) starting at `first`, for the
+    // 16-wide k substep s: lane l gets row/column first + l%32 and the eight k
+    // 16s + 8*(l/32) .. +7.
+    auto read_frag = [&](auto tile, const uint16_t *base, int first, int s) -> half8 {
+        using T = decltype(tile);
+        if constexpr (T::KCONTIG) {
+            const int row = first + lr;
+            return *reinterpret_cast<const half8 *>(base + row * BK + 8 * swz(row, 2 * s + lk));
+        } else {
+            const uint16_t *at = base + (16 * s + tr_row) * T::PITCH + first + tr_col;
+            const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4 *)(at));
+            const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4 *)(at + 4 * T::PITCH));
+            const short4v both[2] = {lo, hi};
+            return __builtin_bit_cast(half8, both);
+        }
+    };
     // Operand fragments of one 16-wide k substep, double-buffered in registers:
     // the fragments of substep s+1 are read from LDS while the MFMAs of
     // substep s run.
     half8 fa[2][Cfg::FM], fb[2][Cfg::FN];
     auto read_frags = [&](int buf, int s, half8 *a, half8 *b) {
-        const uint16_t *la = lds + buf * Cfg::BUF_HALVES;
-        const uint16_t *lb = la + Cfg::A_HALVES;
-        const int c = 2 * s + lk;   // A chunk: halves 16s + 8*lk .. +7
+        const uint16_t *la = lds + buf * BUF_HALVES;
+        const uint16_t *lb = la + TileA::HALVES;
 #pragma unroll
-        for (int i = 0; i < Cfg::FM; ++i) {
-            const int row = wm * Cfg::TM + 32 * i + lr;
-            a[i] = *reinterpret_cast<const half8 *>(la + row * BK + 8 * swz(row, c));
-        }
+        for (int i = 0; i < Cfg::FM; ++i) a[i] = read_frag(TileA{}, la, wm * Cfg::TM + 32 * i, s);
 #pragma unroll
-        for (int jj = 0; jj < Cfg::FN; ++jj) {
-            const uint16_t *base = lb + (16 * s + tr_row) * LDB + tr_col + 32 * jj;
-            const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4 *)(base));
-            const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4 *)(base + 4 * LDB));
-            const short4v both[2] = {lo, hi};
-            b[jj] = __builtin_bit_cast(half8, both);
-        }
+        for (int jj = 0; jj < Cfg::FN; ++jj) b[jj] = read_frag(TileB{}, lb, wn * Cfg::TN + 32 * jj, s);
     };
     auto mfmas = [&](const half8 *a, const half8 *b) {
 #pragma unroll
@@ -290,14 +303,18 @@ __global__ __launch_bounds__(256) void hgemm_mfma_kernel(HgemmArgs p)
 // STAGES slices of BK k in LDS and fetches slice t+STAGES while slice t is
 // computed.  Because a wave's load fills 1 KB of LDS contiguously, the
 // swizzled layouts are produced by choosing, per lane, which global chunk to
-// fetch for the LDS position the lane owns:
-//   * A slice: BM rows of BK halves (four or eight 16-byte k chunks); the
-//     chunk at physical position p of row r holds logical chunk p ^ swz_a(r);
-//   * B slice: BK rows of BN halves (row-major [k][n]); the chunk at physical
-//     position p of row k holds logical chunk p ^ swz_b(k).
+// fetch for the LDS position the lane owns.  Each operand slice keeps its
+// stored orientation:
+//   * K-contiguous (A stored M x K, B stored N x K): R rows (R = BM or BN) of
+//     BK halves (four or eight 16-byte k chunks); the chunk at physical
+//     position p of row r holds logical chunk p ^ swz_a(r); one ds_read_b128
+//     per lane and fragment;
+//   * MN-contiguous (A stored K x M, B stored K x N): BK rows of R halves; the
+//     chunk at physical position p of row k holds logical chunk p ^ swz_b(k);
+//     two ds_read_b64_tr_b16 per lane and fragment.
 // swz_a keeps the rows one LDS cycle serves on distinct banks for the 16-byte
-// A operand reads; swz_b does the same for the four rows a transposed B read
-// touches (measured conflict-free on gfx950 for 128- and 256-byte windows).
+// reads; swz_b does the same for the four rows a transposed read touches
+// (measured conflict-free on gfx950 for 128- and 256-byte windows).
 // The workgroup runs WM x WN waves; with eight waves two share each SIMD, so
 // one wave's MFMAs cover the other's LDS latency.
 // Requires M % BM == 0, N % BN == 0, K % BK == 0, K >= STAGES*BK, 16-byte
@@ -314,10 +331,8 @@ struct HgDmaCfg {
     static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
     static constexpr int A_LOADS = A_BYTES / 1024 / NW;         // per wave per slice
     static constexpr int B_LOADS = B_BYTES / 1024 / NW;
-    static constexpr int B_CPR = BN / 8;                        // 16-byte chunks per B row
-    static constexpr int B_RPL = 64 / B_CPR;                    // B rows per wave load
     static_assert(A_BYTES % (1024 * NW) == 0 && B_BYTES % (1024 * NW) == 0, "slices must split over the waves");
-    static_assert(A_CPR == 4 || A_CPR == 8, "A rows of 64 or 128 bytes");
+    static_assert(A_CPR == 4 || A_CPR == 8, "K-contiguous rows of 64 or 128 bytes");
     static_assert(STAGES * STAGE_BYTES <= 160 * 1024, "LDS ring too large");
 };
 
@@ -367,10 +382,46 @@ __device__ __forceinline__ void wait_vmcnt()
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-template <class Cfg>
+// Per-lane byte offset (within one slice of global memory) of the 16-byte
+// chunk that lane `lane` of wave load g fetches for an operand slice of R rows
+// or columns and BK k; see the layouts above.
+template <bool KC, int R, int BK>
+__device__ __forceinline__ unsigned dma_offset(int g, int lane, long long ld)
+{
+    if (KC) {
+        constexpr int CPR = BK / 8;
+        const int r = (64 / CPR) * g + lane / CPR;
+        return (unsigned)(r * ld + 8 * ((lane % CPR) ^ swz_a<CPR>(r))) * 2u;
+    }
+    constexpr int CPR = R / 8, RPL = 64 / CPR;   // chunks per row, rows per wave load
+    const int k = RPL * g + lane / CPR;
+    return (unsigned)(k * ld + 8 * ((lane % CPR) ^ swz_b(k))) * 2u;
+}
+
+// Fragment read address (bytes within a slot, substep 0, MFMA block 0) for the
+// lane; KC: the rows start at `first`, MN-contiguous: the columns do.
+// K-contiguous fragments of substep s and block i add 16*(s-chunk XOR) and
+// i*32 rows; MN-contiguous ones add 16*s rows and 32*i columns.
+template <bool KC, int R, int BK>
+__device__ __forceinline__ unsigned frag_offset(int first, int lane, int s)
+{
+    const int lr = lane & 31, lk = lane >> 5, q = lane >> 4, j = lane & 15;
+    if (KC) {
+        const int r = first + lr;
+        return (unsigned)(r * BK * 2 + 16 * ((2 * s + lk) ^ swz_a<BK / 8>(r)));
+    }
+    const int kq = 8 * (q >> 1) + (j >> 2);     // row within a 16-row substep (plus 4*h)
+    const int n = first + 16 * (q & 1) + 4 * (j & 3);
+    return (unsigned)(kq * R * 2 + 16 * ((n >> 3) ^ swz_b(kq)) + 2 * (n & 7));
+}
+
+// TA: A stored K x M; TB: B stored N x K.
+template <class Cfg, bool TA, bool TB>
 __global__ __launch_bounds__(Cfg::NT) void hgemm_dma_kernel(HgemmArgs p)
 {
     constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, S = Cfg::STAGES;
+    constexpr bool A_KC = !TA, B_KC = TB;
+    static_assert((A_KC || BM >= 128) && (B_KC || BN >= 128), "MN-contiguous slices need 16 chunks per row");
     __shared__ __attribute__((aligned(1024))) unsigned char lds[S * Cfg::STAGE_BYTES];
     const unsigned lds0 = (unsigned)(uintptr_t)lds;
 
@@ -379,29 +430,23 @@ __global__ __launch_bounds__(Cfg::NT) void hgemm_dma_kernel(HgemmArgs p)
     tile_coords(blockIdx.x, p.tiles_m, p.tiles_n, &tm, &tn);
     const long long m0 = (long long)tm * BM, n0 = (long long)tn * BN;
     const long long lda = p.lda, ldb = p.ldb, ldc = p.ldc;
-    const char *Ab = reinterpret_cast<const char *>(p.A + (long long)blockIdx.z * p.sA + m0 * lda);
-    const char *Bb = reinterpret_cast<const char *>(p.B + (long long)blockIdx.z * p.sB + n0);
+    // first element of the tile's slice 0 in each operand, and the bytes
+    // between consecutive slices
+    const char *Ab = reinterpret_cast<const char *>(p.A + (long long)blockIdx.z * p.sA + (A_KC ? m0 * lda : m0));
+    const char *Bb = reinterpret_cast<const char *>(p.B + (long long)blockIdx.z * p.sB + (B_KC ? n0 * ldb : n0));
+    const long long stepA = A_KC ? BK * 2 : BK * lda * 2;
+    const long long stepB = B_KC ? BK * 2 : BK * ldb * 2;
     float *C = p.C + (long long)blockIdx.z * p.sC;
 
-    // Per-lane byte offsets of the chunks this lane fetches (relative to the
-    // slice's first row and, for B, the tile's first column).
     unsigned offA[Cfg::A_LOADS], offB[Cfg::B_LOADS];
 #pragma unroll
-    for (int i = 0; i < Cfg::A_LOADS; ++i) {
-        const int g = wave * Cfg::A_LOADS + i;
-        const int r = (64 / Cfg::A_CPR) * g + lane / Cfg::A_CPR;
-        offA[i] = (unsigned)(r * lda + 8 * ((lane % Cfg::A_CPR) ^ swz_a<Cfg::A_CPR>(r))) * 2u;
-    }
+    for (int i = 0; i < Cfg::A_LOADS; ++i) offA[i] = dma_offset<A_KC, BM, BK>(wave * Cfg::A_LOADS + i, lane, lda);
 #pragma unroll
-    for (int i = 0; i < Cfg::B_LOADS; ++i) {
-        const int g = wave * Cfg::B_LOADS + i;
-        const int k = Cfg::B_RPL * g + lane / Cfg::B_CPR;
-        offB[i] = (unsigned)(k * ldb + 8 * ((lane % Cfg::B_CPR) ^ swz_b(k))) * 2u;
-    }
+    for (int i = 0; i < Cfg::B_LOADS; ++i) offB[i] = dma_offset<B_KC, BN, BK>(wave * Cfg::B_LOADS + i, lane, ldb);
     const int uwave = __builtin_amdgcn_readfirstlane(wave);
     auto issue_slice = [&](int kt, int slot) {
-        const char *a = Ab + (long long)kt * BK * 2;
-        const char *b = Bb + (long long)kt * BK * ldb * 2;
+        const char *a = Ab + (long long)kt * stepA;
+        const char *b = Bb + (long long)kt * stepB;
         const unsigned la = lds0 + slot * Cfg::STAGE_BYTES + uwave * Cfg::A_LOADS * 1024;
         const unsigned lb = lds0 + slot * Cfg::STAGE_BYTES + Cfg::A_BYTES + uwave * Cfg::B_LOADS * 1024;
 #pragma unroll
@@ -411,22 +456,23 @@ __global__ __launch_bounds__(Cfg::NT) void hgemm_dma_kernel(HgemmArgs p)
     };
     constexpr int LOADS = Cfg::A_LOADS + Cfg::B_LOADS;   // vector-memory ops per slice per lane
 
-    // Fragment read addresses (bytes, without the slot base).
+    // Fragment read addresses (bytes, without the slot base): per substep for a
+    // K-contiguous operand (blocks are 32 rows apart, which the swizzle
+    // ignores), per block for an MN-contiguous one (substeps are 16 rows
+    // apart, which the swizzle ignores too).
     const int wm = wave / Cfg::WN, wn = wave % Cfg::WN;
-    const int lr = lane & 31, lk = lane >> 5, q = lane >> 4, j = lane & 15;
-    unsigned fragA[BK / 16];
+    const int lr = lane & 31, lk = lane >> 5;
+    constexpr int NS = BK / 16;
+    constexpr int NFA = A_KC ? NS : Cfg::FM, NFB = B_KC ? NS : Cfg::FN;
+    unsigned fragA[NFA], fragB[NFB];
 #pragma unroll
-    for (int s = 0; s < BK / 16; ++s) {
-        const int r = wm * Cfg::TM + lr;
-        fragA[s] = (unsigned)(r * BK * 2 + 16 * ((2 * s + lk) ^ swz_a<Cfg::A_CPR>(r)));
-    }
-    unsigned fragB[Cfg::FN];
-    const int kq = 8 * (q >> 1) + (j >> 2);     // row within a 16-row substep (plus 4*h)
+    for (int x = 0; x < NFA; ++x)
+        fragA[x] = A_KC ? frag_offset<true, BM, BK>(wm * Cfg::TM, lane, x)
+                        : frag_offset<false, BM, BK>(wm * Cfg::TM + 32 * x, lane, 0);
 #pragma unroll
-    for (int jj = 0; jj < Cfg::FN; ++jj) {
-        const int n = wn * Cfg::TN + 32 * jj + 16 * (q & 1) + 4 * (j & 3);
-        fragB[jj] = (unsigned)(Cfg::A_BYTES + kq * BN * 2 + 16 * ((n >> 3) ^ swz_b(kq)) + 2 * (n & 7));
-    }
+    for (int x = 0; x < NFB; ++x)
+        fragB[x] = Cfg::A_BYTES + (B_KC ? frag_offset<true, BN, BK>(wn * Cfg::TN, lane, x)
+                                        : frag_offset<false, BN, BK>(wn * Cfg::TN + 32 * x, lane, 0));
 
     f32x16 acc[Cfg::FM][Cfg::FN];
 #pragma unroll
@@ -436,20 +482,28 @@ __global__ __launch_bounds__(Cfg::NT) void hgemm_dma_kernel(HgemmArgs p)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][jj][r] = 0.f;
 
+    // Fragment x (MFMA block) of substep s of an operand with R rows/columns.
+    auto frag = [&](auto kc, auto rr, unsigned base, const unsigned *off, int x, int s) -> half8 {
+        constexpr int R = decltype(rr)::value;
+        if constexpr (decltype(kc)::value) {
+            return *(const lds_half8 *)(uintptr_t)(base + off[s] + x * 32 * BK * 2);
+        } else {
+            const unsigned at = base + off[x] + 16 * s * R * 2;
+            const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4 *)(uintptr_t)at);
+            const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4 *)(uintptr_t)(at + 4 * R * 2));
+            const short4v both[2] = {lo, hi};
+            return __builtin_bit_cast(half8, both);
+        }
+    };
     half8 fa[2][Cfg::FM], fb[2][Cfg::FN];
     auto read_frags = [&](int slot, int s, half8 *a, half8 *b) {
         const unsigned base = lds0 + slot * Cfg::STAGE_BYTES;
 #pragma unroll
         for (int i = 0; i < Cfg::FM; ++i)
-            a[i] = *(const lds_half8 *)(uintptr_t)(base + fragA[s] + i * 32 * BK * 2);
+            a[i] = frag(std::bool_constant<A_KC>{}, std::integral_constant<int, BM>{}, base, fragA, i, s);
 #pragma unroll
-        for (int jj = 0; jj < Cfg::FN; ++jj) {
-            const unsigned bb = base + fragB[jj] + 16 * s * BN * 2;
-            const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4 *)(uintptr_t)bb);
-            const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4 *)(uintptr_t)(bb + 4 * BN * 2));
-            const short4v both[2] = {lo, hi};
-            b[jj] = __builtin_bit_cast(half8, both);
-        }
+        for (int jj = 0; jj < Cfg::FN; ++jj)
+            b[jj] = frag(std::bool_constant<B_KC>{}, std::integral_constant<int, BN>{}, base, fragB, jj, s);
     };
     auto mfmas = [&](const half8 *a, const half8 *b) {
 #pragma unroll
@@ -478,7 +532,6 @@ __global__ __launch_bounds__(Cfg::NT) void hgemm_dma_kernel(HgemmArgs p)
     // outstanding slices, then the barrier) and every wave holds its slice-t
     // fragments, slot t % S is refilled with slice t+S and the first fragments
     // of slice t+1 are read while the last substep of slice t is computed.
-    constexpr int NS = BK / 16;
     auto step = [&](int t, auto pending, auto refill) {
         const int slot = t % S;
 #pragma unroll
@@ -554,6 +607,18 @@ __global__ __launch_bounds__(Cfg::NT) void hgemm_dma_kernel(HgemmArgs p)
 
 using Hg128 = HgCfg<128, 128>;
 
+template <class Cfg, bool TA, bool TB>
+void launch_cfg_kernel(const HgemmArgs &a, bool whole, bool vec, dim3 grid, hipStream_t stream)
+{
+    const dim3 block(Cfg::NT);
+    if (whole)
+        hipLaunchKernelGGL((hgemm_mfma_kernel<Cfg, false, true, TA, TB>), grid, block, 0, stream, a);
+    else if (vec)
+        hipLaunchKernelGGL((hgemm_mfma_kernel<Cfg, true, true, TA, TB>), grid, block, 0, stream, a);
+    else
+        hipLaunchKernelGGL((hgemm_mfma_kernel<Cfg, true, false, TA, TB>), grid, block, 0, stream, a);
+}
+
 template <class Cfg>
 hipError_t launch_cfg(const GemmProblem &q, hipStream_t stream)
 {
@@ -570,14 +635,15 @@ hipError_t launch_cfg(const GemmProblem &q, hipStream_t stream)
                      (reinterpret_cast<uintptr_t>(q.B) % 16 == 0) &&
                      (q.strideA % 8 == 0) && (q.strideB % 8 == 0);
     const bool whole = vec && q.M % Cfg::BM == 0 && q.N % Cfg::BN == 0 && q.K % Cfg::BK == 0;
-    dim3 grid(a.tiles_m * a.tiles_n, 1, q.batch);
-    dim3 block(Cfg::NT);
-    if (whole)
-        hipLaunchKernelGGL((hgemm_mfma_kernel<Cfg, false, true>), grid, block, 0, stream, a);
-    else if (vec)
-        hipLaunchKernelGGL((hgemm_mfma_kernel<Cfg, true, true>), grid, block, 0, stream, a);
+    const dim3 grid(a.tiles_m * a.tiles_n, 1, q.batch);
+    if (!q.transA && !q.transB)
+        launch_cfg_kernel<Cfg, false, false>(a, whole, vec, grid, stream);
+    else if (!q.transA)
+        launch_cfg_kernel<Cfg, false, true>(a, whole, vec, grid, stream);
+    else if (!q.transB)
+        launch_cfg_kernel<Cfg, true, false>(a, whole, vec, grid, stream);
     else
-        hipLaunchKernelGGL((hgemm_mfma_kernel<Cfg, true, false>), grid, block, 0, stream, a);
+        launch_cfg_kernel<Cfg, true, true>(a, whole, vec, grid, stream);
     return hipGetLastError();
 }
 
@@ -597,7 +663,9 @@ bool dma_ok(const GemmProblem &q)
                          (reinterpret_cast<uintptr_t>(q.B) % 16 == 0);
     const bool whole = q.M % Cfg::BM == 0 && q.N % Cfg::BN == 0 && q.K % Cfg::BK == 0 &&
                        q.K >= Cfg::BK * Cfg::STAGES;
-    const bool fits = (long long)Cfg::BM * q.lda * 2 < (1LL << 31) && (long long)Cfg::BK * q.ldb * 2 < (1LL << 31);
+    // per-lane offsets within one slice are 32-bit: rows of the slice times ld
+    const long long rows_a = q.transA ? Cfg::BK : Cfg::BM, rows_b = q.transB ? Cfg::BN : Cfg::BK;
+    const bool fits = rows_a * q.lda * 2 < (1LL << 31) && rows_b * q.ldb * 2 < (1LL << 31);
     return aligned && whole && fits;
 }
 
@@ -612,7 +680,15 @@ hipError_t launch_dma(const GemmProblem &q, hipStream_t stream)
     a.C = q.C; a.ldc = q.ldc; a.sC = q.strideC;
     a.tiles_m = q.M / Cfg::BM;
     a.tiles_n = q.N / Cfg::BN;
-    hipLaunchKernelGGL((hgemm_dma_kernel<Cfg>), dim3(a.tiles_m * a.tiles_n, 1, q.batch), dim3(Cfg::NT), 0, stream, a);
+    const dim3 grid(a.tiles_m * a.tiles_n, 1, q.batch), block(Cfg::NT);
+    if (!q.transA && !q.transB)
+        hipLaunchKernelGGL((hgemm_dma_kernel<Cfg, false, false>), grid, block, 0, stream, a);
+    else if (!q.transA)
+        hipLaunchKernelGGL((hgemm_dma_kernel<Cfg, false, true>), grid, block, 0, stream, a);
+    else if (!q.transB)
+        hipLaunchKernelGGL((hgemm_dma_kernel<Cfg, true, false>), grid, block, 0, stream, a);
+    else
+        hipLaunchKernelGGL((hgemm_dma_kernel<Cfg, true, true>), grid, block, 0, stream, a);
     return hipGetLastError();
 }
 

@@ -24,6 +24,15 @@
 // Two instantiations per tile shape: MASK = false for problems made of whole
 // tiles with 16-byte aligned rows (no bounds checks anywhere), MASK = true for
 // everything else.  Workgroups are mapped to tiles XCD by XCD (tile_order.h).
+//
+// Transposed operands (C = alpha*op(A)op(B) + beta*C, the MindNotes 'GEMM'
+// page, section "core problem and arithmetic characteristics"): every kernel
+// is instantiated for the four storage combinations.  An operand is either
+// K-contiguous (A stored M x K, or B stored N x K) or MN-contiguous (A stored
+// K x M, or B stored K x N); each kernel reads a tile from global memory in its
+// stored orientation, with 16-byte loads along the contiguous dimension, and
+// only the LDS placement and the operand reads depend on the orientation.  The
+// order in which k terms meet each MFMA is the same for all four.
 #include "gemm_internal.h"
 #include "tile_order.h"
 #include "epilogue.h"
@@ -55,10 +64,6 @@ struct SgCfg {
     static constexpr int NT = 64 * WM * WN;
     static constexpr int TM = BM / WM, TN = BN / WN;      // wave tile
     static constexpr int FM = TM / 32, FN = TN / 32;      // MFMA blocks per wave
-    static constexpr int LDA_S = BM + 2;                  // A^T row pitch in LDS (floats)
-    static constexpr int LDB_S = BN + 4;                  // B row pitch in LDS (floats, 16 B multiple)
-    static constexpr int A_CPR = BK / 4;                  // float4 chunks per A row
-    static constexpr int B_CPR = BN / 4;                  // float4 chunks per B row
     static constexpr int A_LOADS = BM * BK / 4 / NT;
     static constexpr int B_LOADS = BK * BN / 4 / NT;
     static_assert(BM % (32 * WM) == 0 && BN % (32 * WN) == 0, "wave tile must be whole MFMA blocks");
@@ -66,13 +71,42 @@ struct SgCfg {
     static_assert(BK % 2 == 0, "MFMA consumes k in pairs");
 };
 
-template <class Cfg, bool MASK, bool VEC>
+// Four consecutive floats (r, c..c+3) of a row-major rows x cols matrix X with
+// leading dimension ld; with MASK, elements outside the matrix read as zero
+// (VEC: a 16-byte load is allowed where all four are inside).
+template <bool MASK, bool VEC>
+__device__ __forceinline__ float4 load4(const float *X, long long ld, long long r, long long c, long long rows,
+                                        long long cols)
+{
+    const float *src = X + r * ld + c;
+    if (!MASK || (VEC && r < rows && c + 3 < cols)) return *reinterpret_cast<const float4 *>(src);
+    const bool rok = r < rows;
+    float4 v;
+    v.x = (rok && c + 0 < cols) ? src[0] : 0.f;
+    v.y = (rok && c + 1 < cols) ? src[1] : 0.f;
+    v.z = (rok && c + 2 < cols) ? src[2] : 0.f;
+    v.w = (rok && c + 3 < cols) ? src[3] : 0.f;
+    return v;
+}
+
+// TA: A stored K x M; TB: B stored N x K.  In LDS both operands are kept
+// MN-contiguous ([k][m] and [k][n]); a K-contiguous operand is transposed on
+// its way in by four scalar LDS writes, an MN-contiguous one is written as
+// 16-byte rows.
+template <class Cfg, bool MASK, bool VEC, bool TA, bool TB>
 __global__ __launch_bounds__(Cfg::NT) void sgemm_mfma_kernel(SgemmArgs p)
 {
     constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK;
-    constexpr int LDA_S = Cfg::LDA_S, LDB_S = Cfg::LDB_S;
-    __shared__ float lds_a[2 * BK * LDA_S];
-    __shared__ float lds_b[2 * BK * LDB_S];
+    // LDS row pitches (floats): a multiple of four where rows are written as
+    // float4, 2 mod 4 where they are written by transposing scatter (spreads
+    // the four scattered k rows over the banks).
+    constexpr int LDA_S = TA ? BM + 4 : BM + 2;
+    constexpr int LDB_S = TB ? BN + 2 : BN + 4;
+    // float4 chunks per row of each tile as stored in global memory
+    constexpr int A_CPR = (TA ? BM : BK) / 4;
+    constexpr int B_CPR = (TB ? BK : BN) / 4;
+    __shared__ __attribute__((aligned(16))) float lds_a[2 * BK * LDA_S];
+    __shared__ __attribute__((aligned(16))) float lds_b[2 * BK * LDB_S];
 
     const int tid = threadIdx.x;
     int tm, tn;
@@ -90,36 +124,16 @@ __global__ __launch_bounds__(Cfg::NT) void sgemm_mfma_kernel(SgemmArgs p)
 #pragma unroll
         for (int i = 0; i < Cfg::A_LOADS; ++i) {
             const int id = i * Cfg::NT + tid;
-            const int row = id / Cfg::A_CPR, kc = (id % Cfg::A_CPR) * 4;
-            const long long gm = m0 + row;
-            const int gk = k0 + kc;
-            const float *src = A + gm * lda + gk;
-            if (!MASK || (VEC && gm < M && gk + 3 < K)) {
-                ra[i] = *reinterpret_cast<const float4 *>(src);
-            } else {
-                const bool rok = gm < M;
-                ra[i].x = (rok && gk + 0 < K) ? src[0] : 0.f;
-                ra[i].y = (rok && gk + 1 < K) ? src[1] : 0.f;
-                ra[i].z = (rok && gk + 2 < K) ? src[2] : 0.f;
-                ra[i].w = (rok && gk + 3 < K) ? src[3] : 0.f;
-            }
+            const int r = id / A_CPR, c = (id % A_CPR) * 4;
+            ra[i] = TA ? load4<MASK, VEC>(A, lda, k0 + r, m0 + c, K, M)
+                       : load4<MASK, VEC>(A, lda, m0 + r, k0 + c, M, K);
         }
 #pragma unroll
         for (int i = 0; i < Cfg::B_LOADS; ++i) {
             const int id = i * Cfg::NT + tid;
-            const int krow = id / Cfg::B_CPR, nc = (id % Cfg::B_CPR) * 4;
-            const int gk = k0 + krow;
-            const long long gn = n0 + nc;
-            const float *src = B + (long long)gk * ldb + gn;
-            if (!MASK || (VEC && gk < K && gn + 3 < N)) {
-                rb[i] = *reinterpret_cast<const float4 *>(src);
-            } else {
-                const bool kok = gk < K;
-                rb[i].x = (kok && gn + 0 < N) ? src[0] : 0.f;
-                rb[i].y = (kok && gn + 1 < N) ? src[1] : 0.f;
-                rb[i].z = (kok && gn + 2 < N) ? src[2] : 0.f;
-                rb[i].w = (kok && gn + 3 < N) ? src[3] : 0.f;
-            }
+            const int r = id / B_CPR, c = (id % B_CPR) * 4;
+            rb[i] = TB ? load4<MASK, VEC>(B, ldb, n0 + r, k0 + c, N, K)
+                       : load4<MASK, VEC>(B, ldb, k0 + r, n0 + c, K, N);
         }
     };
 
@@ -129,17 +143,28 @@ __global__ __launch_bounds__(Cfg::NT) void sgemm_mfma_kernel(SgemmArgs p)
 #pragma unroll
         for (int i = 0; i < Cfg::A_LOADS; ++i) {
             const int id = i * Cfg::NT + tid;
-            const int row = id / Cfg::A_CPR, kc = (id % Cfg::A_CPR) * 4;
-            as[(kc + 0) * LDA_S + row] = ra[i].x;
-            as[(kc + 1) * LDA_S + row] = ra[i].y;
-            as[(kc + 2) * LDA_S + row] = ra[i].z;
-            as[(kc + 3) * LDA_S + row] = ra[i].w;
+            const int r = id / A_CPR, c = (id % A_CPR) * 4;
+            if (TA) {   // r = k, c = m
+                *reinterpret_cast<float4 *>(&as[r * LDA_S + c]) = ra[i];
+            } else {    // r = m, c = k
+                as[(c + 0) * LDA_S + r] = ra[i].x;
+                as[(c + 1) * LDA_S + r] = ra[i].y;
+                as[(c + 2) * LDA_S + r] = ra[i].z;
+                as[(c + 3) * LDA_S + r] = ra[i].w;
+            }
         }
 #pragma unroll
         for (int i = 0; i < Cfg::B_LOADS; ++i) {
             const int id = i * Cfg::NT + tid;
-            const int krow = id / Cfg::B_CPR, nc = (id % Cfg::B_CPR) * 4;
-            *reinterpret_cast<float4 *>(&bs[krow * LDB_S + nc]) = rb[i];
+            const int r = id / B_CPR, c = (id % B_CPR) * 4;
+            if (TB) {   // r = n, c = k
+                bs[(c + 0) * LDB_S + r] = rb[i].x;
+                bs[(c + 1) * LDB_S + r] = rb[i].y;
+                bs[(c + 2) * LDB_S + r] = rb[i].z;
+                bs[(c + 3) * LDB_S + r] = rb[i].w;
+            } else {    // r = k, c = n
+                *reinterpret_cast<float4 *>(&bs[r * LDB_S + c]) = rb[i];
+            }
         }
     };
 
@@ -216,19 +241,23 @@ __global__ __launch_bounds__(Cfg::NT) void sgemm_mfma_kernel(SgemmArgs p)
 // slice t+1 waits and slice t is computed, which at fp32-MFMA speed (64
 // cycles per 32x32x2 op) leaves a whole slice of compute to hide the fetch.
 //
-// Operand layouts in LDS and the k order:
-//   * A slice: BM rows of 128 bytes (eight 16-byte chunks of four k); the chunk
-//     at physical position p of row r holds logical chunk p ^ ((r ^ r>>3) & 7),
-//     so the sixteen rows one LDS cycle serves fall on distinct banks.  A lane
-//     reads one whole chunk (four consecutive k of its row) per ds_read_b128:
-//     lanes 0-31 the chunk 2u, lanes 32-63 the chunk 2u+1.  Element e of that
-//     read feeds the e-th MFMA of quad u, so that MFMA's k pair is
-//     {8u+e, 8u+4+e} -- a fixed reordering of the sum over k;
-//   * B slice: 32 rows of BN floats, row-major; the chunk at physical
-//     position p of row k holds logical chunk p ^ (8 * ((k >> 2) & 1)), which
-//     puts rows k and k+4 (read by the two half-waves of one MFMA operand) on
-//     different banks.  The B operand of MFMA (u, e) is row 8u+e+4*(lane/32),
-//     column lane%32 -- one ds_read_b32 per lane.
+// Each operand slice is kept in LDS in its stored orientation:
+//   * K-contiguous (A stored M x K, B stored N x K): R rows (R = BM or BN) of
+//     128 bytes (eight 16-byte chunks of four k); the chunk at physical
+//     position p of row r holds logical chunk p ^ ((r ^ r>>3) & 7), so the
+//     sixteen rows one LDS cycle serves fall on distinct banks.  A lane reads
+//     one whole chunk (four consecutive k of its row) per ds_read_b128: lanes
+//     0-31 the chunk 2u, lanes 32-63 the chunk 2u+1.  Element e of that read
+//     feeds the e-th MFMA of quad u;
+//   * MN-contiguous (A stored K x M, B stored K x N): 32 rows of R floats; the
+//     chunk at physical position p of row k holds logical chunk
+//     p ^ (8 * ((k >> 2) & 1)), which puts rows k and k+4 (read by the two
+//     half-waves of one MFMA operand) on different banks.  The operand of
+//     MFMA (u, e) is row 8u+e+4*(lane/32), column lane%32 -- one ds_read_b32
+//     per lane.
+// Either way lane l of MFMA (u, e) holds k = 8u + 4*(l/32) + e, so the op's k
+// pair is {8u+e, 8u+4+e} -- one fixed reordering of the sum over k for all
+// four storage combinations.
 template <int BM_, int BN_, int WM_, int WN_>
 struct SgDmaCfg {
     static constexpr int BM = BM_, BN = BN_, BK = 32, WM = WM_, WN = WN_, SLOTS = 2;
@@ -240,9 +269,8 @@ struct SgDmaCfg {
     static constexpr int SLOT_BYTES = A_BYTES + B_BYTES;
     static constexpr int A_LOADS = A_BYTES / 1024 / NW;      // per wave per slice
     static constexpr int B_LOADS = B_BYTES / 1024 / NW;
-    static constexpr int B_CPR = BN / 4;                     // 16-byte chunks per B row
-    static constexpr int B_RPL = 256 / BN;                   // B rows per wave load
     static_assert(A_BYTES % (1024 * NW) == 0 && B_BYTES % (1024 * NW) == 0, "slices must split over the waves");
+    static_assert(BM >= 64 && BN >= 64, "MN-contiguous slices need at least 16 chunks per row");
     static_assert(SLOTS * SLOT_BYTES <= 160 * 1024, "LDS slots too large");
 };
 
@@ -261,10 +289,27 @@ typedef float f32x4v __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) f32x4v lds_f32x4;
 typedef __attribute__((address_space(3))) float lds_f32;
 
-template <class Cfg>
+// Per-lane byte offset (within one slice of global memory) of the 16-byte
+// chunk that lane `lane` of wave load g fetches for an operand slice of R rows
+// or columns; see the layouts above.
+template <bool KC, int R>
+__device__ __forceinline__ unsigned sg_dma_offset(int g, int lane, long long ld)
+{
+    if (KC) {
+        const int r = 8 * g + (lane >> 3);
+        return (unsigned)(r * ld + 4 * ((lane & 7) ^ sg_swz_a(r))) * 4u;
+    }
+    constexpr int CPR = R / 4, RPL = 256 / R;   // chunks per row, rows per wave load
+    const int k = RPL * g + lane / CPR;
+    return (unsigned)(k * ld + 4 * ((lane % CPR) ^ sg_swz_b(k))) * 4u;
+}
+
+// TA: A stored K x M; TB: B stored N x K.
+template <class Cfg, bool TA, bool TB>
 __global__ __launch_bounds__(Cfg::NT) void sgemm_dma_kernel(SgemmArgs p)
 {
     constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK;
+    constexpr bool A_KC = !TA, B_KC = TB;
     __shared__ __attribute__((aligned(1024))) unsigned char lds[Cfg::SLOTS * Cfg::SLOT_BYTES];
     const unsigned lds0 = (unsigned)(uintptr_t)lds;
 
@@ -274,24 +319,22 @@ __global__ __launch_bounds__(Cfg::NT) void sgemm_dma_kernel(SgemmArgs p)
     tile_coords(blockIdx.x, p.tiles_m, p.tiles_n, &tm, &tn);
     const long long m0 = (long long)tm * BM, n0 = (long long)tn * BN;
     const long long lda = p.lda, ldb = p.ldb, ldc = p.ldc;
-    const char *Ab = reinterpret_cast<const char *>(p.A + (long long)blockIdx.z * p.sA + m0 * lda);
-    const char *Bb = reinterpret_cast<const char *>(p.B + (long long)blockIdx.z * p.sB + n0);
+    // first element of the tile's slice 0 in each operand
+    const char *Ab = reinterpret_cast<const char *>(p.A + (long long)blockIdx.z * p.sA + (A_KC ? m0 * lda : m0));
+    const char *Bb = reinterpret_cast<const char *>(p.B + (long long)blockIdx.z * p.sB + (B_KC ? n0 * ldb : n0));
     float *C = p.C + (long long)blockIdx.z * p.sC;
+    // bytes between consecutive slices
+    const long long stepA = A_KC ? BK * 4 : BK * lda * 4;
+    const long long stepB = B_KC ? BK * 4 : BK * ldb * 4;
 
     unsigned offA[Cfg::A_LOADS], offB[Cfg::B_LOADS];
 #pragma unroll
-    for (int i = 0; i < Cfg::A_LOADS; ++i) {
-        const int r = 8 * (uwave * Cfg::A_LOADS + i) + (lane >> 3);
-        offA[i] = (unsigned)(r * lda + 4 * ((lane & 7) ^ sg_swz_a(r))) * 4u;
-    }
+    for (int i = 0; i < Cfg::A_LOADS; ++i) offA[i] = sg_dma_offset<A_KC, BM>(uwave * Cfg::A_LOADS + i, lane, lda);
 #pragma unroll
-    for (int i = 0; i < Cfg::B_LOADS; ++i) {
-        const int k = Cfg::B_RPL * (uwave * Cfg::B_LOADS + i) + lane / Cfg::B_CPR;
-        offB[i] = (unsigned)(k * ldb + 4 * ((lane % Cfg::B_CPR) ^ sg_swz_b(k))) * 4u;
-    }
+    for (int i = 0; i < Cfg::B_LOADS; ++i) offB[i] = sg_dma_offset<B_KC, BN>(uwave * Cfg::B_LOADS + i, lane, ldb);
     auto issue_slice = [&](int kt, int slot) {
-        const char *a = Ab + (long long)kt * BK * 4;
-        const char *b = Bb + (long long)kt * BK * ldb * 4;
+        const char *a = Ab + (long long)kt * stepA;
+        const char *b = Bb + (long long)kt * stepB;
         const unsigned la = lds0 + slot * Cfg::SLOT_BYTES + uwave * Cfg::A_LOADS * 1024;
         const unsigned lb = lds0 + slot * Cfg::SLOT_BYTES + Cfg::A_BYTES + uwave * Cfg::B_LOADS * 1024;
 #pragma unroll
@@ -302,21 +345,34 @@ __global__ __launch_bounds__(Cfg::NT) void sgemm_dma_kernel(SgemmArgs p)
 
     const int wm = wave / Cfg::WN, wn = wave % Cfg::WN;
     const int lr = lane & 31, lk = lane >> 5;
-    // A operand rows and the lane part of their chunk index (logical chunk 2u+lk).
-    unsigned rowA[Cfg::FM], tA[Cfg::FM];
+    // Operand read addresses (bytes within a slot).  K-contiguous: the row and
+    // the lane part of its chunk index (logical chunk 2u+lk).  MN-contiguous:
+    // row 4*lk (plus 8u+e), logical chunk (32-column block + lr)/4, physical
+    // chunk flipped by 8 when lk = 1.
+    unsigned rowA[Cfg::FM], tA[Cfg::FM], rowB[Cfg::FN], tB[Cfg::FN];
 #pragma unroll
     for (int i = 0; i < Cfg::FM; ++i) {
         const int r = wm * Cfg::TM + 32 * i + lr;
-        rowA[i] = (unsigned)(r * BK * 4);
-        tA[i] = (unsigned)(lk ^ sg_swz_a(r));
+        if (A_KC) {
+            rowA[i] = (unsigned)(r * BK * 4);
+            tA[i] = (unsigned)(lk ^ sg_swz_a(r));
+        } else {
+            const int q = r >> 2;
+            rowA[i] = (unsigned)(4 * lk * BM * 4 + 16 * (q ^ (8 * lk)) + 4 * (lr & 3));
+            tA[i] = 0;
+        }
     }
-    // B operand: row 8u+e+4*lk, logical chunk (wn*TN + 32j + lr)/4, physical
-    // chunk flipped by 8 when lk = 1.
-    unsigned colB[Cfg::FN];
 #pragma unroll
     for (int j = 0; j < Cfg::FN; ++j) {
-        const int q = ((wn * Cfg::TN + 32 * j) >> 2) + (lr >> 2);
-        colB[j] = (unsigned)(Cfg::A_BYTES + 4 * lk * BN * 4 + 16 * (q ^ (8 * lk)) + 4 * (lr & 3));
+        const int c = wn * Cfg::TN + 32 * j + lr;
+        if (B_KC) {
+            rowB[j] = (unsigned)(Cfg::A_BYTES + c * BK * 4);
+            tB[j] = (unsigned)(lk ^ sg_swz_a(c));
+        } else {
+            const int q = c >> 2;
+            rowB[j] = (unsigned)(Cfg::A_BYTES + 4 * lk * BN * 4 + 16 * (q ^ (8 * lk)) + 4 * (lr & 3));
+            tB[j] = 0;
+        }
     }
 
     f32x16 acc[Cfg::FM][Cfg::FN];
@@ -331,21 +387,31 @@ __global__ __launch_bounds__(Cfg::NT) void sgemm_dma_kernel(SgemmArgs p)
         const unsigned base = lds0 + slot * Cfg::SLOT_BYTES;
 #pragma unroll
         for (int u = 0; u < BK / 8; ++u) {
-            f32x4v a[Cfg::FM];
+            f32x4v qa[Cfg::FM], qb[Cfg::FN];
+            if constexpr (A_KC) {
 #pragma unroll
-            for (int i = 0; i < Cfg::FM; ++i)
-                a[i] = *(const lds_f32x4 *)(uintptr_t)(base + rowA[i] + 16 * (tA[i] ^ (2u * u)));
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                float b[Cfg::FN];
+                for (int i = 0; i < Cfg::FM; ++i)
+                    qa[i] = *(const lds_f32x4 *)(uintptr_t)(base + rowA[i] + 16 * (tA[i] ^ (2u * u)));
+            }
+            if constexpr (B_KC) {
 #pragma unroll
                 for (int j = 0; j < Cfg::FN; ++j)
-                    b[j] = *(const lds_f32 *)(uintptr_t)(base + colB[j] + (8 * u + e) * BN * 4);
+                    qb[j] = *(const lds_f32x4 *)(uintptr_t)(base + rowB[j] + 16 * (tB[j] ^ (2u * u)));
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                float a[Cfg::FM], b[Cfg::FN];
+#pragma unroll
+                for (int i = 0; i < Cfg::FM; ++i)
+                    a[i] = A_KC ? qa[i][e] : *(const lds_f32 *)(uintptr_t)(base + rowA[i] + (8 * u + e) * BM * 4);
+#pragma unroll
+                for (int j = 0; j < Cfg::FN; ++j)
+                    b[j] = B_KC ? qb[j][e] : *(const lds_f32 *)(uintptr_t)(base + rowB[j] + (8 * u + e) * BN * 4);
 #pragma unroll
                 for (int i = 0; i < Cfg::FM; ++i)
 #pragma unroll
                     for (int j = 0; j < Cfg::FN; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(b[j], a[i][e], acc[i][j], 0, 0, 0);
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(b[j], a[i], acc[i][j], 0, 0, 0);
             }
         }
     };
@@ -408,7 +474,9 @@ bool sg_dma_ok(const GemmProblem &q)
                          (q.strideB % 4 == 0) && (reinterpret_cast<uintptr_t>(q.A) % 16 == 0) &&
                          (reinterpret_cast<uintptr_t>(q.B) % 16 == 0);
     const bool whole = q.M % Cfg::BM == 0 && q.N % Cfg::BN == 0 && q.K % Cfg::BK == 0 && q.K >= 2 * Cfg::BK;
-    const bool fits = (long long)Cfg::BM * q.lda * 4 < (1LL << 31) && (long long)Cfg::BK * q.ldb * 4 < (1LL << 31);
+    // per-lane offsets within one slice are 32-bit: rows of the slice times ld
+    const long long rows_a = q.transA ? Cfg::BK : Cfg::BM, rows_b = q.transB ? Cfg::BN : Cfg::BK;
+    const bool fits = rows_a * q.lda * 4 < (1LL << 31) && rows_b * q.ldb * 4 < (1LL << 31);
     return aligned && whole && fits;
 }
 
@@ -423,7 +491,15 @@ hipError_t launch_sg_dma(const GemmProblem &q, hipStream_t stream)
     a.C = q.C; a.ldc = q.ldc; a.sC = q.strideC;
     a.tiles_m = q.M / Cfg::BM;
     a.tiles_n = q.N / Cfg::BN;
-    hipLaunchKernelGGL((sgemm_dma_kernel<Cfg>), dim3(a.tiles_m * a.tiles_n, 1, q.batch), dim3(Cfg::NT), 0, stream, a);
+    const dim3 grid(a.tiles_m * a.tiles_n, 1, q.batch), block(Cfg::NT);
+    if (!q.transA && !q.transB)
+        hipLaunchKernelGGL((sgemm_dma_kernel<Cfg, false, false>), grid, block, 0, stream, a);
+    else if (!q.transA)
+        hipLaunchKernelGGL((sgemm_dma_kernel<Cfg, false, true>), grid, block, 0, stream, a);
+    else if (!q.transB)
+        hipLaunchKernelGGL((sgemm_dma_kernel<Cfg, true, false>), grid, block, 0, stream, a);
+    else
+        hipLaunchKernelGGL((sgemm_dma_kernel<Cfg, true, true>), grid, block, 0, stream, a);
     return hipGetLastError();
 }
 
@@ -441,13 +517,17 @@ hipError_t launch_sg_dma(const GemmProblem &q, hipStream_t stream)
 // order (wave 0 + wave 1 + wave 2 + wave 3), so results are deterministic; each
 // wave then finishes one quarter of the tile (its register quad) through the
 // alpha/beta epilogue.  Out-of-range rows, columns and k load as zero.
+// A transposed operand changes only the loads: a K-contiguous operand (A
+// stored M x K, B stored N x K) is read as 16-byte quads of four k, an
+// MN-contiguous one as one float per lane and k (coalesced across the lanes).
 template <int FM_, int FN_>
 struct SgSmallCfg {
     static constexpr int FM = FM_, FN = FN_, KW = 4, NT = 64 * KW, P = 4;
     static constexpr int TM = 32 * FM, TN = 32 * FN;
 };
 
-template <class Cfg, bool VECA>
+// VEC: every K-contiguous operand has 16-byte aligned rows.
+template <class Cfg, bool VEC, bool TA, bool TB>
 __global__ __launch_bounds__(256) void sgemm_small_kernel(SgemmArgs p)
 {
     constexpr int FM = Cfg::FM, FN = Cfg::FN, KW = Cfg::KW, P = Cfg::P;
@@ -469,6 +549,9 @@ __global__ __launch_bounds__(256) void sgemm_small_kernel(SgemmArgs p)
     const int kb = w * kc;
     const int ke = (kb + kc < K) ? kb + kc : K;
 
+    // Row i of op(A) starts at arow[i] and its k-th element is arow[i][k * sa];
+    // column j of op(B) likewise with bcol[j] and sb.
+    const long long sa = TA ? lda : 1, sb = TB ? 1 : ldb;
     bool rowok[FM], colok[FN];
     const float *arow[FM];
     const float *bcol[FN];
@@ -476,35 +559,33 @@ __global__ __launch_bounds__(256) void sgemm_small_kernel(SgemmArgs p)
     for (int i = 0; i < FM; ++i) {
         const long long r = m0 + 32 * i + lr;
         rowok[i] = r < M;
-        arow[i] = A + (rowok[i] ? r : 0) * lda;
+        arow[i] = A + (rowok[i] ? r : 0) * (TA ? 1 : lda);
     }
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
         const long long c = n0 + 32 * j + lr;
         colok[j] = c < N;
-        bcol[j] = B + (colok[j] ? c : 0);
+        bcol[j] = B + (colok[j] ? c : 0) * (TB ? ldb : 1);
     }
 
-    f32x4_t ra[P][FM];
-    float rb[P][FN][4];
-    auto load_step = [&](int k, f32x4_t *a, float (*b)[4]) {
-        const int ka = k + 4 * lk;   // this lane's A quad starts here
+    // Four k of one operand row or column starting at kq (zero outside).
+    auto quad = [&](const float *x, long long stride, bool ok, int kq, bool kcontig) {
+        f32x4_t v;
+        if (kcontig && VEC && ok && kq + 3 < ke) {
+            v = *reinterpret_cast<const f32x4_t *>(x + kq);
+        } else {
 #pragma unroll
-        for (int i = 0; i < FM; ++i) {
-            if (VECA && rowok[i] && ka + 3 < ke) {
-                a[i] = *reinterpret_cast<const f32x4_t *>(arow[i] + ka);
-            } else {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) a[i][e] = (rowok[i] && ka + e < ke) ? arow[i][ka + e] : 0.f;
-            }
+            for (int e = 0; e < 4; ++e) v[e] = (ok && kq + e < ke) ? x[(long long)(kq + e) * stride] : 0.f;
         }
+        return v;
+    };
+    f32x4_t ra[P][FM], rb[P][FN];
+    auto load_step = [&](int k, f32x4_t *a, f32x4_t *b) {
+        const int kq = k + 4 * lk;   // this lane's k quad starts here
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
+        for (int i = 0; i < FM; ++i) a[i] = quad(arow[i], sa, rowok[i], kq, !TA);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int kk = k + e + 4 * lk;
-                b[j][e] = (colok[j] && kk < ke) ? bcol[j][(long long)kk * ldb] : 0.f;
-            }
+        for (int j = 0; j < FN; ++j) b[j] = quad(bcol[j], sb, colok[j], kq, TB);
     };
 
     f32x16 acc[FM][FN];
@@ -567,6 +648,15 @@ __global__ __launch_bounds__(256) void sgemm_small_kernel(SgemmArgs p)
         }
 }
 
+template <class Cfg, bool TA, bool TB>
+void launch_small_kernel(const SgemmArgs &a, bool vec, dim3 grid, hipStream_t stream)
+{
+    if (vec)
+        hipLaunchKernelGGL((sgemm_small_kernel<Cfg, true, TA, TB>), grid, dim3(Cfg::NT), 0, stream, a);
+    else
+        hipLaunchKernelGGL((sgemm_small_kernel<Cfg, false, TA, TB>), grid, dim3(Cfg::NT), 0, stream, a);
+}
+
 template <class Cfg>
 hipError_t launch_small(const GemmProblem &q, hipStream_t stream)
 {
@@ -578,12 +668,20 @@ hipError_t launch_small(const GemmProblem &q, hipStream_t stream)
     a.C = q.C; a.ldc = q.ldc; a.sC = q.strideC;
     a.tiles_m = (q.M + Cfg::TM - 1) / Cfg::TM;
     a.tiles_n = (q.N + Cfg::TN - 1) / Cfg::TN;
-    const bool veca = (q.lda % 4 == 0) && (reinterpret_cast<uintptr_t>(q.A) % 16 == 0) && (q.strideA % 4 == 0);
-    dim3 grid(a.tiles_m * a.tiles_n, 1, q.batch);
-    if (veca)
-        hipLaunchKernelGGL((sgemm_small_kernel<Cfg, true>), grid, dim3(Cfg::NT), 0, stream, a);
+    // 16-byte quads are loaded from K-contiguous operands only
+    const bool veca = q.transA || ((q.lda % 4 == 0) && (reinterpret_cast<uintptr_t>(q.A) % 16 == 0) &&
+                                   (q.strideA % 4 == 0));
+    const bool vecb = !q.transB || ((q.ldb % 4 == 0) && (reinterpret_cast<uintptr_t>(q.B) % 16 == 0) &&
+                                    (q.strideB % 4 == 0));
+    const dim3 grid(a.tiles_m * a.tiles_n, 1, q.batch);
+    if (!q.transA && !q.transB)
+        launch_small_kernel<Cfg, false, false>(a, veca && vecb, grid, stream);
+    else if (!q.transA)
+        launch_small_kernel<Cfg, false, true>(a, veca && vecb, grid, stream);
+    else if (!q.transB)
+        launch_small_kernel<Cfg, true, false>(a, veca && vecb, grid, stream);
     else
-        hipLaunchKernelGGL((sgemm_small_kernel<Cfg, false>), grid, dim3(Cfg::NT), 0, stream, a);
+        launch_small_kernel<Cfg, true, true>(a, veca && vecb, grid, stream);
     return hipGetLastError();
 }
 
@@ -591,6 +689,18 @@ using SgSmall64 = SgSmallCfg<2, 2>;
 using SgSmall32 = SgSmallCfg<1, 1>;
 
 using SgBig = SgCfg<128, 128, 16, 2, 2>;
+
+template <class Cfg, bool TA, bool TB>
+void launch_cfg_kernel(const SgemmArgs &a, bool whole, bool vec, dim3 grid, hipStream_t stream)
+{
+    const dim3 block(Cfg::NT);
+    if (whole)
+        hipLaunchKernelGGL((sgemm_mfma_kernel<Cfg, false, true, TA, TB>), grid, block, 0, stream, a);
+    else if (vec)
+        hipLaunchKernelGGL((sgemm_mfma_kernel<Cfg, true, true, TA, TB>), grid, block, 0, stream, a);
+    else
+        hipLaunchKernelGGL((sgemm_mfma_kernel<Cfg, true, false, TA, TB>), grid, block, 0, stream, a);
+}
 
 template <class Cfg>
 hipError_t launch_cfg(const GemmProblem &q, hipStream_t stream)
@@ -608,14 +718,15 @@ hipError_t launch_cfg(const GemmProblem &q, hipStream_t stream)
                      (reinterpret_cast<uintptr_t>(q.B) % 16 == 0) &&
                      (q.strideA % 4 == 0) && (q.strideB % 4 == 0);
     const bool whole = vec && q.M % Cfg::BM == 0 && q.N % Cfg::BN == 0 && q.K % Cfg::BK == 0;
-    dim3 grid(a.tiles_m * a.tiles_n, 1, q.batch);
-    dim3 block(Cfg::NT);
-    if (whole)
-        hipLaunchKernelGGL((sgemm_mfma_kernel<Cfg, false, true>), grid, block, 0, stream, a);
-    else if (vec)
-        hipLaunchKernelGGL((sgemm_mfma_kernel<Cfg, true, true>), grid, block, 0, stream, a);
+    const dim3 grid(a.tiles_m * a.tiles_n, 1, q.batch);
+    if (!q.transA && !q.transB)
+        launch_cfg_kernel<Cfg, false, false>(a, whole, vec, grid, stream);
+    else if (!q.transA)
+        launch_cfg_kernel<Cfg, false, true>(a, whole, vec, grid, stream);
+    else if (!q.transB)
+        launch_cfg_kernel<Cfg, true, false>(a, whole, vec, grid, stream);
     else
-        hipLaunchKernelGGL((sgemm_mfma_kernel<Cfg, true, false>), grid, block, 0, stream, a);
+        launch_cfg_kernel<Cfg, true, true>(a, whole, vec, grid, stream);
     return hipGetLastError();
 }
 

@@ -50,11 +50,13 @@ typedef struct ihipStream_t *hipStream_t; /* the HIP runtime's stream handle */
 enum {
     GEMM_OK = 0,
     GEMM_ERR_SIZE = -1,      /* M, N, K or batch_count negative, or an extent overflows 64 bits */
-    GEMM_ERR_LD = -2,        /* lda < max(1,K), ldb < max(1,N), ldc < max(1,N), negative stride, or
+    GEMM_ERR_LD = -2,        /* lda < max(1,K), ldb < max(1,N) (with transA: lda < max(1,M); with
+                                transB: ldb < max(1,K)), ldc < max(1,N), negative stride, or
                                 strideC smaller than one C member when batch_count > 1 */
     GEMM_ERR_NULL = -3,      /* NULL pointer for an operand that the call would read or write */
     GEMM_ERR_ALIGN = -4,     /* pointer not aligned to its element size */
-    GEMM_ERR_LAUNCH = -5     /* the HIP runtime refused a kernel launch (hipGetLastError) */
+    GEMM_ERR_LAUNCH = -5,    /* the HIP runtime refused a kernel launch (hipGetLastError) */
+    GEMM_ERR_OP = -6         /* transA or transB is neither 0 nor 1 */
 };
 
 /*
@@ -94,6 +96,32 @@ int gemm_batched_f16_f32acc(int M, int N, int K, float alpha,
                             const uint16_t *B, int ldb, long long strideB,
                             float beta, float *C, int ldc, long long strideC,
                             int batch_count, hipStream_t stream);
+
+/*
+ * The _ex forms compute C <- alpha*op(A)*op(B) + beta*C, op(X) = X or X^T, the
+ * general form of the MindNotes page's definition (section "core problem and
+ * arithmetic characteristics").  op(A) is M x K and op(B) is K x N:
+ *   transA = 0: A is stored M x K, element (i,k) at A[i*lda + k], lda >= max(1,K);
+ *   transA = 1: A is stored K x M, element (i,k) at A[k*lda + i], lda >= max(1,M);
+ *   transB = 0: B is stored K x N, element (k,j) at B[k*ldb + j], ldb >= max(1,N);
+ *   transB = 1: B is stored N x K, element (k,j) at B[j*ldb + k], ldb >= max(1,K).
+ * C is always M x N row-major.  Flags other than 0 or 1 return GEMM_ERR_OP.
+ * Everything else is as for the entry points above (which are the _ex forms
+ * with transA = transB = 0).
+ */
+int gemm_f32_ex(int transA, int transB, int M, int N, int K, float alpha,
+                const float *A, int lda, const float *B, int ldb,
+                float beta, float *C, int ldc, hipStream_t stream);
+
+int gemm_f16_f32acc_ex(int transA, int transB, int M, int N, int K, float alpha,
+                       const uint16_t *A, int lda, const uint16_t *B, int ldb,
+                       float beta, float *C, int ldc, hipStream_t stream);
+
+int gemm_batched_f16_f32acc_ex(int transA, int transB, int M, int N, int K, float alpha,
+                               const uint16_t *A, int lda, long long strideA,
+                               const uint16_t *B, int ldb, long long strideB,
+                               float beta, float *C, int ldc, long long strideC,
+                               int batch_count, hipStream_t stream);
 
 /* gemm_status_string -- a static, NUL-terminated description of a status code. */
 const char *gemm_status_string(int status);

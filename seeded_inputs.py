@@ -84,25 +84,39 @@ def matrix(seed: int, rows: int, cols: int, ld: int | None = None, kind: str = "
 def gemm_problem(M: int, N: int, K: int, *, lda: int | None = None, ldb: int | None = None,
                  ldc: int | None = None, in_dtype=np.float32, kind: str = "pm1",
                  c_kind: str | None = None, seed: int = 42, batch: int = 0,
-                 with_c: bool = True) -> dict:
-    """Operands of one GEMM C = alpha*A*B + beta*C (row-major, see :func:`matrix`).
+                 with_c: bool = True, transA: bool = False, transB: bool = False) -> dict:
+    """Operands of one GEMM C = alpha*op(A)*op(B) + beta*C (row-major, see :func:`matrix`).
 
-    Returns a dict with flat buffers ``A`` (M x K, lda), ``B`` (K x N, ldb) in
-    ``in_dtype`` and ``C`` (M x N, ldc, float32), plus the shape and leading
-    dimensions.  ``batch`` selects the seed offset of one member of a batch.
+    Returns a dict with flat buffers ``A`` and ``B`` in ``in_dtype`` and ``C``
+    (M x N, ldc, float32), plus the shape, leading dimensions and flags.  A is
+    stored M x K, or K x M when ``transA``; B is stored K x N, or N x K when
+    ``transB`` (the draw fills the stored matrix row by row either way).
+    ``batch`` selects the seed offset of one member of a batch.
     ``with_c=False`` leaves ``C`` as None (for beta = 0, where C is never read).
     """
-    lda = max(K, 1) if lda is None else lda
-    ldb = max(N, 1) if ldb is None else ldb
+    a_rows, a_cols = (K, M) if transA else (M, K)
+    b_rows, b_cols = (N, K) if transB else (K, N)
+    lda = max(a_cols, 1) if lda is None else lda
+    ldb = max(b_cols, 1) if ldb is None else ldb
     ldc = max(N, 1) if ldc is None else ldc
     c_kind = kind if c_kind is None else c_kind
     base = seed + 3 * batch
     return {
         "M": M, "N": N, "K": K, "lda": lda, "ldb": ldb, "ldc": ldc,
-        "A": matrix(base + 0, M, K, lda, kind, in_dtype),
-        "B": matrix(base + 1, K, N, ldb, kind, in_dtype),
+        "transA": bool(transA), "transB": bool(transB),
+        "A": matrix(base + 0, a_rows, a_cols, lda, kind, in_dtype),
+        "B": matrix(base + 1, b_rows, b_cols, ldb, kind, in_dtype),
         "C": matrix(base + 2, M, N, ldc, c_kind, np.float32) if with_c else None,
     }
+
+
+def logical_transpose(buf: np.ndarray, rows: int, cols: int, ld: int | None = None) -> np.ndarray:
+    """The same values stored the other way round: a ``rows x cols`` matrix
+    (flat, leading dimension ``ld``) as a flat ``cols x rows`` buffer with
+    leading dimension ``rows``.  A pure relayout, no arithmetic."""
+    ld = cols if ld is None else ld
+    m = np.asarray(buf)[: rows * ld].reshape(rows, ld)[:, :cols]
+    return np.ascontiguousarray(m.T).reshape(-1)
 
 
 def sample_rows(seed: int, M: int, n: int = 64) -> np.ndarray:

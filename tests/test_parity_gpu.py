@@ -46,7 +46,11 @@ def to_dev(buf):
 
 def call(kind, p, alpha, beta, dA, dB, dC, stream=None):
     M, N, K = p["M"], p["N"], p["K"]
-    if kind == "f32":
+    tA, tB = int(p.get("transA", False)), int(p.get("transB", False))
+    if tA or tB:   # the op(A)/op(B) entry points
+        fn = dg.gemm_f32_ex if kind == "f32" else dg.gemm_f16_f32acc_ex
+        fn(tA, tB, M, N, K, alpha, dA, p["lda"], dB, p["ldb"], beta, dC, p["ldc"], stream)
+    elif kind == "f32":
         dg.gemm_f32(M, N, K, alpha, dA, p["lda"], dB, p["ldb"], beta, dC, p["ldc"], stream)
     else:
         dg.gemm_f16_f32acc(M, N, K, alpha, dA, p["lda"], dB, p["ldb"], beta, dC, p["ldc"], stream)
@@ -62,12 +66,12 @@ def rows_of(dC, M, N, ldc, rows=None):
 
 
 def run_and_check(kind, M, N, K, alpha, beta, *, kind_vals="pm1", lda=None, ldb=None, ldc=None,
-                  sample=None, exact=False, seed=42, c_nan=False):
+                  sample=None, exact=False, seed=42, c_nan=False, transA=False, transB=False):
     in_dtype = np.float32 if kind == "f32" else np.float16
     note(f"{kind} M={M} N={N} K={K} alpha={alpha} beta={beta} vals={kind_vals} lda={lda} ldb={ldb} "
-         f"ldc={ldc} sample={sample} seed={seed}")
+         f"ldc={ldc} sample={sample} seed={seed} transA={int(transA)} transB={int(transB)}")
     p = si.gemm_problem(M, N, K, lda=lda, ldb=ldb, ldc=ldc, in_dtype=in_dtype, kind=kind_vals, seed=seed,
-                        with_c=not c_nan)
+                        with_c=not c_nan, transA=transA, transB=transB)
     dA, dB = to_dev(p["A"]), to_dev(p["B"])
     if c_nan:   # beta = 0: C must be written without being read
         dC = torch.full((M * p["ldc"],), float("nan"), dtype=torch.float32, device="cuda")
@@ -78,7 +82,7 @@ def run_and_check(kind, M, N, K, alpha, beta, *, kind_vals="pm1", lda=None, ldb=
     rows = si.sample_rows(seed, M, sample) if sample else None
     got = rows_of(dC, M, N, p["ldc"], rows)
     ref, bound = oracle.gemm_ref(M, N, K, alpha, p["A"], p["lda"], p["B"], p["ldb"], beta,
-                                 None if beta == 0 else p["C"], p["ldc"], rows=rows)
+                                 None if beta == 0 else p["C"], p["ldc"], rows=rows, transA=transA, transB=transB)
     if exact:
         want = ref.astype(np.float32)
         bad = np.argwhere(got != want)
@@ -126,14 +130,16 @@ def test_cfg4_hgemm(n):
 
 
 def batched_check(M, N, K, nb, alpha, beta, *, kind_vals="pm1", sample=None, exact=False, seed=42,
-                  pad=0, share_a=False):
+                  pad=0, share_a=False, transA=False, transB=False):
     note(f"batched M={M} N={N} K={K} batch={nb} alpha={alpha} beta={beta} vals={kind_vals} "
-         f"sample={sample} pad={pad} share_a={share_a}")
-    lda, ldb, ldc = K + pad, N + pad, N + pad
+         f"sample={sample} pad={pad} share_a={share_a} transA={int(transA)} transB={int(transB)}")
+    a_rows, a_cols = (K, M) if transA else (M, K)
+    b_rows, b_cols = (N, K) if transB else (K, N)
+    lda, ldb, ldc = a_cols + pad, b_cols + pad, N + pad
     probs = [si.gemm_problem(M, N, K, lda=lda, ldb=ldb, ldc=ldc, in_dtype=np.float16, kind=kind_vals,
-                             seed=seed, batch=b) for b in range(nb)]
-    sA = 0 if share_a else M * lda + 8 * pad
-    sB, sC = K * ldb + 8 * pad, M * ldc + 8 * pad
+                             seed=seed, batch=b, transA=transA, transB=transB) for b in range(nb)]
+    sA = 0 if share_a else a_rows * lda + 8 * pad
+    sB, sC = b_rows * ldb + 8 * pad, M * ldc + 8 * pad
 
     def pack(key, stride, n_el, dtype):
         buf = np.full(stride * (nb - 1) + n_el if stride else n_el, np.nan, dtype=dtype)
@@ -141,18 +147,22 @@ def batched_check(M, N, K, nb, alpha, beta, *, kind_vals="pm1", sample=None, exa
             buf[b * stride: b * stride + n_el] = probs[b][key]
         return buf
 
-    A = pack("A", sA, M * lda, np.float16)
-    B = pack("B", sB, K * ldb, np.float16)
+    A = pack("A", sA, a_rows * lda, np.float16)
+    B = pack("B", sB, b_rows * ldb, np.float16)
     C = pack("C", sC, M * ldc, np.float32)
     dA, dB, dC = to_dev(A), to_dev(B), to_dev(C)
-    dg.gemm_batched_f16_f32acc(M, N, K, alpha, dA, lda, sA, dB, ldb, sB, beta, dC, ldc, sC, nb)
+    if transA or transB:
+        dg.gemm_batched_f16_f32acc_ex(int(transA), int(transB), M, N, K, alpha, dA, lda, sA, dB, ldb, sB, beta,
+                                      dC, ldc, sC, nb)
+    else:
+        dg.gemm_batched_f16_f32acc(M, N, K, alpha, dA, lda, sA, dB, ldb, sB, beta, dC, ldc, sC, nb)
     torch.cuda.synchronize()
     rows = si.sample_rows(seed, M, sample) if sample else None
     worst = 0.0
     for b in range(nb):
         got = rows_of(dC[b * sC:], M, N, ldc, rows)
         ref, bound = oracle.gemm_ref(M, N, K, alpha, A[b * sA:], lda, B[b * sB:], ldb, beta,
-                                     C[b * sC: b * sC + M * ldc], ldc, rows=rows)
+                                     C[b * sC: b * sC + M * ldc], ldc, rows=rows, transA=transA, transB=transB)
         if exact:
             assert np.array_equal(got, ref.astype(np.float32)), f"member {b} not bit-exact"
         e = oracle.normalized_error(got, ref, bound)
@@ -290,3 +300,88 @@ def test_runs_on_the_given_stream():
         s.synchronize()
         ref, bound = oracle.gemm_ref(256, 192, 320, 1.0, p["A"], 320, p["B"], 192, 1.0, p["C"], 192)
         assert oracle.normalized_error(rows_of(dC, 256, 192, 192), ref, bound) <= TOL
+
+
+# ------------------------------------------------------------------ op(A) / op(B)
+# C = alpha*op(A)op(B) + beta*C with A stored K x M (transA) and/or B stored
+# N x K (transB).  Each case names the kernel it reaches; the int4 runs are
+# bit-exact, which also proves that no element is read from the wrong place.
+OPS = [(True, False), (False, True), (True, True)]
+
+
+@pytest.mark.parametrize("kind", ["f32", "f16"])
+@pytest.mark.parametrize("tA,tB", OPS)
+@pytest.mark.parametrize("M,N,K", [(1, 7, 3), (33, 65, 17), (127, 129, 63), (257, 255, 129), (300, 17, 1000)])
+def test_transposed_ragged(kind, tA, tB, M, N, K):
+    # SGEMM: split-K small-problem kernel; HGEMM: masked register-staged kernel
+    run_and_check(kind, M, N, K, 1.5, -0.5, transA=tA, transB=tB)
+    a_cols, b_cols = (M if tA else K), (K if tB else N)
+    run_and_check(kind, M, N, K, 1.5, -0.5, lda=a_cols + 3, ldb=b_cols + 5, ldc=N + 1, kind_vals="int4",
+                  exact=True, transA=tA, transB=tB, seed=13)
+
+
+@pytest.mark.parametrize("tA,tB", OPS)
+def test_transposed_sgemm_register_kernel(tA, tB):
+    # >= 256 tiles of 128x128: ragged edges -> masked register kernel; whole tiles
+    # with K % 32 != 0 -> unmasked register kernel
+    run_and_check("f32", 2100, 2100, 100, 1.5, -0.5, sample=64, transA=tA, transB=tB)
+    run_and_check("f32", 2100, 2100, 100, 1.0, 1.0, sample=64, kind_vals="int4", exact=True, transA=tA,
+                  transB=tB, seed=5)
+    run_and_check("f32", 2048, 2048, 48, 1.0, 0.0, sample=64, c_nan=True, transA=tA, transB=tB)
+
+
+@pytest.mark.parametrize("kind", ["f32", "f16"])
+@pytest.mark.parametrize("tA,tB", OPS)
+def test_transposed_fast_paths(kind, tA, tB):
+    # whole tiles, 16-byte aligned rows, padded leading dimensions: the direct-to-LDS
+    # kernels (256x256 tiles at 4096^2, 128x128 below)
+    M = N = 4096
+    K = 256
+    a_cols, b_cols = (M if tA else K), (K if tB else N)
+    run_and_check(kind, M, N, K, 1.5, -0.5, lda=a_cols + 8, ldb=b_cols + 16, ldc=N + 4, sample=64,
+                  transA=tA, transB=tB)
+    run_and_check(kind, M, N, K, 1.0, 0.0, sample=32, kind_vals="int4", exact=True, transA=tA, transB=tB,
+                  seed=17)
+    if kind == "f32":
+        M, N, K = 2048, 2048, 320
+    else:
+        M, N, K = 512, 384, 320
+    a_cols, b_cols = (M if tA else K), (K if tB else N)
+    run_and_check(kind, M, N, K, 1.5, -0.5, lda=a_cols + 8, ldb=b_cols + 8, ldc=N + 4, sample=128,
+                  transA=tA, transB=tB)
+    run_and_check(kind, M, N, K, 1.0, 1.0, sample=64, kind_vals="int4", exact=True, transA=tA, transB=tB,
+                  seed=19)
+
+
+@pytest.mark.parametrize("tA,tB", OPS)
+def test_transposed_hgemm_register_whole_tiles(tA, tB):
+    # whole 128x128 tiles but K too short for the direct-to-LDS ring: unmasked register kernel
+    run_and_check("f16", 256, 256, 128, 1.5, -0.5, transA=tA, transB=tB)
+    run_and_check("f16", 256, 256, 128, 1.0, 0.0, kind_vals="int4", exact=True, transA=tA, transB=tB)
+
+
+@pytest.mark.parametrize("tA,tB", OPS)
+def test_transposed_batched(tA, tB):
+    batched_check(384, 256, 320, 3, 1.5, -0.5, transA=tA, transB=tB)
+    batched_check(33, 65, 17, 4, 1.0, 0.0, kind_vals="int4", exact=True, pad=1, transA=tA, transB=tB)
+    batched_check(200, 136, 72, 3, 1.0, 1.0, pad=3, share_a=True, transA=tA, transB=tB)
+
+
+@pytest.mark.parametrize("kind", ["f32", "f16"])
+@pytest.mark.parametrize("tA,tB", OPS)
+def test_transposed_matches_untransposed(kind, tA, tB):
+    # the same logical product through the plain and the op() entry points gives
+    # the same bits (all four combinations use one k order)
+    M, N, K = (4096, 4096, 512)
+    note(f"{kind} op() vs plain M={M} N={N} K={K} transA={int(tA)} transB={int(tB)}")
+    in_dtype = np.float32 if kind == "f32" else np.float16
+    p = si.gemm_problem(M, N, K, in_dtype=in_dtype, seed=61)
+    A2 = si.logical_transpose(p["A"], M, K) if tA else p["A"]
+    B2 = si.logical_transpose(p["B"], K, N) if tB else p["B"]
+    q = dict(p, transA=tA, transB=tB, lda=(M if tA else K), ldb=(K if tB else N))
+    dA, dB, dA2, dB2 = to_dev(p["A"]), to_dev(p["B"]), to_dev(A2), to_dev(B2)
+    dC1, dC2 = to_dev(p["C"]), to_dev(p["C"])
+    call(kind, p, 1.5, -0.5, dA, dB, dC1)
+    call(kind, q, 1.5, -0.5, dA2, dB2, dC2)
+    torch.cuda.synchronize()
+    assert torch.equal(dC1, dC2)
