@@ -385,3 +385,74 @@ def test_transposed_matches_untransposed(kind, tA, tB):
     call(kind, q, 1.5, -0.5, dA2, dB2, dC2)
     torch.cuda.synchronize()
     assert torch.equal(dC1, dC2)
+
+
+# ------------------------------------------------------------------ maximum sizes
+def test_batched_beyond_one_launch():
+    # more members than one launch's grid z holds (65535): the host splits the batch;
+    # members on both sides of the split are checked against the oracle
+    M, N, K, nb = 3, 5, 4, 70001
+    note(f"batched M={M} N={N} K={K} batch={nb} (split over launches)")
+    A = si.draw(101, nb * M * K).astype(np.float16)
+    B = si.draw(102, nb * K * N).astype(np.float16)
+    C = si.draw(103, nb * M * N)
+    dA, dB, dC = to_dev(A), to_dev(B), to_dev(C)
+    dg.gemm_batched_f16_f32acc(M, N, K, 1.5, dA, K, M * K, dB, N, K * N, -0.5, dC, N, M * N, nb)
+    torch.cuda.synchronize()
+    got = dC.cpu().numpy()
+    members = sorted({0, 1, 65533, 65534, 65535, 65536, 65537, nb - 1} |
+                     {int(x) % nb for x in si.splitmix64(7, 24)})
+    for b in members:
+        ref, bound = oracle.gemm_ref(M, N, K, 1.5, A[b * M * K:], K, B[b * K * N:], N, -0.5,
+                                     C[b * M * N: (b + 1) * M * N], N)
+        e = oracle.normalized_error(got[b * M * N: (b + 1) * M * N].reshape(M, N), ref, bound)
+        assert e <= TOL, f"member {b}: normalized error {e:.3e}"
+
+
+@pytest.mark.parametrize("M,N,K", [(256, 256, 256), (100, 70, 40)])
+def test_batched_offsets_beyond_32_bits(M, N, K):
+    # member 1 of each operand starts 2^31 + 64 elements after member 0: every
+    # batch offset must be formed in 64 bits (the gap is NaN, so a wrapped offset
+    # shows up as NaN or as a wrong value)
+    stride = (1 << 31) + 64
+    note(f"batched M={M} N={N} K={K} strides {stride} (64-bit member offsets)")
+    probs = [si.gemm_problem(M, N, K, in_dtype=np.float16, seed=300, batch=b) for b in range(2)]
+    dA = torch.full((stride + M * K,), float("nan"), dtype=torch.float16, device="cuda")
+    dB = torch.full((stride + K * N,), float("nan"), dtype=torch.float16, device="cuda")
+    dC = torch.full((stride + M * N,), float("nan"), dtype=torch.float32, device="cuda")
+    for b in range(2):
+        dA[b * stride: b * stride + M * K] = to_dev(probs[b]["A"])
+        dB[b * stride: b * stride + K * N] = to_dev(probs[b]["B"])
+        dC[b * stride: b * stride + M * N] = to_dev(probs[b]["C"])
+    dg.gemm_batched_f16_f32acc(M, N, K, 1.0, dA, K, stride, dB, N, stride, 1.0, dC, N, stride, 2)
+    torch.cuda.synchronize()
+    for b in range(2):
+        got = dC[b * stride: b * stride + M * N].view(M, N).cpu().numpy()
+        ref, bound = oracle.gemm_ref(M, N, K, 1.0, probs[b]["A"], K, probs[b]["B"], N, 1.0, probs[b]["C"], N)
+        e = oracle.normalized_error(got, ref, bound)
+        assert e <= TOL, f"member {b}: normalized error {e:.3e}"
+    # the gap after member 0's C is untouched
+    assert bool(torch.isnan(dC[M * N: M * N + 4096]).all())
+    del dA, dB, dC
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("transA", [False, True])
+def test_row_offsets_beyond_32_bits(transA):
+    # a leading dimension of 2^29 + 4 floats: row starts lie beyond 2^31 elements
+    # (an 8 GiB operand of five stored rows), so row offsets are formed in 64 bits
+    M, N, K = 5, 40, 5
+    ld = (1 << 29) + 4
+    note(f"f32 M={M} N={N} K={K} lda={ld} transA={int(transA)} (64-bit row offsets)")
+    a_rows, a_cols = (K, M) if transA else (M, K)
+    p = si.gemm_problem(M, N, K, in_dtype=np.float32, seed=310, transA=transA)
+    dA = torch.full(((a_rows - 1) * ld + a_cols,), float("nan"), dtype=torch.float32, device="cuda")
+    for r in range(a_rows):
+        dA[r * ld: r * ld + a_cols] = to_dev(p["A"][r * a_cols: (r + 1) * a_cols])
+    dB, dC = to_dev(p["B"]), to_dev(p["C"])
+    dg.gemm_f32_ex(int(transA), 0, M, N, K, 1.5, dA, ld, dB, N, -0.5, dC, N)
+    torch.cuda.synchronize()
+    ref, bound = oracle.gemm_ref(M, N, K, 1.5, p["A"], a_cols, p["B"], N, -0.5, p["C"], N, transA=transA)
+    assert oracle.normalized_error(rows_of(dC, M, N, N), ref, bound) <= TOL
+    del dA
+    torch.cuda.empty_cache()
