@@ -4,8 +4,9 @@
 // the A fragment as the second, so a 32x32 accumulator block holds the
 // transposed product: register r of lane l is C[row l%32][col 8*(r/4) +
 // 4*(l/32) + r%4] of the block.  Registers 4g..4g+3 are therefore four
-// consecutive columns of one row, written with one 16-byte store when the
-// row pointer allows it.
+// consecutive columns of one row, written with one 16-byte store.  Multi-dword
+// global accesses need only dword alignment on CDNA, so the 16-byte store is
+// used for any fp32 C (every float is 4-byte aligned).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -13,20 +14,22 @@
 namespace mi355gemm {
 
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+// four consecutive floats in global memory at dword (not 16-byte) alignment
+typedef float f32x4_g __attribute__((ext_vector_type(4), aligned(4)));
 
 // C[row][col..col+3] = alpha*acc + beta*C (beta term only when WITH_C).
-// MASK: rows >= M and columns >= N are skipped.  VEC: 16-byte access allowed
-// (ldc % 4 == 0 and C 16-byte aligned; col is a multiple of 4).
+// MASK: rows >= M and columns >= N are skipped (a row whose four columns are
+// all inside is still written with one 16-byte access).
 template <bool MASK, bool WITH_C>
 __device__ __forceinline__ void store_row4(float *C, long long ldc, long long row, long long col,
-                                           f32x4_t acc, float alpha, float beta, int M, int N, bool vec)
+                                           f32x4_t acc, float alpha, float beta, int M, int N)
 {
     if (MASK && row >= M) return;
     float *dst = C + row * ldc + col;
-    if (vec && (!MASK || col + 3 < N)) {
+    if (!MASK || col + 3 < N) {
         f32x4_t v = alpha * acc;
-        if (WITH_C) v += beta * *reinterpret_cast<const f32x4_t *>(dst);
-        *reinterpret_cast<f32x4_t *>(dst) = v;
+        if (WITH_C) v += beta * f32x4_t(*reinterpret_cast<const f32x4_g *>(dst));
+        *reinterpret_cast<f32x4_g *>(dst) = v;
         return;
     }
 #pragma unroll

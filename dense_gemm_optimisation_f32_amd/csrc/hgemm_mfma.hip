@@ -56,6 +56,9 @@ typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef short short4v __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+// 16 bytes in global memory at dword (not 16-byte) alignment: multi-dword
+// global loads need only dword alignment on CDNA
+typedef unsigned int u32x4_g __attribute__((ext_vector_type(4), aligned(4)));
 typedef __attribute__((address_space(3))) short4v lds_short4;
 
 struct HgemmArgs {
@@ -115,16 +118,16 @@ __device__ __forceinline__ u32x4 load8_masked(const uint16_t *p, int valid)
 }
 
 // Eight consecutive halves (r, c..c+7) of a row-major rows x cols matrix X;
-// with MASK, elements outside it read as zero (VEC: one 16-byte load where all
-// eight are inside).
+// with MASK, elements outside it read as zero.  VEC: row starts are 4-byte
+// aligned, so eight halves inside the matrix are one 16-byte load.
 template <bool MASK, bool VEC>
 __device__ __forceinline__ u32x4 load8(const uint16_t *X, long long ld, long long r, long long c, long long rows,
                                        long long cols)
 {
     const uint16_t *src = X + r * ld + c;
-    if (!MASK) return *reinterpret_cast<const u32x4 *>(src);
+    if (!MASK) return *reinterpret_cast<const u32x4_g *>(src);
     if (r >= rows || c >= cols) return u32x4{0u, 0u, 0u, 0u};
-    if (VEC && c + 8 <= cols) return *reinterpret_cast<const u32x4 *>(src);
+    if (VEC && c + 8 <= cols) return *reinterpret_cast<const u32x4_g *>(src);
     return load8_masked(src, (int)(cols - c));
 }
 
@@ -271,7 +274,6 @@ __global__ __launch_bounds__(256) void hgemm_mfma_kernel(HgemmArgs p)
     // Epilogue (operands were swapped, so each lane holds four consecutive
     // columns of one row per register quad; see epilogue.h).
     const float alpha = p.alpha, beta = p.beta;
-    const bool cvec = (ldc % 4 == 0) && (reinterpret_cast<uintptr_t>(C) % 16 == 0);
     auto epilogue = [&](auto with_c) {
 #pragma unroll
         for (int i = 0; i < Cfg::FM; ++i) {
@@ -283,7 +285,7 @@ __global__ __launch_bounds__(256) void hgemm_mfma_kernel(HgemmArgs p)
                     const long long col = n0 + wn * Cfg::TN + 32 * jj + 8 * g + 4 * lk;
                     const f32x4_t v = {acc[i][jj][4 * g], acc[i][jj][4 * g + 1], acc[i][jj][4 * g + 2],
                                        acc[i][jj][4 * g + 3]};
-                    store_row4<MASK, decltype(with_c)::value>(C, ldc, row, col, v, alpha, beta, M, N, cvec);
+                    store_row4<MASK, decltype(with_c)::value>(C, ldc, row, col, v, alpha, beta, M, N);
                 }
             }
         }
@@ -582,7 +584,6 @@ __global__ __launch_bounds__(Cfg::NT) void hgemm_dma_kernel(HgemmArgs p)
     }
 
     const float alpha = p.alpha, beta = p.beta;
-    const bool cvec = (ldc % 4 == 0) && (reinterpret_cast<uintptr_t>(C) % 16 == 0);
     auto epilogue = [&](auto with_c) {
 #pragma unroll
         for (int i = 0; i < Cfg::FM; ++i) {
@@ -594,7 +595,7 @@ __global__ __launch_bounds__(Cfg::NT) void hgemm_dma_kernel(HgemmArgs p)
                     const long long col = n0 + wn * Cfg::TN + 32 * jj + 8 * g + 4 * lk;
                     const f32x4_t v = {acc[i][jj][4 * g], acc[i][jj][4 * g + 1], acc[i][jj][4 * g + 2],
                                        acc[i][jj][4 * g + 3]};
-                    store_row4<false, decltype(with_c)::value>(C, ldc, row, col, v, alpha, beta, 0, 0, cvec);
+                    store_row4<false, decltype(with_c)::value>(C, ldc, row, col, v, alpha, beta, 0, 0);
                 }
             }
         }
@@ -630,10 +631,12 @@ hipError_t launch_cfg(const GemmProblem &q, hipStream_t stream)
     a.C = q.C; a.ldc = q.ldc; a.sC = q.strideC;
     a.tiles_m = (q.M + Cfg::BM - 1) / Cfg::BM;
     a.tiles_n = (q.N + Cfg::BN - 1) / Cfg::BN;
-    const bool vec = (q.lda % 8 == 0) && (q.ldb % 8 == 0) &&
-                     (reinterpret_cast<uintptr_t>(q.A) % 16 == 0) &&
-                     (reinterpret_cast<uintptr_t>(q.B) % 16 == 0) &&
-                     (q.strideA % 8 == 0) && (q.strideB % 8 == 0);
+    // 16-byte loads need 4-byte aligned row starts (column offsets are
+    // multiples of eight halves)
+    const bool vec = (q.lda % 2 == 0) && (q.ldb % 2 == 0) &&
+                     (reinterpret_cast<uintptr_t>(q.A) % 4 == 0) &&
+                     (reinterpret_cast<uintptr_t>(q.B) % 4 == 0) &&
+                     (q.strideA % 2 == 0) && (q.strideB % 2 == 0);
     const bool whole = vec && q.M % Cfg::BM == 0 && q.N % Cfg::BN == 0 && q.K % Cfg::BK == 0;
     const dim3 grid(a.tiles_m * a.tiles_n, 1, q.batch);
     if (!q.transA && !q.transB)

@@ -22,8 +22,9 @@
 // Why MFMA and not VALU: fp32 VALU FMA without the packed form reaches half of
 // the chip's fp32 rate; the fp32 MFMA path has the full rate.
 // Two instantiations per tile shape: MASK = false for problems made of whole
-// tiles with 16-byte aligned rows (no bounds checks anywhere), MASK = true for
-// everything else.  Workgroups are mapped to tiles XCD by XCD (tile_order.h).
+// tiles (no bounds checks anywhere), MASK = true for everything else.  Global
+// accesses are 16 bytes wide at any leading dimension: multi-dword global
+// loads and stores need only dword alignment on CDNA.  Workgroups are mapped to tiles XCD by XCD (tile_order.h).
 //
 // Transposed operands (C = alpha*op(A)op(B) + beta*C, the MindNotes 'GEMM'
 // page, section "core problem and arithmetic characteristics"): every kernel
@@ -72,16 +73,16 @@ struct SgCfg {
 };
 
 // Four consecutive floats (r, c..c+3) of a row-major rows x cols matrix X with
-// leading dimension ld; with MASK, elements outside the matrix read as zero
-// (VEC: a 16-byte load is allowed where all four are inside).
-template <bool MASK, bool VEC>
-__device__ __forceinline__ float4 load4(const float *X, long long ld, long long r, long long c, long long rows,
-                                        long long cols)
+// leading dimension ld, as one 16-byte load (dword alignment suffices for it);
+// with MASK, elements outside the matrix read as zero.
+template <bool MASK>
+__device__ __forceinline__ f32x4_t load4(const float *X, long long ld, long long r, long long c, long long rows,
+                                         long long cols)
 {
     const float *src = X + r * ld + c;
-    if (!MASK || (VEC && r < rows && c + 3 < cols)) return *reinterpret_cast<const float4 *>(src);
+    if (!MASK || (r < rows && c + 3 < cols)) return *reinterpret_cast<const f32x4_g *>(src);
     const bool rok = r < rows;
-    float4 v;
+    f32x4_t v;
     v.x = (rok && c + 0 < cols) ? src[0] : 0.f;
     v.y = (rok && c + 1 < cols) ? src[1] : 0.f;
     v.z = (rok && c + 2 < cols) ? src[2] : 0.f;
@@ -93,7 +94,7 @@ __device__ __forceinline__ float4 load4(const float *X, long long ld, long long 
 // MN-contiguous ([k][m] and [k][n]); a K-contiguous operand is transposed on
 // its way in by four scalar LDS writes, an MN-contiguous one is written as
 // 16-byte rows.
-template <class Cfg, bool MASK, bool VEC, bool TA, bool TB>
+template <class Cfg, bool MASK, bool TA, bool TB>
 __global__ __launch_bounds__(Cfg::NT) void sgemm_mfma_kernel(SgemmArgs p)
 {
     constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK;
@@ -118,22 +119,20 @@ __global__ __launch_bounds__(Cfg::NT) void sgemm_mfma_kernel(SgemmArgs p)
     float *C = p.C + (long long)blockIdx.z * p.sC;
     const long long lda = p.lda, ldb = p.ldb, ldc = p.ldc;
 
-    float4 ra[Cfg::A_LOADS], rb[Cfg::B_LOADS];
+    f32x4_t ra[Cfg::A_LOADS], rb[Cfg::B_LOADS];
 
     auto load_tiles = [&](int k0) {
 #pragma unroll
         for (int i = 0; i < Cfg::A_LOADS; ++i) {
             const int id = i * Cfg::NT + tid;
             const int r = id / A_CPR, c = (id % A_CPR) * 4;
-            ra[i] = TA ? load4<MASK, VEC>(A, lda, k0 + r, m0 + c, K, M)
-                       : load4<MASK, VEC>(A, lda, m0 + r, k0 + c, M, K);
+            ra[i] = TA ? load4<MASK>(A, lda, k0 + r, m0 + c, K, M) : load4<MASK>(A, lda, m0 + r, k0 + c, M, K);
         }
 #pragma unroll
         for (int i = 0; i < Cfg::B_LOADS; ++i) {
             const int id = i * Cfg::NT + tid;
             const int r = id / B_CPR, c = (id % B_CPR) * 4;
-            rb[i] = TB ? load4<MASK, VEC>(B, ldb, n0 + r, k0 + c, N, K)
-                       : load4<MASK, VEC>(B, ldb, k0 + r, n0 + c, K, N);
+            rb[i] = TB ? load4<MASK>(B, ldb, n0 + r, k0 + c, N, K) : load4<MASK>(B, ldb, k0 + r, n0 + c, K, N);
         }
     };
 
@@ -145,7 +144,7 @@ __global__ __launch_bounds__(Cfg::NT) void sgemm_mfma_kernel(SgemmArgs p)
             const int id = i * Cfg::NT + tid;
             const int r = id / A_CPR, c = (id % A_CPR) * 4;
             if (TA) {   // r = k, c = m
-                *reinterpret_cast<float4 *>(&as[r * LDA_S + c]) = ra[i];
+                *reinterpret_cast<f32x4_t *>(&as[r * LDA_S + c]) = ra[i];
             } else {    // r = m, c = k
                 as[(c + 0) * LDA_S + r] = ra[i].x;
                 as[(c + 1) * LDA_S + r] = ra[i].y;
@@ -163,7 +162,7 @@ __global__ __launch_bounds__(Cfg::NT) void sgemm_mfma_kernel(SgemmArgs p)
                 bs[(c + 2) * LDB_S + r] = rb[i].z;
                 bs[(c + 3) * LDB_S + r] = rb[i].w;
             } else {    // r = k, c = n
-                *reinterpret_cast<float4 *>(&bs[r * LDB_S + c]) = rb[i];
+                *reinterpret_cast<f32x4_t *>(&bs[r * LDB_S + c]) = rb[i];
             }
         }
     };
@@ -211,7 +210,6 @@ __global__ __launch_bounds__(Cfg::NT) void sgemm_mfma_kernel(SgemmArgs p)
     // Epilogue (operands were swapped, so each lane holds four consecutive
     // columns of one row per register quad; see epilogue.h).
     const float alpha = p.alpha, beta = p.beta;
-    const bool cvec = (ldc % 4 == 0) && (reinterpret_cast<uintptr_t>(C) % 16 == 0);
     auto epilogue = [&](auto with_c) {
 #pragma unroll
         for (int i = 0; i < Cfg::FM; ++i) {
@@ -223,7 +221,7 @@ __global__ __launch_bounds__(Cfg::NT) void sgemm_mfma_kernel(SgemmArgs p)
                     const long long col = n0 + wn * Cfg::TN + 32 * jj + 8 * g + 4 * lk;
                     const f32x4_t v = {acc[i][jj][4 * g], acc[i][jj][4 * g + 1], acc[i][jj][4 * g + 2],
                                        acc[i][jj][4 * g + 3]};
-                    store_row4<MASK, decltype(with_c)::value>(C, ldc, row, col, v, alpha, beta, M, N, cvec);
+                    store_row4<MASK, decltype(with_c)::value>(C, ldc, row, col, v, alpha, beta, M, N);
                 }
             }
         }
@@ -439,7 +437,6 @@ __global__ __launch_bounds__(Cfg::NT) void sgemm_dma_kernel(SgemmArgs p)
     }
 
     const float alpha = p.alpha, beta = p.beta;
-    const bool cvec = (ldc % 4 == 0) && (reinterpret_cast<uintptr_t>(C) % 16 == 0);
     auto epilogue = [&](auto with_c) {
 #pragma unroll
         for (int i = 0; i < Cfg::FM; ++i) {
@@ -451,7 +448,7 @@ __global__ __launch_bounds__(Cfg::NT) void sgemm_dma_kernel(SgemmArgs p)
                     const long long col = n0 + wn * Cfg::TN + 32 * jj + 8 * g + 4 * lk;
                     const f32x4_t v = {acc[i][jj][4 * g], acc[i][jj][4 * g + 1], acc[i][jj][4 * g + 2],
                                        acc[i][jj][4 * g + 3]};
-                    store_row4<false, decltype(with_c)::value>(C, ldc, row, col, v, alpha, beta, 0, 0, cvec);
+                    store_row4<false, decltype(with_c)::value>(C, ldc, row, col, v, alpha, beta, 0, 0);
                 }
             }
         }
@@ -526,8 +523,7 @@ struct SgSmallCfg {
     static constexpr int TM = 32 * FM, TN = 32 * FN;
 };
 
-// VEC: every K-contiguous operand has 16-byte aligned rows.
-template <class Cfg, bool VEC, bool TA, bool TB>
+template <class Cfg, bool TA, bool TB>
 __global__ __launch_bounds__(256) void sgemm_small_kernel(SgemmArgs p)
 {
     constexpr int FM = Cfg::FM, FN = Cfg::FN, KW = Cfg::KW, P = Cfg::P;
@@ -571,8 +567,8 @@ __global__ __launch_bounds__(256) void sgemm_small_kernel(SgemmArgs p)
     // Four k of one operand row or column starting at kq (zero outside).
     auto quad = [&](const float *x, long long stride, bool ok, int kq, bool kcontig) {
         f32x4_t v;
-        if (kcontig && VEC && ok && kq + 3 < ke) {
-            v = *reinterpret_cast<const f32x4_t *>(x + kq);
+        if (kcontig && ok && kq + 3 < ke) {
+            v = *reinterpret_cast<const f32x4_g *>(x + kq);
         } else {
 #pragma unroll
             for (int e = 0; e < 4; ++e) v[e] = (ok && kq + e < ke) ? x[(long long)(kq + e) * stride] : 0.f;
@@ -630,7 +626,6 @@ __global__ __launch_bounds__(256) void sgemm_small_kernel(SgemmArgs p)
 
     // Wave w reduces quad g = w of every block and writes it.
     const float alpha = p.alpha, beta = p.beta;
-    const bool cvec = (ldc % 4 == 0) && (reinterpret_cast<uintptr_t>(C) % 16 == 0);
     const int g = w;
 #pragma unroll
     for (int i = 0; i < FM; ++i)
@@ -642,20 +637,12 @@ __global__ __launch_bounds__(256) void sgemm_small_kernel(SgemmArgs p)
             const long long row = m0 + 32 * i + lr;
             const long long col = n0 + 32 * j + 8 * g + 4 * lk;
             if (beta != 0.f)
-                store_row4<true, true>(C, ldc, row, col, sum, alpha, beta, M, N, cvec);
+                store_row4<true, true>(C, ldc, row, col, sum, alpha, beta, M, N);
             else
-                store_row4<true, false>(C, ldc, row, col, sum, alpha, beta, M, N, cvec);
+                store_row4<true, false>(C, ldc, row, col, sum, alpha, beta, M, N);
         }
 }
 
-template <class Cfg, bool TA, bool TB>
-void launch_small_kernel(const SgemmArgs &a, bool vec, dim3 grid, hipStream_t stream)
-{
-    if (vec)
-        hipLaunchKernelGGL((sgemm_small_kernel<Cfg, true, TA, TB>), grid, dim3(Cfg::NT), 0, stream, a);
-    else
-        hipLaunchKernelGGL((sgemm_small_kernel<Cfg, false, TA, TB>), grid, dim3(Cfg::NT), 0, stream, a);
-}
 
 template <class Cfg>
 hipError_t launch_small(const GemmProblem &q, hipStream_t stream)
@@ -668,20 +655,15 @@ hipError_t launch_small(const GemmProblem &q, hipStream_t stream)
     a.C = q.C; a.ldc = q.ldc; a.sC = q.strideC;
     a.tiles_m = (q.M + Cfg::TM - 1) / Cfg::TM;
     a.tiles_n = (q.N + Cfg::TN - 1) / Cfg::TN;
-    // 16-byte quads are loaded from K-contiguous operands only
-    const bool veca = q.transA || ((q.lda % 4 == 0) && (reinterpret_cast<uintptr_t>(q.A) % 16 == 0) &&
-                                   (q.strideA % 4 == 0));
-    const bool vecb = !q.transB || ((q.ldb % 4 == 0) && (reinterpret_cast<uintptr_t>(q.B) % 16 == 0) &&
-                                    (q.strideB % 4 == 0));
-    const dim3 grid(a.tiles_m * a.tiles_n, 1, q.batch);
+    const dim3 grid(a.tiles_m * a.tiles_n, 1, q.batch), block(Cfg::NT);
     if (!q.transA && !q.transB)
-        launch_small_kernel<Cfg, false, false>(a, veca && vecb, grid, stream);
+        hipLaunchKernelGGL((sgemm_small_kernel<Cfg, false, false>), grid, block, 0, stream, a);
     else if (!q.transA)
-        launch_small_kernel<Cfg, false, true>(a, veca && vecb, grid, stream);
+        hipLaunchKernelGGL((sgemm_small_kernel<Cfg, false, true>), grid, block, 0, stream, a);
     else if (!q.transB)
-        launch_small_kernel<Cfg, true, false>(a, veca && vecb, grid, stream);
+        hipLaunchKernelGGL((sgemm_small_kernel<Cfg, true, false>), grid, block, 0, stream, a);
     else
-        launch_small_kernel<Cfg, true, true>(a, veca && vecb, grid, stream);
+        hipLaunchKernelGGL((sgemm_small_kernel<Cfg, true, true>), grid, block, 0, stream, a);
     return hipGetLastError();
 }
 
@@ -691,15 +673,13 @@ using SgSmall32 = SgSmallCfg<1, 1>;
 using SgBig = SgCfg<128, 128, 16, 2, 2>;
 
 template <class Cfg, bool TA, bool TB>
-void launch_cfg_kernel(const SgemmArgs &a, bool whole, bool vec, dim3 grid, hipStream_t stream)
+void launch_cfg_kernel(const SgemmArgs &a, bool whole, dim3 grid, hipStream_t stream)
 {
     const dim3 block(Cfg::NT);
     if (whole)
-        hipLaunchKernelGGL((sgemm_mfma_kernel<Cfg, false, true, TA, TB>), grid, block, 0, stream, a);
-    else if (vec)
-        hipLaunchKernelGGL((sgemm_mfma_kernel<Cfg, true, true, TA, TB>), grid, block, 0, stream, a);
+        hipLaunchKernelGGL((sgemm_mfma_kernel<Cfg, false, TA, TB>), grid, block, 0, stream, a);
     else
-        hipLaunchKernelGGL((sgemm_mfma_kernel<Cfg, true, false, TA, TB>), grid, block, 0, stream, a);
+        hipLaunchKernelGGL((sgemm_mfma_kernel<Cfg, true, TA, TB>), grid, block, 0, stream, a);
 }
 
 template <class Cfg>
@@ -713,20 +693,16 @@ hipError_t launch_cfg(const GemmProblem &q, hipStream_t stream)
     a.C = q.C; a.ldc = q.ldc; a.sC = q.strideC;
     a.tiles_m = (q.M + Cfg::BM - 1) / Cfg::BM;
     a.tiles_n = (q.N + Cfg::BN - 1) / Cfg::BN;
-    const bool vec = (q.lda % 4 == 0) && (q.ldb % 4 == 0) &&
-                     (reinterpret_cast<uintptr_t>(q.A) % 16 == 0) &&
-                     (reinterpret_cast<uintptr_t>(q.B) % 16 == 0) &&
-                     (q.strideA % 4 == 0) && (q.strideB % 4 == 0);
-    const bool whole = vec && q.M % Cfg::BM == 0 && q.N % Cfg::BN == 0 && q.K % Cfg::BK == 0;
+    const bool whole = q.M % Cfg::BM == 0 && q.N % Cfg::BN == 0 && q.K % Cfg::BK == 0;
     const dim3 grid(a.tiles_m * a.tiles_n, 1, q.batch);
     if (!q.transA && !q.transB)
-        launch_cfg_kernel<Cfg, false, false>(a, whole, vec, grid, stream);
+        launch_cfg_kernel<Cfg, false, false>(a, whole, grid, stream);
     else if (!q.transA)
-        launch_cfg_kernel<Cfg, false, true>(a, whole, vec, grid, stream);
+        launch_cfg_kernel<Cfg, false, true>(a, whole, grid, stream);
     else if (!q.transB)
-        launch_cfg_kernel<Cfg, true, false>(a, whole, vec, grid, stream);
+        launch_cfg_kernel<Cfg, true, false>(a, whole, grid, stream);
     else
-        launch_cfg_kernel<Cfg, true, true>(a, whole, vec, grid, stream);
+        launch_cfg_kernel<Cfg, true, true>(a, whole, grid, stream);
     return hipGetLastError();
 }
 
