@@ -381,36 +381,50 @@ __global__ __launch_bounds__(Cfg::NT) void sgemm_dma_kernel(SgemmArgs p)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    auto compute_slice = [&](int slot) {
+    // Operand fragments of one eight-k step u: element e of fa[i] / fb[j] is the
+    // operand of MFMA (u, e) for block i / j.  A K-contiguous fragment is one
+    // 16-byte read, an MN-contiguous one four 4-byte reads.
+    auto read_frags = [&](int slot, int u, f32x4v *fa, f32x4v *fb) {
         const unsigned base = lds0 + slot * Cfg::SLOT_BYTES;
 #pragma unroll
-        for (int u = 0; u < BK / 8; ++u) {
-            f32x4v qa[Cfg::FM], qb[Cfg::FN];
+        for (int i = 0; i < Cfg::FM; ++i) {
             if constexpr (A_KC) {
+                fa[i] = *(const lds_f32x4 *)(uintptr_t)(base + rowA[i] + 16 * (tA[i] ^ (2u * u)));
+            } else {
 #pragma unroll
-                for (int i = 0; i < Cfg::FM; ++i)
-                    qa[i] = *(const lds_f32x4 *)(uintptr_t)(base + rowA[i] + 16 * (tA[i] ^ (2u * u)));
+                for (int e = 0; e < 4; ++e)
+                    fa[i][e] = *(const lds_f32 *)(uintptr_t)(base + rowA[i] + (8 * u + e) * BM * 4);
             }
+        }
+#pragma unroll
+        for (int j = 0; j < Cfg::FN; ++j) {
             if constexpr (B_KC) {
+                fb[j] = *(const lds_f32x4 *)(uintptr_t)(base + rowB[j] + 16 * (tB[j] ^ (2u * u)));
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    fb[j][e] = *(const lds_f32 *)(uintptr_t)(base + rowB[j] + (8 * u + e) * BN * 4);
+            }
+        }
+    };
+    auto mfmas = [&](const f32x4v *fa, const f32x4v *fb) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+            for (int i = 0; i < Cfg::FM; ++i)
 #pragma unroll
                 for (int j = 0; j < Cfg::FN; ++j)
-                    qb[j] = *(const lds_f32x4 *)(uintptr_t)(base + rowB[j] + 16 * (tB[j] ^ (2u * u)));
-            }
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(fb[j][e], fa[i][e], acc[i][j], 0, 0, 0);
+    };
+    // Issue the LDS reads of the next step one after each of this step's first
+    // MFMAs, so they have the rest of the step to land.
+    constexpr int READS = Cfg::FM * (A_KC ? 1 : 4) + Cfg::FN * (B_KC ? 1 : 4);
+    static_assert(READS <= 4 * Cfg::FM * Cfg::FN, "more reads than MFMAs per step");
+    auto interleave = [&]() {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                float a[Cfg::FM], b[Cfg::FN];
-#pragma unroll
-                for (int i = 0; i < Cfg::FM; ++i)
-                    a[i] = A_KC ? qa[i][e] : *(const lds_f32 *)(uintptr_t)(base + rowA[i] + (8 * u + e) * BM * 4);
-#pragma unroll
-                for (int j = 0; j < Cfg::FN; ++j)
-                    b[j] = B_KC ? qb[j][e] : *(const lds_f32 *)(uintptr_t)(base + rowB[j] + (8 * u + e) * BN * 4);
-#pragma unroll
-                for (int i = 0; i < Cfg::FM; ++i)
-#pragma unroll
-                    for (int j = 0; j < Cfg::FN; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(b[j], a[i], acc[i][j], 0, 0, 0);
-            }
+        for (int r = 0; r < READS; ++r) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
         }
     };
     auto lds_barrier = [&]() {
@@ -421,18 +435,47 @@ __global__ __launch_bounds__(Cfg::NT) void sgemm_dma_kernel(SgemmArgs p)
     constexpr int LOADS = Cfg::A_LOADS + Cfg::B_LOADS;
     static_assert(LOADS < 64, "vmcnt range");
 
+    // Fragments are double-buffered in registers: step u+1's are read while
+    // step u's MFMAs run.  Before the last step of slice t, once slice t+1 has
+    // landed for every wave (own loads drained, then the barrier) and every
+    // wave holds its slice-t fragments, the slot of slice t is refilled with
+    // slice t+2 and the first fragments of slice t+1 are read.
+    constexpr int NU = BK / 8;
+    f32x4v fa[2][Cfg::FM], fb[2][Cfg::FN];
+    auto step = [&](int t, auto refill) {
+        const int slot = t & 1;
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
+            const int cur = u & 1, nxt = cur ^ 1;
+            if (u + 1 < NU) {
+                read_frags(slot, u + 1, fa[nxt], fb[nxt]);
+            } else {
+                __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): slice t+1 done for this lane
+                __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's slice-t reads are done
+                lds_barrier();
+                if (decltype(refill)::value) issue_slice(t + 2, slot);
+                read_frags(slot ^ 1, 0, fa[nxt], fb[nxt]);
+            }
+            mfmas(fa[cur], fb[cur]);
+            interleave();
+        }
+    };
+
     const int nk = p.K / BK;   // >= 2 (checked by the launcher)
     issue_slice(0, 0);
     issue_slice(1, 1);
     __builtin_amdgcn_s_waitcnt((LOADS & 15) | ((LOADS >> 4) << 14) | (7 << 4) | (15 << 8));   // slice 0 done
     lds_barrier();
-    for (int t = 0; t < nk; ++t) {
-        compute_slice(t & 1);
-        if (t + 1 < nk) {
-            __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): slice t+1 done for this lane
-            __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's slice-t reads are done
-            lds_barrier();
-            if (t + 2 < nk) issue_slice(t + 2, t & 1);
+    read_frags(0, 0, fa[0], fb[0]);
+    for (int t = 0; t + 2 < nk; ++t) step(t, std::true_type{});
+    step(nk - 2, std::false_type{});
+    {   // last slice: resident, nothing left to fetch
+        const int slot = (nk - 1) & 1;
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
+            const int cur = u & 1, nxt = cur ^ 1;
+            if (u + 1 < NU) read_frags(slot, u + 1, fa[nxt], fb[nxt]);
+            mfmas(fa[cur], fb[cur]);
         }
     }
 
