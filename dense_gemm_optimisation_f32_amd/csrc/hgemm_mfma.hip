@@ -28,9 +28,11 @@
 //   * workgroups are mapped to tiles so that the tiles one XCD (one L2) runs
 //     form a compact block of C;
 //   * epilogue C = alpha*acc + beta*C (C not read when beta == 0).
-// Two instantiations per tile shape: MASK = false for problems made of whole
-// tiles with 16-byte aligned rows (no bounds checks anywhere), MASK = true for
-// everything else (out-of-range elements load as zero, stores are masked).
+// Instantiations per tile shape: MASK = false for problems made of whole
+// tiles whose rows start 4-byte aligned (no bounds checks anywhere), MASK =
+// true for everything else (out-of-range elements load as zero, stores are
+// masked; VEC says whether rows start 4-byte aligned, which allows 16-byte
+// loads -- CDNA's multi-dword global loads need only dword alignment).
 //
 // Transposed operands (C = alpha*op(A)op(B) + beta*C, the MindNotes 'GEMM'
 // page, section "core problem and arithmetic characteristics"): each kernel is

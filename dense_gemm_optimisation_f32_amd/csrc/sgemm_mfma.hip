@@ -24,7 +24,8 @@
 // Two instantiations per tile shape: MASK = false for problems made of whole
 // tiles (no bounds checks anywhere), MASK = true for everything else.  Global
 // accesses are 16 bytes wide at any leading dimension: multi-dword global
-// loads and stores need only dword alignment on CDNA.  Workgroups are mapped to tiles XCD by XCD (tile_order.h).
+// loads and stores need only dword alignment on CDNA.  Workgroups are mapped
+// to tiles XCD by XCD (tile_order.h).
 //
 // Transposed operands (C = alpha*op(A)op(B) + beta*C, the MindNotes 'GEMM'
 // page, section "core problem and arithmetic characteristics"): every kernel
