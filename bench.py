@@ -34,17 +34,28 @@ METRIC = "TFLOPS (2MNK/t) + % of dtype peak: SGEMM 4096x4096x1024, HGEMM 4096^3"
 PEAK_F32_TFLOPS = 157.3
 PEAK_F16_TFLOPS = 2516.6
 PEAK_HBM_GBS = 8000.0
+_CSRC = "dense_gemm_optimisation_f32_amd/csrc/"
+# the files whose code makes up each kernel (its source and the headers it includes)
 KERNEL_SOURCES = {
-    "sgemm": "dense_gemm_optimisation_f32_amd/csrc/sgemm_mfma.hip",
-    "hgemm": "dense_gemm_optimisation_f32_amd/csrc/hgemm_mfma.hip",
+    "sgemm": [_CSRC + f for f in ("sgemm_mfma.hip", "epilogue.h", "tile_order.h", "gemm_internal.h")],
+    "hgemm": [_CSRC + f for f in ("hgemm_mfma.hip", "epilogue.h", "tile_order.h", "gemm_internal.h")],
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.md")
 COPY_BYTES = 256 << 20   # size of the calibration copy (read and written)
 
 
 def source_digest(kind: str) -> str:
-    with open(os.path.join(ROOT, KERNEL_SOURCES[kind]), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Digest of a kernel's code: its files with comments and whitespace removed,
+    so that a counter record stays valid across comment-only edits."""
+    import re
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES[kind]:
+        with open(os.path.join(ROOT, rel)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
+    return h.hexdigest()[:16]
 
 
 def _traffic_records():
