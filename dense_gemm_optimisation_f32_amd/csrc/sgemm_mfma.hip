@@ -548,27 +548,28 @@ hipError_t launch_sg_dma(const GemmProblem &q, hipStream_t stream)
 // Small / under-filled problems: split K inside the workgroup.
 //
 // When even 128x128 tiles leave most CUs idle (M*N small next to K), one
-// workgroup owns a (32*FM) x (32*FN) tile of C and its four waves split K
-// into four contiguous ranges (multiples of 8).  Each wave streams its
+// workgroup owns a (32*FM) x (32*FN) tile of C and its KW waves split K
+// into KW contiguous ranges (multiples of 8).  Each wave streams its
 // operands straight from global memory into registers -- A as 16-byte quads
 // of four consecutive k of a row (element e of quad u feeds k pair
 // {8u+e, 8u+4+e}, as in the whole-tile kernel), B as one float per lane and k
 // -- keeping P steps of eight k in flight, and accumulates its partial tile on
-// the fp32 MFMA.  The four partial tiles meet in LDS and are summed in a fixed
-// order (wave 0 + wave 1 + wave 2 + wave 3), so results are deterministic; each
-// wave then finishes one quarter of the tile (its register quad) through the
-// alpha/beta epilogue.  Out-of-range rows, columns and k load as zero.
+// the fp32 MFMA.  The KW partial tiles meet in LDS and are summed in a fixed
+// order (wave 0 + wave 1 + ...), so results are deterministic; each wave then
+// finishes its share of the tile's register quads through the alpha/beta
+// epilogue.  Out-of-range rows, columns and k load as zero.
 // A transposed operand changes only the loads: a K-contiguous operand (A
 // stored M x K, B stored N x K) is read as 16-byte quads of four k, an
 // MN-contiguous one as one float per lane and k (coalesced across the lanes).
-template <int FM_, int FN_>
+template <int FM_, int FN_, int KW_ = 4>
 struct SgSmallCfg {
-    static constexpr int FM = FM_, FN = FN_, KW = 4, NT = 64 * KW, P = 4;
+    static constexpr int FM = FM_, FN = FN_, KW = KW_, NT = 64 * KW, P = 4;
     static constexpr int TM = 32 * FM, TN = 32 * FN;
+    static_assert(KW * FM * FN * 4 * 64 * 16 <= 160 * 1024, "partial tiles exceed LDS");
 };
 
 template <class Cfg, bool TA, bool TB>
-__global__ __launch_bounds__(256) void sgemm_small_kernel(SgemmArgs p)
+__global__ __launch_bounds__(Cfg::NT) void sgemm_small_kernel(SgemmArgs p)
 {
     constexpr int FM = Cfg::FM, FN = Cfg::FN, KW = Cfg::KW, P = Cfg::P;
     __shared__ f32x4_t part[KW * FM * FN * 4 * 64];
@@ -668,23 +669,26 @@ __global__ __launch_bounds__(256) void sgemm_small_kernel(SgemmArgs p)
                     f32x4_t{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
     __syncthreads();
 
-    // Wave w reduces quad g = w of every block and writes it.
+    // The FM*FN*4 (block, quad) pairs q = (i*FN + j)*4 + g are shared out
+    // round robin: wave w reduces pairs w, w + KW, ... over the KW partial
+    // tiles in wave order and writes them.
     const float alpha = p.alpha, beta = p.beta;
-    const int g = w;
+    constexpr int PAIRS = FM * FN * 4;
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+    for (int q0 = 0; q0 < PAIRS; q0 += KW) {
+        const int q = q0 + w;
+        if (PAIRS % KW != 0 && q >= PAIRS) break;
+        f32x4_t sum = part[q * 64 + lane];
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
-            f32x4_t sum = part[((i * FN + j) * 4 + g) * 64 + lane];
-#pragma unroll
-            for (int ww = 1; ww < KW; ++ww) sum += part[(((ww * FM + i) * FN + j) * 4 + g) * 64 + lane];
-            const long long row = m0 + 32 * i + lr;
-            const long long col = n0 + 32 * j + 8 * g + 4 * lk;
-            if (beta != 0.f)
-                store_row4<true, true>(C, ldc, row, col, sum, alpha, beta, M, N);
-            else
-                store_row4<true, false>(C, ldc, row, col, sum, alpha, beta, M, N);
-        }
+        for (int ww = 1; ww < KW; ++ww) sum += part[(ww * PAIRS + q) * 64 + lane];
+        const int b = q >> 2, g = q & 3, i = b / FN, j = b % FN;
+        const long long row = m0 + 32 * i + lr;
+        const long long col = n0 + 32 * j + 8 * g + 4 * lk;
+        if (beta != 0.f)
+            store_row4<true, true>(C, ldc, row, col, sum, alpha, beta, M, N);
+        else
+            store_row4<true, false>(C, ldc, row, col, sum, alpha, beta, M, N);
+    }
 }
 
 
@@ -711,8 +715,9 @@ hipError_t launch_small(const GemmProblem &q, hipStream_t stream)
     return hipGetLastError();
 }
 
-using SgSmall64 = SgSmallCfg<2, 2>;
-using SgSmall32 = SgSmallCfg<1, 1>;
+// eight waves, two per SIMD, so that one wave's loads overlap the other's MFMAs
+using SgSmall64 = SgSmallCfg<2, 2, 8>;
+using SgSmall32 = SgSmallCfg<1, 1, 8>;
 
 using SgBig = SgCfg<128, 128, 16, 2, 2>;
 
