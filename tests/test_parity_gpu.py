@@ -456,3 +456,33 @@ def test_row_offsets_beyond_32_bits(transA):
     assert oracle.normalized_error(rows_of(dC, M, N, N), ref, bound) <= TOL
     del dA
     torch.cuda.empty_cache()
+
+
+# ------------------------------------------------------------------ seeded random sweep
+def _sweep_cases(n):
+    """n problems drawn from a counter-based stream: shapes, padding, flags, alpha/beta."""
+    u = si.splitmix64(2024, 16 * n)
+    pick = lambda k, lo, hi: lo + int(u[k] % np.uint64(hi - lo + 1))
+    alphas, betas = [1.0, 1.5, -0.75, 0.0], [0.0, 1.0, -0.5, 2.0]
+    cases = []
+    for c in range(n):
+        b = 16 * c
+        cases.append(dict(kind="f32" if u[b] % np.uint64(2) == 0 else "f16",
+                          M=pick(b + 1, 1, 700), N=pick(b + 2, 1, 700), K=pick(b + 3, 1, 600),
+                          pa=pick(b + 4, 0, 9), pb=pick(b + 5, 0, 9), pc=pick(b + 6, 0, 9),
+                          tA=bool(u[b + 7] % np.uint64(2)), tB=bool(u[b + 8] % np.uint64(2)),
+                          alpha=alphas[int(u[b + 9] % np.uint64(4))], beta=betas[int(u[b + 10] % np.uint64(4))],
+                          ints=bool(u[b + 11] % np.uint64(3) == 0), seed=500 + c))
+    return cases
+
+
+@pytest.mark.parametrize("case", _sweep_cases(48), ids=lambda c: f"{c['kind']}-{c['M']}x{c['N']}x{c['K']}"
+                         f"-t{int(c['tA'])}{int(c['tB'])}")
+def test_random_sweep(case):
+    # alpha = 0 and beta = 0 combinations included: C <- beta*C without reading A, B
+    c = case
+    a_cols, b_cols = (c["M"] if c["tA"] else c["K"]), (c["K"] if c["tB"] else c["N"])
+    run_and_check(c["kind"], c["M"], c["N"], c["K"], c["alpha"], c["beta"],
+                  kind_vals="int4" if c["ints"] else "pm1", exact=c["ints"],
+                  lda=a_cols + c["pa"], ldb=b_cols + c["pb"], ldc=c["N"] + c["pc"],
+                  transA=c["tA"], transB=c["tB"], seed=c["seed"], c_nan=(c["beta"] == 0.0))
