@@ -52,6 +52,8 @@ int check(const GemmProblem &p, size_t elem_in)
             return GEMM_ERR_SIZE;
     }
     if (p.M == 0 || p.N == 0 || p.batch == 0) return GEMM_OK;
+    // one workgroup per tile of at least 32 x 32: the grid must fit a launch
+    if (((long long)p.M + 31) / 32 * (((long long)p.N + 31) / 32) > INT_MAX) return GEMM_ERR_SIZE;
     const bool reads_ab = p.K > 0 && p.alpha != 0.f;
     if (!p.C) return GEMM_ERR_NULL;
     if (reads_ab && (!p.A || !p.B)) return GEMM_ERR_NULL;

@@ -49,7 +49,8 @@ typedef struct ihipStream_t *hipStream_t; /* the HIP runtime's stream handle */
 
 enum {
     GEMM_OK = 0,
-    GEMM_ERR_SIZE = -1,      /* M, N, K or batch_count negative, or an extent overflows 64 bits */
+    GEMM_ERR_SIZE = -1,      /* M, N, K or batch_count negative, an extent overflows 64 bits, or
+                                ceil(M/32)*ceil(N/32) exceeds INT_MAX (one launch's grid) */
     GEMM_ERR_LD = -2,        /* lda < max(1,K), ldb < max(1,N) (with transA: lda < max(1,M); with
                                 transB: ldb < max(1,K)), ldc < max(1,N), negative stride, or
                                 strideC smaller than one C member when batch_count > 1 */

@@ -169,3 +169,11 @@ def test_binding_transposed_extent_check():
     with pytest.raises(dg.GemmError) as e:
         dg.gemm_f32_ex(2, 0, 4, 4, 4, 1.0, FAKE, 4, FAKE, 4, 0.0, FAKE, 4, stream=0)
     assert e.value.status == EOP
+
+
+def test_grid_too_large_is_refused(lib):
+    # ceil(M/32) * ceil(N/32) beyond INT_MAX cannot be one launch's grid: refused
+    # before any HIP call (the pointers are never dereferenced)
+    big = 2**31 - 1
+    assert f32(lib, big, big, 1, 1.0, FAKE, 1, FAKE, big, 0.0, FAKE, big) == ESIZE
+    assert f16(lib, big, big, 1, 1.0, FAKE, 1, FAKE, big, 0.0, FAKE, big) == ESIZE
