@@ -333,9 +333,14 @@ struct HgDmaCfg {
     static constexpr int A_BYTES = BM * BK * 2;                 // one A slice
     static constexpr int B_BYTES = BK * BN * 2;                 // one B slice
     static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
-    static constexpr int A_LOADS = A_BYTES / 1024 / NW;         // per wave per slice
-    static constexpr int B_LOADS = B_BYTES / 1024 / NW;
-    static_assert(A_BYTES % (1024 * NW) == 0 && B_BYTES % (1024 * NW) == 0, "slices must split over the waves");
+    // The upper half of the waves (one per SIMD) issues every direct-to-LDS
+    // load: a 1 KB load occupies the CU's vector-memory path for about 16
+    // cycles, and a wave blocked on issuing them cannot issue MFMAs, so the
+    // other wave on each SIMD is left free to keep the matrix core busy.
+    static constexpr int LW = NW / 2;                           // loading waves
+    static constexpr int A_LOADS = A_BYTES / 1024 / LW;         // per loading wave per slice
+    static constexpr int B_LOADS = B_BYTES / 1024 / LW;
+    static_assert(A_BYTES % (1024 * LW) == 0 && B_BYTES % (1024 * LW) == 0, "slices must split over the loaders");
     static_assert(A_CPR == 4 || A_CPR == 8, "K-contiguous rows of 64 or 128 bytes");
     static_assert(STAGES * STAGE_BYTES <= 160 * 1024, "LDS ring too large");
 };
@@ -442,23 +447,30 @@ __global__ __launch_bounds__(Cfg::NT) void hgemm_dma_kernel(HgemmArgs p)
     const long long stepB = B_KC ? BK * 2 : BK * ldb * 2;
     float *C = p.C + (long long)blockIdx.z * p.sC;
 
+    // Loading waves are NW-LW .. NW-1; loader index lw numbers their 1 KB
+    // pieces of each slice.
+    const int uwave = __builtin_amdgcn_readfirstlane(wave);
+    const bool loader = uwave >= Cfg::NW - Cfg::LW;
+    const int lw = loader ? uwave - (Cfg::NW - Cfg::LW) : 0;
     unsigned offA[Cfg::A_LOADS], offB[Cfg::B_LOADS];
 #pragma unroll
-    for (int i = 0; i < Cfg::A_LOADS; ++i) offA[i] = dma_offset<A_KC, BM, BK>(wave * Cfg::A_LOADS + i, lane, lda);
+    for (int i = 0; i < Cfg::A_LOADS; ++i) offA[i] = dma_offset<A_KC, BM, BK>(lw * Cfg::A_LOADS + i, lane, lda);
 #pragma unroll
-    for (int i = 0; i < Cfg::B_LOADS; ++i) offB[i] = dma_offset<B_KC, BN, BK>(wave * Cfg::B_LOADS + i, lane, ldb);
-    const int uwave = __builtin_amdgcn_readfirstlane(wave);
+    for (int i = 0; i < Cfg::B_LOADS; ++i) offB[i] = dma_offset<B_KC, BN, BK>(lw * Cfg::B_LOADS + i, lane, ldb);
     auto issue_slice = [&](int kt, int slot) {
+        if (!loader) return;
         const char *a = Ab + (long long)kt * stepA;
         const char *b = Bb + (long long)kt * stepB;
-        const unsigned la = lds0 + slot * Cfg::STAGE_BYTES + uwave * Cfg::A_LOADS * 1024;
-        const unsigned lb = lds0 + slot * Cfg::STAGE_BYTES + Cfg::A_BYTES + uwave * Cfg::B_LOADS * 1024;
+        const unsigned la = lds0 + slot * Cfg::STAGE_BYTES + lw * Cfg::A_LOADS * 1024;
+        const unsigned lb = lds0 + slot * Cfg::STAGE_BYTES + Cfg::A_BYTES + lw * Cfg::B_LOADS * 1024;
 #pragma unroll
         for (int i = 0; i < Cfg::A_LOADS; ++i) dma16(a, offA[i], la + 1024 * i);
 #pragma unroll
         for (int i = 0; i < Cfg::B_LOADS; ++i) dma16(b, offB[i], lb + 1024 * i);
     };
-    constexpr int LOADS = Cfg::A_LOADS + Cfg::B_LOADS;   // vector-memory ops per slice per lane
+    // vector-memory ops per slice per loading lane (the other waves have none
+    // outstanding, so their waits on this count return at once)
+    constexpr int LOADS = Cfg::A_LOADS + Cfg::B_LOADS;
 
     // Fragment read addresses (bytes, without the slot base): per substep for a
     // K-contiguous operand (blocks are 32 rows apart, which the swizzle
