@@ -266,9 +266,12 @@ struct SgDmaCfg {
     static constexpr int A_BYTES = BM * BK * 4;
     static constexpr int B_BYTES = BK * BN * 4;
     static constexpr int SLOT_BYTES = A_BYTES + B_BYTES;
-    static constexpr int A_LOADS = A_BYTES / 1024 / NW;      // per wave per slice
-    static constexpr int B_LOADS = B_BYTES / 1024 / NW;
-    static_assert(A_BYTES % (1024 * NW) == 0 && B_BYTES % (1024 * NW) == 0, "slices must split over the waves");
+    // The upper half of the waves (one per SIMD with eight waves) issues every
+    // slice load, so the other waves are never blocked issuing them.
+    static constexpr int LW = NW / 2;                        // loading waves
+    static constexpr int A_LOADS = A_BYTES / 1024 / LW;      // per loading wave per slice
+    static constexpr int B_LOADS = B_BYTES / 1024 / LW;
+    static_assert(A_BYTES % (1024 * LW) == 0 && B_BYTES % (1024 * LW) == 0, "slices must split over the loaders");
     static_assert(BM >= 64 && BN >= 64, "MN-contiguous slices need at least 16 chunks per row");
     static_assert(SLOTS * SLOT_BYTES <= 160 * 1024, "LDS slots too large");
 };
@@ -326,16 +329,19 @@ __global__ __launch_bounds__(Cfg::NT) void sgemm_dma_kernel(SgemmArgs p)
     const long long stepA = A_KC ? BK * 4 : BK * lda * 4;
     const long long stepB = B_KC ? BK * 4 : BK * ldb * 4;
 
+    const bool loader = uwave >= Cfg::NW - Cfg::LW;
+    const int lw = loader ? uwave - (Cfg::NW - Cfg::LW) : 0;   // loader index
     unsigned offA[Cfg::A_LOADS], offB[Cfg::B_LOADS];
 #pragma unroll
-    for (int i = 0; i < Cfg::A_LOADS; ++i) offA[i] = sg_dma_offset<A_KC, BM>(uwave * Cfg::A_LOADS + i, lane, lda);
+    for (int i = 0; i < Cfg::A_LOADS; ++i) offA[i] = sg_dma_offset<A_KC, BM>(lw * Cfg::A_LOADS + i, lane, lda);
 #pragma unroll
-    for (int i = 0; i < Cfg::B_LOADS; ++i) offB[i] = sg_dma_offset<B_KC, BN>(uwave * Cfg::B_LOADS + i, lane, ldb);
+    for (int i = 0; i < Cfg::B_LOADS; ++i) offB[i] = sg_dma_offset<B_KC, BN>(lw * Cfg::B_LOADS + i, lane, ldb);
     auto issue_slice = [&](int kt, int slot) {
+        if (!loader) return;
         const char *a = Ab + (long long)kt * stepA;
         const char *b = Bb + (long long)kt * stepB;
-        const unsigned la = lds0 + slot * Cfg::SLOT_BYTES + uwave * Cfg::A_LOADS * 1024;
-        const unsigned lb = lds0 + slot * Cfg::SLOT_BYTES + Cfg::A_BYTES + uwave * Cfg::B_LOADS * 1024;
+        const unsigned la = lds0 + slot * Cfg::SLOT_BYTES + lw * Cfg::A_LOADS * 1024;
+        const unsigned lb = lds0 + slot * Cfg::SLOT_BYTES + Cfg::A_BYTES + lw * Cfg::B_LOADS * 1024;
 #pragma unroll
         for (int i = 0; i < Cfg::A_LOADS; ++i) sg_dma16(a, offA[i], la + 1024 * i);
 #pragma unroll
