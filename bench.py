@@ -90,9 +90,14 @@ def main() -> int:
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn two rocprofv3 counter_collection.csv files (FETCH_SIZE, WRITE_SIZE) of a "
                          "--copy-calibration run into profiles/hbm_traffic.md; uses no GPU")
+    ap.add_argument("--write-counters", nargs="+", metavar="CSV",
+                    help="turn rocprofv3 counter_collection.csv files of the step's kernels into "
+                         "profiles/counters_sgemm4096x4096x1024_hgemm4096cube.md; uses no GPU")
     args = ap.parse_args()
     if args.write_traffic:
         return write_traffic(*args.write_traffic)
+    if args.write_counters:
+        return write_counters(args.write_counters)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: this library has no multi-GPU path "
@@ -214,6 +219,72 @@ def main() -> int:
         "extra": extra,
     }
     print(json.dumps(line), flush=True)
+    return 0
+
+
+COUNTER_PASSES = (
+    "SQ_INSTS_MFMA SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE "
+    "SQ_INSTS_VALU SQ_INSTS_VMEM_RD SQ_INSTS_VMEM_WR GRBM_GUI_ACTIVE",
+    "SQ_WAVES SQ_WAVE_CYCLES SQ_BUSY_CYCLES SQ_WAIT_INST_ANY SQ_WAIT_ANY SQ_WAIT_INST_LDS "
+    "SQ_ACTIVE_INST_LDS SQ_LDS_ADDR_CONFLICT GRBM_GUI_ACTIVE",
+)
+
+
+def write_counters(csv_paths) -> int:
+    """Per-launch means of rocprofv3 counters for the step's two kernels, with the
+    derived figures the kernel design relies on (cycles per MFMA instruction, LDS bank
+    conflicts), written as a markdown summary under profiles/."""
+    import csv
+
+    vals = {}          # kind -> counter -> list of per-dispatch values
+    durs = {}          # kind -> list of dispatch durations (ns)
+    names = {}
+    for path in csv_paths:
+        for r in csv.DictReader(open(path)):
+            name = r["Kernel_Name"]
+            kind = "sgemm" if "sgemm" in name else "hgemm" if "hgemm" in name else None
+            if kind is None:
+                continue
+            names[kind] = name
+            vals.setdefault(kind, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+            durs.setdefault(kind, []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    mean = {k: {c: sum(v) / len(v) for c, v in d.items()} for k, d in vals.items()}
+    kinds = [k for k in ("sgemm", "hgemm") if k in mean]
+    counters = sorted({c for k in kinds for c in mean[k]})
+    cmds = "\n".join(
+        f"cd /tmp && rocprofv3 --pmc {p} --output-format csv -d $R/gpurun_out/counters{i} -o c -- "
+        f"python3 $R/bench.py --no-cpu --no-extra --steps 3 --warmup 1" for i, p in enumerate(COUNTER_PASSES, 1))
+    cmds += ("\npython3 $R/bench.py --write-counters $R/gpurun_out/counters1/c_counter_collection.csv "
+             "$R/gpurun_out/counters2/c_counter_collection.csv   # R = repository root")
+    lines = ["# rocprofv3 counters per launch: bench step kernels (SGEMM 4096x4096x1024 fp32, "
+             "HGEMM 4096^3 fp16->fp32)", "",
+             "Commands (one MI355X; each pass is a run of its own):", "", "```", cmds, "```", "",
+             "Mean over the dispatches of each kernel in the runs (the counters are summed over the "
+             "whole device; SQ_LDS_* and SQ_*_CYCLES count in units of four cycles).", "",
+             "| counter | " + " | ".join(kinds) + " |", "|---|" + "---|" * len(kinds)]
+    for c in counters:
+        lines.append(f"| {c} | " + " | ".join(f"{mean[k].get(c, float('nan')):.4g}" for k in kinds) + " |")
+    lines += ["", "Derived:", ""]
+    for k in kinds:
+        m = mean[k]
+        d = sum(durs[k]) / len(durs[k]) / 1e3
+        short = names[k].replace("mi355gemm::(anonymous namespace)::", "").split("(")[0]
+        parts = [f"- {k} (`{short}`, "
+                 f"{d:.1f} us per profiled launch):"]
+        if m.get("SQ_INSTS_MFMA"):
+            parts.append(f"{m['SQ_VALU_MFMA_BUSY_CYCLES'] / m['SQ_INSTS_MFMA']:.1f} matrix-core cycles "
+                         f"per MFMA instruction, {m['SQ_INSTS_MFMA']:.4g} MFMA instructions;")
+        if m.get("SQ_LDS_IDX_ACTIVE"):
+            parts.append(f"LDS bank conflicts {100 * m.get('SQ_LDS_BANK_CONFLICT', 0) / m['SQ_LDS_IDX_ACTIVE']:.2f}% "
+                         f"of LDS-active cycles;")
+        if m.get("SQ_INSTS_MFMA") and m.get("SQ_INSTS_VALU") is not None:
+            parts.append(f"{m['SQ_INSTS_VALU'] / m['SQ_INSTS_MFMA']:.2f} VALU instructions (MFMA included) "
+                         f"per MFMA.")
+        lines.append(" ".join(parts))
+    path = os.path.join(ROOT, "profiles", "counters_sgemm4096x4096x1024_hgemm4096cube.md")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(path)
     return 0
 
 
