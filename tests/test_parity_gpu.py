@@ -486,3 +486,46 @@ def test_random_sweep(case):
                   kind_vals="int4" if c["ints"] else "pm1", exact=c["ints"],
                   lda=a_cols + c["pa"], ldb=b_cols + c["pb"], ldc=c["N"] + c["pc"],
                   transA=c["tA"], transB=c["tB"], seed=c["seed"], c_nan=(c["beta"] == 0.0))
+
+
+# ------------------------------------------------------------------ graph capture
+def test_graph_capture_replays_match_eager():
+    # the library enqueues plain kernel launches on the caller's stream (no memset,
+    # no allocation), so a captured sequence replays exactly; every replay is
+    # checked, with eager work and synchronisation between replays
+    note("graph capture of gemm_f32 + gemm_f16_f32acc + batched, 4 replays")
+    ps = si.gemm_problem(1001, 777, 513, seed=71)
+    ph = si.gemm_problem(512, 384, 320, in_dtype=np.float16, seed=72)
+    sA, sB, hA, hB = to_dev(ps["A"]), to_dev(ps["B"]), to_dev(ph["A"]), to_dev(ph["B"])
+    bA = to_dev(si.draw(73, 3 * 64 * 96).astype(np.float16))
+    bB = to_dev(si.draw(74, 3 * 96 * 80).astype(np.float16))
+    sC0, hC0 = to_dev(ps["C"]), to_dev(ph["C"])
+    bC0 = to_dev(si.draw(75, 3 * 64 * 80))
+
+    def work(sC, hC, bC, stream=None):
+        dg.gemm_f32(1001, 777, 513, 1.5, sA, 513, sB, 777, -0.5, sC, 777, stream)
+        dg.gemm_f16_f32acc(512, 384, 320, 1.0, hA, 320, hB, 384, 1.0, hC, 384, stream)
+        dg.gemm_batched_f16_f32acc(64, 80, 96, 1.0, bA, 96, 64 * 96, bB, 80, 96 * 80, 0.5, bC, 80, 64 * 80, 3,
+                                   stream)
+
+    eager = [sC0.clone(), hC0.clone(), bC0.clone()]
+    work(*eager)
+    torch.cuda.synchronize()
+
+    outs = [torch.empty_like(sC0), torch.empty_like(hC0), torch.empty_like(bC0)]
+    for o, c0 in zip(outs, (sC0, hC0, bC0)):
+        o.copy_(c0)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    with torch.cuda.graph(g, stream=side):
+        work(*outs, stream=side)
+    for replay in range(4):
+        for o, c0 in zip(outs, (sC0, hC0, bC0)):
+            o.copy_(c0)        # beta != 0: every replay starts from the same C
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for o, e in zip(outs, eager):
+            assert torch.equal(o, e), f"replay {replay} differs from the eager result"
+        _ = (sA * 2).sum().item()   # unrelated eager work between replays
