@@ -14,6 +14,9 @@ benchmark configurations (SGEMM 512^3, the 1001x777x513 and 1024x1024x512
 SGEMMs, HGEMM 2048^3 and 16 batched 1024^3 HGEMMs with beta = 1) are timed
 after the main run and reported under "extra" (not part of the value).
 
+Warm-up: under this load the clocks take about 40 ms (about 100 steps) to
+settle; the default 200 untimed steps cover that, and 50 steps are timed.
+
 Prints exactly one JSON line.
 """
 from __future__ import annotations
@@ -80,8 +83,10 @@ def measured_traffic(kind: str, workload: str):
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    # the chip's clocks settle only after some tens of milliseconds of this load
+    # (about 100 steps); the warm-up covers that so the timed steps are steady
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--no-extra", action="store_true", help="skip the other configurations")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU-oracle time budget")
@@ -90,6 +95,9 @@ def main() -> int:
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn two rocprofv3 counter_collection.csv files (FETCH_SIZE, WRITE_SIZE) of a "
                          "--copy-calibration run into profiles/hbm_traffic.md; uses no GPU")
+    ap.add_argument("--write-trace", nargs=3, metavar=("STATS_CSV", "TRACE_CSV", "BENCH_LOG"),
+                    help="turn a rocprofv3 --kernel-trace --stats run of this script into "
+                         "profiles/kernel_trace_sgemm4096x4096x1024_hgemm4096cube.md; uses no GPU")
     ap.add_argument("--write-counters", nargs="+", metavar="CSV",
                     help="turn rocprofv3 counter_collection.csv files of the step's kernels into "
                          "profiles/counters_sgemm4096x4096x1024_hgemm4096cube.md; uses no GPU")
@@ -98,6 +106,8 @@ def main() -> int:
         return write_traffic(*args.write_traffic)
     if args.write_counters:
         return write_counters(args.write_counters)
+    if args.write_trace:
+        return write_trace(*args.write_trace)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: this library has no multi-GPU path "
@@ -219,6 +229,57 @@ def main() -> int:
         "extra": extra,
     }
     print(json.dumps(line), flush=True)
+    return 0
+
+
+TRACE_STEPS, TRACE_WARMUP = 50, 200
+
+
+def write_trace(stats_csv: str, trace_csv: str, bench_log: str) -> int:
+    """Kernel-trace summary of a profiled run of this script: rocprofv3's statistics over
+    all launches, the same over the timed launches only (the last TRACE_STEPS of each
+    kernel), and the bench line's own HIP-event averages for comparison."""
+    import csv
+
+    def short(n):
+        return n.replace("mi355gemm::(anonymous namespace)::", "").split("(")[0]
+
+    stats = list(csv.DictReader(open(stats_csv)))
+    per = {}
+    for r in csv.DictReader(open(trace_csv)):
+        per.setdefault(r["Kernel_Name"], []).append(
+            (int(r["Start_Timestamp"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+    line = next(l for l in open(bench_log) if l.startswith('{"metric"'))
+    bench_line = json.loads(line)
+    cmd = (f"cd /tmp && rocprofv3 --kernel-trace --stats --output-format csv -d $R/gpurun_out/prof -o run -- "
+           f"python3 $R/bench.py --no-cpu --no-extra --steps {TRACE_STEPS} --warmup {TRACE_WARMUP} "
+           f"> $R/gpurun_out/prof.log\n"
+           f"python3 $R/bench.py --write-trace $R/gpurun_out/prof/run_kernel_stats.csv "
+           f"$R/gpurun_out/prof/run_kernel_trace.csv $R/gpurun_out/prof.log   # R = repository root")
+    out = ["# rocprofv3 kernel trace: bench step (SGEMM 4096x4096x1024 fp32 + HGEMM 4096^3 fp16->fp32)", "",
+           "Commands (run on one MI355X):", "", "```", cmd, "```", "",
+           "All launches (warm-up included):", "",
+           "| kernel | calls | average (us) | min (us) | max (us) | share |", "|---|---|---|---|---|---|"]
+    for r in stats:
+        out.append(f"| `{short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                   f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.1f}% |")
+    out += ["", f"Timed launches only (the last {TRACE_STEPS} of each kernel), beside the bench line's "
+                "HIP-event averages over the same steps:", "",
+            "| kernel | launches | rocprofv3 average (us) | bench average (us) |", "|---|---|---|---|"]
+    for name, v in per.items():
+        kind = "sgemm" if "sgemm" in name else "hgemm" if "hgemm" in name else None
+        if kind is None:
+            continue
+        v.sort()
+        tail = [d for _, d in v[-TRACE_STEPS:]]
+        out.append(f"| `{short(name)}` | {len(tail)} | {sum(tail) / len(tail) / 1e3:.1f} | "
+                   f"{bench_line['per_kernel'][kind]['avg_ms'] * 1e3:.1f} |")
+    out += ["", "The bench averages include the gap between an event and its kernel; rocprofv3 times "
+                "the kernel alone. Both kernels are the NN (no transpose) instantiations."]
+    path = os.path.join(ROOT, "profiles", "kernel_trace_sgemm4096x4096x1024_hgemm4096cube.md")
+    with open(path, "w") as f:
+        f.write("\n".join(out) + "\n")
+    print(path)
     return 0
 
 
