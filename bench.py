@@ -411,7 +411,7 @@ def write_traffic(fetch_csv: str, write_csv: str) -> int:
     return 0
 
 
-def time_calls(fn, torch, stream, warmup=3, reps=20):
+def time_calls(fn, torch, stream, warmup=20, reps=30):
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
