@@ -288,6 +288,7 @@ COUNTER_PASSES = (
     "SQ_INSTS_VALU SQ_INSTS_VMEM_RD SQ_INSTS_VMEM_WR GRBM_GUI_ACTIVE",
     "SQ_WAVES SQ_WAVE_CYCLES SQ_BUSY_CYCLES SQ_WAIT_INST_ANY SQ_WAIT_ANY SQ_WAIT_INST_LDS "
     "SQ_ACTIVE_INST_LDS SQ_LDS_ADDR_CONFLICT GRBM_GUI_ACTIVE",
+    "TCC_HIT_sum TCC_MISS_sum TCC_EA0_RDREQ_DRAM_sum TCC_EA0_WRREQ_DRAM_sum",
 )
 
 
@@ -315,8 +316,9 @@ def write_counters(csv_paths) -> int:
     cmds = "\n".join(
         f"cd /tmp && rocprofv3 --pmc {p} --output-format csv -d $R/gpurun_out/counters{i} -o c -- "
         f"python3 $R/bench.py --no-cpu --no-extra --steps 3 --warmup 1" for i, p in enumerate(COUNTER_PASSES, 1))
-    cmds += ("\npython3 $R/bench.py --write-counters $R/gpurun_out/counters1/c_counter_collection.csv "
-             "$R/gpurun_out/counters2/c_counter_collection.csv   # R = repository root")
+    cmds += ("\npython3 $R/bench.py --write-counters " +
+             " ".join(f"$R/gpurun_out/counters{i}/c_counter_collection.csv" for i in range(1, len(COUNTER_PASSES) + 1)) +
+             "   # R = repository root")
     lines = ["# rocprofv3 counters per launch: bench step kernels (SGEMM 4096x4096x1024 fp32, "
              "HGEMM 4096^3 fp16->fp32)", "",
              "Commands (one MI355X; each pass is a run of its own):", "", "```", cmds, "```", "",
@@ -338,6 +340,8 @@ def write_counters(csv_paths) -> int:
         if m.get("SQ_LDS_IDX_ACTIVE"):
             parts.append(f"LDS bank conflicts {100 * m.get('SQ_LDS_BANK_CONFLICT', 0) / m['SQ_LDS_IDX_ACTIVE']:.2f}% "
                          f"of LDS-active cycles;")
+        if m.get("TCC_HIT_sum") is not None and m.get("TCC_MISS_sum"):
+            parts.append(f"L2 hit rate {100 * m['TCC_HIT_sum'] / (m['TCC_HIT_sum'] + m['TCC_MISS_sum']):.1f}%;")
         if m.get("SQ_INSTS_MFMA") and m.get("SQ_INSTS_VALU") is not None:
             parts.append(f"{m['SQ_INSTS_VALU'] / m['SQ_INSTS_MFMA']:.2f} VALU instructions (MFMA included) "
                          f"per MFMA.")
@@ -483,6 +487,25 @@ def run_extra(dg, si, np, torch, dev, stream):
         "median_ms": med * 1e3, "tflops": fl / med / 1e12, "frac_of_peak": fl / med / 1e12 / PEAK_F16_TFLOPS,
         "hbm_roofline_tflops": min(PEAK_F16_TFLOPS, fl / bytes_alg * PEAK_HBM_GBS / 1e3),
         "warm_buffers": True}
+    # cold: three operand sets (384 MB, more than the 256 MB last-level cache) used in turn,
+    # so each call finds its inputs in HBM
+    sets = [(torch.empty(nb * n * n, dtype=torch.float16, device=dev).uniform_(-1, 1),
+             torch.empty(nb * n * n, dtype=torch.float16, device=dev).uniform_(-1, 1),
+             torch.empty(nb * n * n, dtype=torch.float32, device=dev).uniform_(-1, 1)) for _ in range(3)]
+    turn = [0]
+
+    def cold_call():
+        a, b, c = sets[turn[0] % 3]
+        turn[0] += 1
+        dg.gemm_batched_f16_f32acc(n, n, n, 1.0, a, n, n * n, b, n, n * n, 1.0, c, n, n * n, nb, stream)
+
+    med, _ = time_calls(cold_call, torch, stream)
+    out["batched_hgemm_16x1024^3_b1_cold"] = {
+        "median_ms": med * 1e3, "tflops": fl / med / 1e12, "frac_of_peak": fl / med / 1e12 / PEAK_F16_TFLOPS,
+        "hbm_roofline_tflops": min(PEAK_F16_TFLOPS, fl / bytes_alg * PEAK_HBM_GBS / 1e3),
+        "frac_of_hbm_roofline": fl / med / 1e12 / min(PEAK_F16_TFLOPS, fl / bytes_alg * PEAK_HBM_GBS / 1e3),
+        "warm_buffers": False, "operand_sets": 3}
+    del sets
     return out
 
 
@@ -509,9 +532,17 @@ def cpu_baseline(si, np, ps, ph, budget_s):
             rows_h += block
             flops += 2.0 * block * 4096 * 4096
     dt = time.perf_counter() - t0
+    # the same loop on one thread, over a short sample of SGEMM rows
+    t1 = time.perf_counter()
+    one_rows = 128
+    oracle.gemm_ref(4096, 4096, 1024, 1.0, ps["A"], 1024, ps["B"], 4096, 0.0, None, 4096,
+                    rows=np.arange(one_rows, dtype=np.int32), threads=1)
+    dt1 = time.perf_counter() - t1
     return {"value": flops / dt / 1e12, "unit": "TFLOPS", "cores": threads, "kind": "oracle",
             "sample": f"first {rows_s} rows of the SGEMM 4096x4096x1024 and first {rows_h} rows of the "
-                      f"HGEMM 4096^3 (fp64 triple loop), {dt:.1f} s"}
+                      f"HGEMM 4096^3 (fp64 triple loop), {dt:.1f} s",
+            "single_thread": {"value": 2.0 * one_rows * 4096 * 1024 / dt1 / 1e12, "unit": "TFLOPS",
+                              "sample": f"first {one_rows} rows of the SGEMM 4096x4096x1024, {dt1:.2f} s"}}
 
 
 if __name__ == "__main__":
