@@ -144,13 +144,13 @@ __global__ __launch_bounds__(256) void hgemm_mfma_kernel(HgemmArgs p)
     __shared__ __attribute__((aligned(16))) uint16_t lds[2 * BUF_HALVES];
 
     const int tid = threadIdx.x;
-    int tm, tn;
-    tile_coords(blockIdx.x, p.tiles_m, p.tiles_n, &tm, &tn);
+    int mb, tm, tn;   // batch member, tile row, tile column
+    tile_coords(blockIdx.x, blockIdx.z, gridDim.z, p.tiles_m, p.tiles_n, &mb, &tm, &tn);
     const long long m0 = (long long)tm * BM, n0 = (long long)tn * BN;
     const int M = p.M, N = p.N, K = p.K;
-    const uint16_t *A = p.A + (long long)blockIdx.z * p.sA;
-    const uint16_t *B = p.B + (long long)blockIdx.z * p.sB;
-    float *C = p.C + (long long)blockIdx.z * p.sC;
+    const uint16_t *A = p.A + (long long)mb * p.sA;
+    const uint16_t *B = p.B + (long long)mb * p.sB;
+    float *C = p.C + (long long)mb * p.sC;
     const long long lda = p.lda, ldb = p.ldb, ldc = p.ldc;
 
     u32x4 ra[TileA::LOADS], rb[TileB::LOADS];
@@ -435,17 +435,17 @@ __global__ __launch_bounds__(Cfg::NT) void hgemm_dma_kernel(HgemmArgs p)
     const unsigned lds0 = (unsigned)(uintptr_t)lds;
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    int tm, tn;
-    tile_coords(blockIdx.x, p.tiles_m, p.tiles_n, &tm, &tn);
+    int mb, tm, tn;   // batch member, tile row, tile column
+    tile_coords(blockIdx.x, blockIdx.z, gridDim.z, p.tiles_m, p.tiles_n, &mb, &tm, &tn);
     const long long m0 = (long long)tm * BM, n0 = (long long)tn * BN;
     const long long lda = p.lda, ldb = p.ldb, ldc = p.ldc;
     // first element of the tile's slice 0 in each operand, and the bytes
     // between consecutive slices
-    const char *Ab = reinterpret_cast<const char *>(p.A + (long long)blockIdx.z * p.sA + (A_KC ? m0 * lda : m0));
-    const char *Bb = reinterpret_cast<const char *>(p.B + (long long)blockIdx.z * p.sB + (B_KC ? n0 * ldb : n0));
+    const char *Ab = reinterpret_cast<const char *>(p.A + (long long)mb * p.sA + (A_KC ? m0 * lda : m0));
+    const char *Bb = reinterpret_cast<const char *>(p.B + (long long)mb * p.sB + (B_KC ? n0 * ldb : n0));
     const long long stepA = A_KC ? BK * 2 : BK * lda * 2;
     const long long stepB = B_KC ? BK * 2 : BK * ldb * 2;
-    float *C = p.C + (long long)blockIdx.z * p.sC;
+    float *C = p.C + (long long)mb * p.sC;
 
     // Loading waves are NW-LW .. NW-1; loader index lw numbers their 1 KB
     // pieces of each slice.

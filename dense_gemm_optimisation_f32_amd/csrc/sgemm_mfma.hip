@@ -111,13 +111,13 @@ __global__ __launch_bounds__(Cfg::NT) void sgemm_mfma_kernel(SgemmArgs p)
     __shared__ __attribute__((aligned(16))) float lds_b[2 * BK * LDB_S];
 
     const int tid = threadIdx.x;
-    int tm, tn;
-    tile_coords(blockIdx.x, p.tiles_m, p.tiles_n, &tm, &tn);
+    int mb, tm, tn;   // batch member, tile row, tile column
+    tile_coords(blockIdx.x, blockIdx.z, gridDim.z, p.tiles_m, p.tiles_n, &mb, &tm, &tn);
     const long long m0 = (long long)tm * BM, n0 = (long long)tn * BN;
     const int M = p.M, N = p.N, K = p.K;
-    const float *A = p.A + (long long)blockIdx.z * p.sA;
-    const float *B = p.B + (long long)blockIdx.z * p.sB;
-    float *C = p.C + (long long)blockIdx.z * p.sC;
+    const float *A = p.A + (long long)mb * p.sA;
+    const float *B = p.B + (long long)mb * p.sB;
+    float *C = p.C + (long long)mb * p.sC;
     const long long lda = p.lda, ldb = p.ldb, ldc = p.ldc;
 
     f32x4_t ra[Cfg::A_LOADS], rb[Cfg::B_LOADS];
@@ -317,14 +317,14 @@ __global__ __launch_bounds__(Cfg::NT) void sgemm_dma_kernel(SgemmArgs p)
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int uwave = __builtin_amdgcn_readfirstlane(wave);
-    int tm, tn;
-    tile_coords(blockIdx.x, p.tiles_m, p.tiles_n, &tm, &tn);
+    int mb, tm, tn;   // batch member, tile row, tile column
+    tile_coords(blockIdx.x, blockIdx.z, gridDim.z, p.tiles_m, p.tiles_n, &mb, &tm, &tn);
     const long long m0 = (long long)tm * BM, n0 = (long long)tn * BN;
     const long long lda = p.lda, ldb = p.ldb, ldc = p.ldc;
     // first element of the tile's slice 0 in each operand
-    const char *Ab = reinterpret_cast<const char *>(p.A + (long long)blockIdx.z * p.sA + (A_KC ? m0 * lda : m0));
-    const char *Bb = reinterpret_cast<const char *>(p.B + (long long)blockIdx.z * p.sB + (B_KC ? n0 * ldb : n0));
-    float *C = p.C + (long long)blockIdx.z * p.sC;
+    const char *Ab = reinterpret_cast<const char *>(p.A + (long long)mb * p.sA + (A_KC ? m0 * lda : m0));
+    const char *Bb = reinterpret_cast<const char *>(p.B + (long long)mb * p.sB + (B_KC ? n0 * ldb : n0));
+    float *C = p.C + (long long)mb * p.sC;
     // bytes between consecutive slices
     const long long stepA = A_KC ? BK * 4 : BK * lda * 4;
     const long long stepB = B_KC ? BK * 4 : BK * ldb * 4;
@@ -582,13 +582,13 @@ __global__ __launch_bounds__(Cfg::NT) void sgemm_small_kernel(SgemmArgs p)
 
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
     const int lr = lane & 31, lk = lane >> 5;
-    int tm, tn;
-    tile_coords(blockIdx.x, p.tiles_m, p.tiles_n, &tm, &tn);
+    int mb, tm, tn;   // batch member, tile row, tile column
+    tile_coords(blockIdx.x, blockIdx.z, gridDim.z, p.tiles_m, p.tiles_n, &mb, &tm, &tn);
     const long long m0 = (long long)tm * Cfg::TM, n0 = (long long)tn * Cfg::TN;
     const int M = p.M, N = p.N, K = p.K;
-    const float *A = p.A + (long long)blockIdx.z * p.sA;
-    const float *B = p.B + (long long)blockIdx.z * p.sB;
-    float *C = p.C + (long long)blockIdx.z * p.sC;
+    const float *A = p.A + (long long)mb * p.sA;
+    const float *B = p.B + (long long)mb * p.sB;
+    float *C = p.C + (long long)mb * p.sC;
     const long long lda = p.lda, ldb = p.ldb, ldc = p.ldc;
 
     // this wave's k range

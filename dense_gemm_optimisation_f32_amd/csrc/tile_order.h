@@ -16,19 +16,32 @@ namespace mi355gemm {
 constexpr int kNumXcd = 8;
 constexpr int kGroupM = 4;
 
-__host__ __device__ inline void tile_coords(int wg, int tiles_m, int tiles_n, int *tm, int *tn)
+// wg: blockIdx.x within one batch member's tiles; z: blockIdx.z (the batch
+// member index within the launch), nbatch: gridDim.z.  The dispatcher numbers
+// workgroups x-fastest, so the linear id is z*tiles + wg; the XCD-contiguous
+// remap runs over all nbatch*tiles workgroups of the launch, which gives each
+// XCD whole batch members when tiles*nbatch is a multiple of 8 and tiles is
+// small (their A and B then pass through one L2), and reduces to the
+// single-problem order when nbatch == 1.  Outputs: the batch member and the
+// tile of it.  A bijection onto [0, nbatch) x [0, tiles_m) x [0, tiles_n).
+__host__ __device__ inline void tile_coords(int wg, int z, int nbatch, int tiles_m, int tiles_n, int *member,
+                                            int *tm, int *tn)
 {
-    const int total = tiles_m * tiles_n;
+    const long long tiles = (long long)tiles_m * tiles_n;
+    const long long total = tiles * nbatch;
+    const long long lin = (long long)z * tiles + wg;
     // XCD-contiguous logical index
-    const int xcd = wg % kNumXcd, slot = wg / kNumXcd;
-    const int per = total / kNumXcd, extra = total % kNumXcd;
-    const int logical = xcd * per + (xcd < extra ? xcd : extra) + slot;
+    const long long xcd = lin % kNumXcd, slot = lin / kNumXcd;
+    const long long per = total / kNumXcd, extra = total % kNumXcd;
+    const long long logical = xcd * per + (xcd < extra ? xcd : extra) + slot;
+    *member = (int)(logical / tiles);
+    const int t = (int)(logical - (long long)(*member) * tiles);
     // grouped order: GROUP_M tile rows at a time, column-major inside a group
     const int per_group = kGroupM * tiles_n;
-    const int group = logical / per_group;
+    const int group = t / per_group;
     const int first_m = group * kGroupM;
     const int rows = (tiles_m - first_m) < kGroupM ? (tiles_m - first_m) : kGroupM;
-    const int in_group = logical - group * per_group;
+    const int in_group = t - group * per_group;
     *tm = first_m + in_group % rows;
     *tn = in_group / rows;
 }

@@ -1,7 +1,8 @@
 """Host check of the workgroup-to-tile mapping (csrc/tile_order.h): for every grid
-shape up to 40 x 40 tiles, the map from workgroup id to (tile row, tile column)
-is a bijection onto the tile grid, and with whole groups the tiles one XCD runs
-form compact blocks of C."""
+shape up to 24 x 24 tiles and up to 5 batch members, the map from (workgroup,
+member) ids to (member, tile row, tile column) is a bijection, with whole groups
+the tiles one XCD runs form compact blocks of C, and a batch of small problems
+gives each XCD whole members."""
 import os
 import subprocess
 
@@ -13,27 +14,44 @@ PROG = r"""
 #include <vector>
 #include "tile_order.h"
 int main() {
-    for (int tm_n = 1; tm_n <= 40; ++tm_n)
-        for (int tn_n = 1; tn_n <= 40; ++tn_n) {
-            std::vector<int> seen(tm_n * tn_n, 0);
-            for (int w = 0; w < tm_n * tn_n; ++w) {
-                int tm, tn;
-                mi355gemm::tile_coords(w, tm_n, tn_n, &tm, &tn);
-                if (tm < 0 || tm >= tm_n || tn < 0 || tn >= tn_n) { std::printf("range %d %d %d\n", tm_n, tn_n, w); return 1; }
-                if (seen[tm * tn_n + tn]++) { std::printf("dup %d %d %d\n", tm_n, tn_n, w); return 1; }
+    // bijection onto (member, tile row, tile column) for grids up to 24 x 24 tiles and 1..5 members
+    for (int nb = 1; nb <= 5; ++nb)
+        for (int tm_n = 1; tm_n <= 24; ++tm_n)
+            for (int tn_n = 1; tn_n <= 24; ++tn_n) {
+                std::vector<int> seen(nb * tm_n * tn_n, 0);
+                for (int z = 0; z < nb; ++z)
+                    for (int w = 0; w < tm_n * tn_n; ++w) {
+                        int mb, tm, tn;
+                        mi355gemm::tile_coords(w, z, nb, tm_n, tn_n, &mb, &tm, &tn);
+                        if (mb < 0 || mb >= nb || tm < 0 || tm >= tm_n || tn < 0 || tn >= tn_n) {
+                            std::printf("range %d %d %d %d %d\n", nb, tm_n, tn_n, z, w); return 1; }
+                        if (seen[(mb * tm_n + tm) * tn_n + tn]++) {
+                            std::printf("dup %d %d %d %d %d\n", nb, tm_n, tn_n, z, w); return 1; }
+                    }
             }
-        }
-    // 16 x 16 tiles (HGEMM 4096^2 with 256^2 tiles): XCD x runs ids x, x+8, ...; they must
-    // cover exactly 4 tile rows and 8 tile columns.
+    // one member, 16 x 16 tiles (HGEMM 4096^2 with 256^2 tiles): XCD x runs linear ids x, x+8,
+    // ...; they must cover exactly 4 tile rows and 8 tile columns.
     for (int x = 0; x < 8; ++x) {
         int rows[16] = {0}, cols[16] = {0}, nr = 0, nc = 0;
         for (int w = x; w < 256; w += 8) {
-            int tm, tn;
-            mi355gemm::tile_coords(w, 16, 16, &tm, &tn);
+            int mb, tm, tn;
+            mi355gemm::tile_coords(w, 0, 1, 16, 16, &mb, &tm, &tn);
             if (!rows[tm]++) ++nr;
             if (!cols[tn]++) ++nc;
         }
         if (nr != 4 || nc != 8) { std::printf("xcd %d spans %d rows %d cols\n", x, nr, nc); return 1; }
+    }
+    // 16 members of 4 x 4 tiles (batched 1024^2 with 256^2 tiles): each XCD runs two whole members
+    for (int x = 0; x < 8; ++x) {
+        int count[16] = {0}, members = 0;
+        for (int lin = x; lin < 256; lin += 8) {
+            int mb, tm, tn;
+            mi355gemm::tile_coords(lin % 16, lin / 16, 16, 4, 4, &mb, &tm, &tn);
+            if (!count[mb]++) ++members;
+        }
+        for (int m = 0; m < 16; ++m)
+            if (count[m] != 0 && count[m] != 16) { std::printf("xcd %d has part of member %d\n", x, m); return 1; }
+        if (members != 2) { std::printf("xcd %d runs %d members\n", x, members); return 1; }
     }
     std::printf("ok\n");
     return 0;
