@@ -426,10 +426,10 @@ __global__ __launch_bounds__(Cfg::NT) void sgemm_dma_kernel(SgemmArgs p)
     // Issue the LDS reads of the next step one after each of this step's first
     // MFMAs, so they have the rest of the step to land.
     constexpr int READS = Cfg::FM * (A_KC ? 1 : 4) + Cfg::FN * (B_KC ? 1 : 4);
-    static_assert(READS <= 4 * Cfg::FM * Cfg::FN, "more reads than MFMAs per step");
+    constexpr int PAIRS = READS < 4 * Cfg::FM * Cfg::FN ? READS : 4 * Cfg::FM * Cfg::FN;
     auto interleave = [&]() {
 #pragma unroll
-        for (int r = 0; r < READS; ++r) {
+        for (int r = 0; r < PAIRS; ++r) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
         }
@@ -509,10 +509,13 @@ __global__ __launch_bounds__(Cfg::NT) void sgemm_dma_kernel(SgemmArgs p)
         epilogue(std::false_type{});
 }
 
-// 256x256 tiles with eight waves (2 x 4 of 128x64, two per SIMD: one wave's
-// MFMAs cover the other's LDS and barrier latency); 128x128 tiles with four.
+// Eight waves, two per SIMD (one wave's MFMAs cover the other's LDS and barrier
+// latency): 256x256 tiles as 2 x 4 waves of 128x64, 128x128 tiles as 2 x 4 of
+// 64x32.  64x64 tiles (four waves of 32x32) serve grids that 128x128 tiles
+// would leave under-filled.
 using SgDma256 = SgDmaCfg<256, 256, 2, 4>;
-using SgDma128 = SgDmaCfg<128, 128, 2, 2>;
+using SgDma128 = SgDmaCfg<128, 128, 2, 4>;
+using SgDma64 = SgDmaCfg<64, 64, 2, 2>;
 
 template <class Cfg>
 bool sg_dma_ok(const GemmProblem &q)
@@ -770,6 +773,8 @@ hipError_t launch_sgemm(const GemmProblem &q, hipStream_t stream)
     // everything else.
     const long long t256 = (long long)(q.M / 256) * (q.N / 256) * q.batch;
     const long long t128 = (long long)((q.M + 127) / 128) * ((q.N + 127) / 128) * q.batch;
+    const long long t64w = (long long)(q.M / 64) * (q.N / 64) * q.batch;   // whole 64x64 tiles
+    if (t128 < 256 && t64w >= 256 && sg_dma_ok<SgDma64>(q)) return launch_sg_dma<SgDma64>(q, stream);
     if (t128 < 256) {
         // fewer 128x128 tiles than CUs: split K inside smaller workgroup tiles
         const long long t64 = (long long)((q.M + 63) / 64) * ((q.N + 63) / 64) * q.batch;

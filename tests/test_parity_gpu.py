@@ -353,6 +353,18 @@ def test_transposed_fast_paths(kind, tA, tB):
                   seed=19)
 
 
+@pytest.mark.parametrize("tA,tB", [(False, False)] + OPS)
+def test_sgemm_64_tiles_direct_to_lds(tA, tB):
+    # fewer than 256 tiles of 128x128 but at least 256 whole 64x64 tiles: the
+    # four-wave 64x64 direct-to-LDS kernel (K = 64 is its shortest ring)
+    for M, N, K in [(1024, 1024, 64), (1024, 2048, 416)]:
+        a_cols, b_cols = (M if tA else K), (K if tB else N)
+        run_and_check("f32", M, N, K, 1.5, -0.5, lda=a_cols + 4, ldb=b_cols + 12, ldc=N + 3, sample=128,
+                      transA=tA, transB=tB)
+        run_and_check("f32", M, N, K, 1.0, 1.0, sample=64, kind_vals="int4", exact=True, transA=tA, transB=tB,
+                      seed=23)
+
+
 @pytest.mark.parametrize("tA,tB", OPS)
 def test_transposed_hgemm_register_whole_tiles(tA, tB):
     # whole 128x128 tiles but K too short for the direct-to-LDS ring: unmasked register kernel
