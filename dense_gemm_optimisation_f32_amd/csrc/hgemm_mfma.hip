@@ -333,11 +333,17 @@ struct HgDmaCfg {
     static constexpr int A_BYTES = BM * BK * 2;                 // one A slice
     static constexpr int B_BYTES = BK * BN * 2;                 // one B slice
     static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
-    // The upper half of the waves (one per SIMD) issues every direct-to-LDS
-    // load: a 1 KB load occupies the CU's vector-memory path for about 16
-    // cycles, and a wave blocked on issuing them cannot issue MFMAs, so the
-    // other wave on each SIMD is left free to keep the matrix core busy.
-    static constexpr int LW = NW / 2;                           // loading waves
+    // A 1 KB direct-to-LDS load occupies the CU's vector-memory path for about
+    // 16 cycles, and a wave blocked on issuing loads cannot issue MFMAs.  With
+    // a two-slot ring the upper half of the waves (one per SIMD) issues every
+    // load, right after the barrier that frees a slot, and the other wave on
+    // each SIMD keeps the matrix core busy meanwhile.  With three or more
+    // slots (STAGGER) every wave loads a share: the lower half right after the
+    // barrier, the upper half two substeps before the next one, into the slot
+    // that the previous barrier freed, so the two waves of a SIMD block on
+    // their loads at different times.
+    static constexpr bool STAGGER = STAGES >= 3;
+    static constexpr int LW = STAGGER ? NW : NW / 2;            // loading waves
     static constexpr int A_LOADS = A_BYTES / 1024 / LW;         // per loading wave per slice
     static constexpr int B_LOADS = B_BYTES / 1024 / LW;
     static_assert(A_BYTES % (1024 * LW) == 0 && B_BYTES % (1024 * LW) == 0, "slices must split over the loaders");
@@ -548,18 +554,24 @@ __global__ __launch_bounds__(Cfg::NT) void hgemm_dma_kernel(HgemmArgs p)
     // outstanding slices, then the barrier) and every wave holds its slice-t
     // fragments, slot t % S is refilled with slice t+S and the first fragments
     // of slice t+1 are read while the last substep of slice t is computed.
-    auto step = [&](int t, auto pending, auto refill) {
+    // Staggered refills: the upper half of the waves loads its share of slice
+    // t-1+S during substep NS-2 of step t (t >= 1).  The count of outstanding
+    // slices at each wait is the same for both halves.
+    const bool late = Cfg::STAGGER && uwave >= Cfg::NW / 2;
+    static_assert(!Cfg::STAGGER || NS >= 2, "staggered refills need two substeps per slice");
+    auto step = [&](int t, auto pending, auto refill, bool late_refill) {
         const int slot = t % S;
 #pragma unroll
         for (int sub = 0; sub < NS; ++sub) {
             const int cur = sub & 1, nxt = cur ^ 1;
             if (sub + 1 < NS) {
                 read_frags(slot, sub + 1, fa[nxt], fb[nxt]);
+                if (Cfg::STAGGER && sub == NS - 2 && late && late_refill) issue_slice(t - 1 + S, (t - 1 + S) % S);
             } else {
                 wait_vmcnt<LOADS * decltype(pending)::value>();
                 __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's slice-t reads are done
                 lds_barrier();
-                if (decltype(refill)::value) issue_slice(t + S, slot);
+                if (decltype(refill)::value && !late) issue_slice(t + S, slot);
                 read_frags((t + 1) % S, 0, fa[nxt], fb[nxt]);
             }
             mfmas(fa[cur], fb[cur]);
@@ -576,16 +588,16 @@ __global__ __launch_bounds__(Cfg::NT) void hgemm_dma_kernel(HgemmArgs p)
     read_frags(0, 0, fa[0], fb[0]);
 
     // Steady state: slices up to t+S-1 issued, slice t+1 needed.
-    for (int t = 0; t + S < nk; ++t) step(t, std::integral_constant<int, S - 2>{}, std::true_type{});
+    for (int t = 0; t + S < nk; ++t) step(t, std::integral_constant<int, S - 2>{}, std::true_type{}, t >= 1);
     // Tail: no more slices to issue; the outstanding count drains to zero.
     const int t0 = nk - S;
     if constexpr (S == 4) {
-        step(t0 + 0, std::integral_constant<int, 2>{}, std::false_type{});
-        step(t0 + 1, std::integral_constant<int, 1>{}, std::false_type{});
-        step(t0 + 2, std::integral_constant<int, 0>{}, std::false_type{});
+        step(t0 + 0, std::integral_constant<int, 2>{}, std::false_type{}, t0 >= 1);
+        step(t0 + 1, std::integral_constant<int, 1>{}, std::false_type{}, false);
+        step(t0 + 2, std::integral_constant<int, 0>{}, std::false_type{}, false);
     } else {
         static_assert(S == 2, "ring of two or four slices");
-        step(t0 + 0, std::integral_constant<int, 0>{}, std::false_type{});
+        step(t0 + 0, std::integral_constant<int, 0>{}, std::false_type{}, false);
     }
     {   // last slice: everything is resident
         const int slot = (nk - 1) % S;

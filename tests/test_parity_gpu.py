@@ -202,6 +202,15 @@ def test_small_problem_split_k(M, N, K):
     run_and_check("f32", M, N, K, 1.0, 1.0, kind_vals="int4", exact=True, seed=11)
 
 
+@pytest.mark.parametrize("K", [256, 320, 384, 512, 1024])
+def test_hgemm_128_ring_lengths(K):
+    # 128x128 direct-to-LDS HGEMM, four-slice ring with staggered refills: K/64 slices
+    # from exactly the ring (no refill) through the tail-only refill to a steady loop
+    run_and_check("f16", 256, 384, K, 1.5, -0.5)
+    run_and_check("f16", 256, 384, K, 1.0, 1.0, kind_vals="int4", exact=True, seed=29)
+    run_and_check("f16", 384, 256, K, 1.0, 0.0, kind_vals="int4", exact=True, seed=31, transA=True, transB=True)
+
+
 def test_batched_whole_tiles_mid_size():
     # 128x128 whole tiles with K a multiple of 64 (the mid-size direct-to-LDS path), 3 members
     batched_check(384, 256, 320, 3, 1.5, -0.5)
