@@ -293,21 +293,31 @@ typedef __attribute__((address_space(3))) float lds_f32;
 
 // Per-lane byte offset (within one slice of global memory) of the 16-byte
 // chunk that lane `lane` of wave load g fetches for an operand slice of R rows
-// or columns; see the layouts above.
-template <bool KC, int R>
-__device__ __forceinline__ unsigned sg_dma_offset(int g, int lane, long long ld)
+// or columns; see the layouts above.  `lim` is how many of the R rows
+// (K-contiguous) or columns (MN-contiguous) lie inside M or N: a chunk past
+// it re-reads a valid one (row lim-1, or chunk 0 of its row), whose products
+// only reach C entries that are never stored.
+template <bool KC, int R, bool CLAMP>
+__device__ __forceinline__ unsigned sg_dma_offset(int g, int lane, long long ld, int lim)
 {
     if (KC) {
         const int r = 8 * g + (lane >> 3);
-        return (unsigned)(r * ld + 4 * ((lane & 7) ^ sg_swz_a(r))) * 4u;
+        const int rr = (CLAMP && r >= lim) ? lim - 1 : r;
+        return (unsigned)(rr * ld + 4 * ((lane & 7) ^ sg_swz_a(r))) * 4u;
     }
     constexpr int CPR = R / 4, RPL = 256 / R;   // chunks per row, rows per wave load
     const int k = RPL * g + lane / CPR;
-    return (unsigned)(k * ld + 4 * ((lane % CPR) ^ sg_swz_b(k))) * 4u;
+    int ch = (lane % CPR) ^ sg_swz_b(k);
+    if (CLAMP && 4 * ch >= lim) ch = 0;
+    return (unsigned)(k * ld + 4 * ch) * 4u;
 }
 
-// TA: A stored K x M; TB: B stored N x K.
-template <class Cfg, bool TA, bool TB>
+// TA: A stored K x M; TB: B stored N x K.  MASK: M and N need not be
+// multiples of the tile, nor K of BK (the loads clamp to valid rows and
+// columns, the K % BK tail is read straight from global memory after the last
+// slice, and stores outside C are skipped); an MN-contiguous operand then
+// needs its M or N to be a multiple of four, so no 16-byte chunk straddles it.
+template <class Cfg, bool TA, bool TB, bool MASK>
 __global__ __launch_bounds__(Cfg::NT) void sgemm_dma_kernel(SgemmArgs p)
 {
     constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK;
@@ -331,11 +341,14 @@ __global__ __launch_bounds__(Cfg::NT) void sgemm_dma_kernel(SgemmArgs p)
 
     const bool loader = uwave >= Cfg::NW - Cfg::LW;
     const int lw = loader ? uwave - (Cfg::NW - Cfg::LW) : 0;   // loader index
+    // rows / columns of the tile inside M and N
+    const int limA = MASK ? (int)(p.M - m0 < BM ? p.M - m0 : BM) : BM;
+    const int limB = MASK ? (int)(p.N - n0 < BN ? p.N - n0 : BN) : BN;
     unsigned offA[Cfg::A_LOADS], offB[Cfg::B_LOADS];
 #pragma unroll
-    for (int i = 0; i < Cfg::A_LOADS; ++i) offA[i] = sg_dma_offset<A_KC, BM>(lw * Cfg::A_LOADS + i, lane, lda);
+    for (int i = 0; i < Cfg::A_LOADS; ++i) offA[i] = sg_dma_offset<A_KC, BM, MASK>(lw * Cfg::A_LOADS + i, lane, lda, limA);
 #pragma unroll
-    for (int i = 0; i < Cfg::B_LOADS; ++i) offB[i] = sg_dma_offset<B_KC, BN>(lw * Cfg::B_LOADS + i, lane, ldb);
+    for (int i = 0; i < Cfg::B_LOADS; ++i) offB[i] = sg_dma_offset<B_KC, BN, MASK>(lw * Cfg::B_LOADS + i, lane, ldb, limB);
     auto issue_slice = [&](int kt, int slot) {
         if (!loader) return;
         const char *a = Ab + (long long)kt * stepA;
@@ -468,7 +481,7 @@ __global__ __launch_bounds__(Cfg::NT) void sgemm_dma_kernel(SgemmArgs p)
         }
     };
 
-    const int nk = p.K / BK;   // >= 2 (checked by the launcher)
+    const int nk = p.K / BK;   // whole slices, >= 2 (checked by the launcher)
     issue_slice(0, 0);
     issue_slice(1, 1);
     __builtin_amdgcn_s_waitcnt((LOADS & 15) | ((LOADS >> 4) << 14) | (7 << 4) | (15 << 8));   // slice 0 done
@@ -485,6 +498,52 @@ __global__ __launch_bounds__(Cfg::NT) void sgemm_dma_kernel(SgemmArgs p)
             mfmas(fa[cur], fb[cur]);
         }
     }
+    if constexpr (MASK) {
+        // The K % BK tail, after the whole slices (k still ascends): each lane
+        // loads its operand quads (four k) straight from global memory, zero
+        // for k >= K, rows and columns clamped as for the slices.
+        const int K = p.K, k0 = nk * BK;
+        if (k0 < K) {
+            const float *Am = p.A + (long long)mb * p.sA;
+            const float *Bm = p.B + (long long)mb * p.sB;
+            long long ar[Cfg::FM], bc[Cfg::FN];
+#pragma unroll
+            for (int i = 0; i < Cfg::FM; ++i) {
+                const long long r = m0 + wm * Cfg::TM + 32 * i + lr;
+                ar[i] = r < p.M ? r : p.M - 1;
+            }
+#pragma unroll
+            for (int j = 0; j < Cfg::FN; ++j) {
+                const long long c = n0 + wn * Cfg::TN + 32 * j + lr;
+                bc[j] = c < p.N ? c : p.N - 1;
+            }
+            // four k from kq of a row (stride 1) or a column (stride ld)
+            auto quad = [&](const float *x, long long stride, int kq) {
+                f32x4v v;
+                if (stride == 1 && kq + 3 < K) {
+                    const f32x4_g w = *reinterpret_cast<const f32x4_g *>(x);
+                    v = f32x4v{w[0], w[1], w[2], w[3]};
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[e] = kq + e < K ? x[e * stride] : 0.f;
+                }
+                return v;
+            };
+#pragma unroll
+            for (int u = 0; u < NU; ++u) {
+                if (k0 + 8 * u >= K) break;
+                const int kq = k0 + 8 * u + 4 * lk;   // this lane's quad
+                f32x4v qa[Cfg::FM], qb[Cfg::FN];
+#pragma unroll
+                for (int i = 0; i < Cfg::FM; ++i)
+                    qa[i] = A_KC ? quad(Am + ar[i] * lda + kq, 1, kq) : quad(Am + (long long)kq * lda + ar[i], lda, kq);
+#pragma unroll
+                for (int j = 0; j < Cfg::FN; ++j)
+                    qb[j] = B_KC ? quad(Bm + bc[j] * ldb + kq, 1, kq) : quad(Bm + (long long)kq * ldb + bc[j], ldb, kq);
+                mfmas(qa, qb);
+            }
+        }
+    }
 
     const float alpha = p.alpha, beta = p.beta;
     auto epilogue = [&](auto with_c) {
@@ -498,7 +557,7 @@ __global__ __launch_bounds__(Cfg::NT) void sgemm_dma_kernel(SgemmArgs p)
                     const long long col = n0 + wn * Cfg::TN + 32 * jj + 8 * g + 4 * lk;
                     const f32x4_t v = {acc[i][jj][4 * g], acc[i][jj][4 * g + 1], acc[i][jj][4 * g + 2],
                                        acc[i][jj][4 * g + 3]};
-                    store_row4<false, decltype(with_c)::value>(C, ldc, row, col, v, alpha, beta, 0, 0);
+                    store_row4<MASK, decltype(with_c)::value>(C, ldc, row, col, v, alpha, beta, p.M, p.N);
                 }
             }
         }
@@ -517,17 +576,34 @@ using SgDma256 = SgDmaCfg<256, 256, 2, 4>;
 using SgDma128 = SgDmaCfg<128, 128, 2, 4>;
 using SgDma64 = SgDmaCfg<64, 64, 2, 2>;
 
+// The direct-to-LDS kernel applies: 16-byte aligned operand rows, at least two
+// whole slices of k, no 16-byte chunk of an MN-contiguous operand (A stored
+// K x M, B stored K x N) straddling M or N, and 32-bit slice offsets.
 template <class Cfg>
 bool sg_dma_ok(const GemmProblem &q)
 {
     const bool aligned = (q.lda % 4 == 0) && (q.ldb % 4 == 0) && (q.strideA % 4 == 0) &&
                          (q.strideB % 4 == 0) && (reinterpret_cast<uintptr_t>(q.A) % 16 == 0) &&
                          (reinterpret_cast<uintptr_t>(q.B) % 16 == 0);
-    const bool whole = q.M % Cfg::BM == 0 && q.N % Cfg::BN == 0 && q.K % Cfg::BK == 0 && q.K >= 2 * Cfg::BK;
+    const bool shape = q.K >= 2 * Cfg::BK && (!q.transA || q.M % 4 == 0) && (q.transB || q.N % 4 == 0);
     // per-lane offsets within one slice are 32-bit: rows of the slice times ld
     const long long rows_a = q.transA ? Cfg::BK : Cfg::BM, rows_b = q.transB ? Cfg::BN : Cfg::BK;
     const bool fits = rows_a * q.lda * 4 < (1LL << 31) && rows_b * q.ldb * 4 < (1LL << 31);
-    return aligned && whole && fits;
+    return aligned && shape && fits;
+}
+
+template <class Cfg, bool MASK>
+void launch_sg_dma_ops(const SgemmArgs &a, dim3 grid, bool tA, bool tB, hipStream_t stream)
+{
+    const dim3 block(Cfg::NT);
+    if (!tA && !tB)
+        hipLaunchKernelGGL((sgemm_dma_kernel<Cfg, false, false, MASK>), grid, block, 0, stream, a);
+    else if (!tA)
+        hipLaunchKernelGGL((sgemm_dma_kernel<Cfg, false, true, MASK>), grid, block, 0, stream, a);
+    else if (!tB)
+        hipLaunchKernelGGL((sgemm_dma_kernel<Cfg, true, false, MASK>), grid, block, 0, stream, a);
+    else
+        hipLaunchKernelGGL((sgemm_dma_kernel<Cfg, true, true, MASK>), grid, block, 0, stream, a);
 }
 
 template <class Cfg>
@@ -539,17 +615,14 @@ hipError_t launch_sg_dma(const GemmProblem &q, hipStream_t stream)
     a.A = static_cast<const float *>(q.A); a.lda = q.lda; a.sA = q.strideA;
     a.B = static_cast<const float *>(q.B); a.ldb = q.ldb; a.sB = q.strideB;
     a.C = q.C; a.ldc = q.ldc; a.sC = q.strideC;
-    a.tiles_m = q.M / Cfg::BM;
-    a.tiles_n = q.N / Cfg::BN;
-    const dim3 grid(a.tiles_m * a.tiles_n, 1, q.batch), block(Cfg::NT);
-    if (!q.transA && !q.transB)
-        hipLaunchKernelGGL((sgemm_dma_kernel<Cfg, false, false>), grid, block, 0, stream, a);
-    else if (!q.transA)
-        hipLaunchKernelGGL((sgemm_dma_kernel<Cfg, false, true>), grid, block, 0, stream, a);
-    else if (!q.transB)
-        hipLaunchKernelGGL((sgemm_dma_kernel<Cfg, true, false>), grid, block, 0, stream, a);
+    a.tiles_m = (q.M + Cfg::BM - 1) / Cfg::BM;
+    a.tiles_n = (q.N + Cfg::BN - 1) / Cfg::BN;
+    const dim3 grid(a.tiles_m * a.tiles_n, 1, q.batch);
+    const bool whole = q.M % Cfg::BM == 0 && q.N % Cfg::BN == 0 && q.K % Cfg::BK == 0;
+    if (whole)
+        launch_sg_dma_ops<Cfg, false>(a, grid, q.transA, q.transB, stream);
     else
-        hipLaunchKernelGGL((sgemm_dma_kernel<Cfg, true, true>), grid, block, 0, stream, a);
+        launch_sg_dma_ops<Cfg, true>(a, grid, q.transA, q.transB, stream);
     return hipGetLastError();
 }
 
@@ -768,16 +841,16 @@ hipError_t launch_cfg(const GemmProblem &q, hipStream_t stream)
 
 hipError_t launch_sgemm(const GemmProblem &q, hipStream_t stream)
 {
-    // Direct-to-LDS whole tiles: 256x256 when that still gives one tile per
-    // CU, else 128x128; register-staged 128x128 tiles with bounds checks for
-    // everything else.
-    const long long t256 = (long long)(q.M / 256) * (q.N / 256) * q.batch;
+    // Direct-to-LDS tiles: 256x256 when that still gives one tile per CU,
+    // else 128x128, else 64x64 while those fill the CUs; the split-K kernel
+    // for smaller grids; register-staged 128x128 tiles with bounds checks for
+    // operands the direct-to-LDS kernel cannot take.
+    const long long t256 = (long long)((q.M + 255) / 256) * ((q.N + 255) / 256) * q.batch;
     const long long t128 = (long long)((q.M + 127) / 128) * ((q.N + 127) / 128) * q.batch;
-    const long long t64w = (long long)(q.M / 64) * (q.N / 64) * q.batch;   // whole 64x64 tiles
-    if (t128 < 256 && t64w >= 256 && sg_dma_ok<SgDma64>(q)) return launch_sg_dma<SgDma64>(q, stream);
+    const long long t64 = (long long)((q.M + 63) / 64) * ((q.N + 63) / 64) * q.batch;
+    if (t128 < 256 && t64 >= 256 && sg_dma_ok<SgDma64>(q)) return launch_sg_dma<SgDma64>(q, stream);
     if (t128 < 256) {
         // fewer 128x128 tiles than CUs: split K inside smaller workgroup tiles
-        const long long t64 = (long long)((q.M + 63) / 64) * ((q.N + 63) / 64) * q.batch;
         if (t64 >= 256) return launch_small<SgSmall64>(q, stream);
         return launch_small<SgSmall32>(q, stream);
     }

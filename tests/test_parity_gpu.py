@@ -374,6 +374,36 @@ def test_sgemm_64_tiles_direct_to_lds(tA, tB):
                       seed=23)
 
 
+def _ld4(cols, pad):
+    # a leading dimension that keeps rows 16-byte aligned (a multiple of four floats)
+    return cols + (-cols) % 4 + pad
+
+
+@pytest.mark.parametrize("tA,tB", [(False, False)] + OPS)
+@pytest.mark.parametrize("M,N,K", [(1000, 1000, 1000), (1000, 1000, 64), (996, 1204, 2000), (2052, 2100, 333),
+                                   (4100, 4100, 95), (4000, 4000, 1024)])
+def test_sgemm_ragged_direct_to_lds(M, N, K, tA, tB):
+    # M, N not multiples of the tile and K not of 32, 16-byte aligned rows: the
+    # direct-to-LDS kernels with clamped loads, the K tail from global memory and
+    # masked stores (64x64 tiles up to 1000^2, 128x128 at 2052x2100, 256x256 above)
+    a_cols, b_cols = (M if tA else K), (K if tB else N)
+    sample = 64 if M * N > 2_000_000 else 128
+    run_and_check("f32", M, N, K, 1.5, -0.5, lda=_ld4(a_cols, 4), ldb=_ld4(b_cols, 8), ldc=N + 3, sample=sample,
+                  transA=tA, transB=tB)
+    run_and_check("f32", M, N, K, 1.0, 1.0, sample=sample, kind_vals="int4", exact=True, transA=tA, transB=tB,
+                  lda=_ld4(a_cols, 0), ldb=_ld4(b_cols, 0), seed=37)
+
+
+@pytest.mark.parametrize("tA,tB", [(False, False), (False, True)])
+def test_sgemm_ragged_direct_to_lds_rows(tA, tB):
+    # M not a multiple of four is fine while A is K-contiguous (its chunks run along k)
+    N = 1200 if not tB else 1201
+    run_and_check("f32", 999, N, 2000, 1.5, -0.5, lda=2004, ldb=_ld4(2000 if tB else N, 4), ldc=N + 1, sample=128,
+                  transA=tA, transB=tB)
+    run_and_check("f32", 999, N, 2000, 1.0, 0.0, c_nan=True, sample=64, kind_vals="int4", exact=True,
+                  transA=tA, transB=tB, seed=41)
+
+
 @pytest.mark.parametrize("tA,tB", OPS)
 def test_transposed_hgemm_register_whole_tiles(tA, tB):
     # whole 128x128 tiles but K too short for the direct-to-LDS ring: unmasked register kernel
