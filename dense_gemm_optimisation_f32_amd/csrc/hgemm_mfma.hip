@@ -399,18 +399,24 @@ __device__ __forceinline__ void wait_vmcnt()
 
 // Per-lane byte offset (within one slice of global memory) of the 16-byte
 // chunk that lane `lane` of wave load g fetches for an operand slice of R rows
-// or columns and BK k; see the layouts above.
-template <bool KC, int R, int BK>
-__device__ __forceinline__ unsigned dma_offset(int g, int lane, long long ld)
+// or columns and BK k; see the layouts above.  With CLAMP, `lim` is how many
+// of the R rows (K-contiguous) or columns (MN-contiguous) lie inside M or N:
+// a chunk past it re-reads a valid one (row lim-1, or chunk 0 of its row),
+// whose products only reach C entries that are never stored.
+template <bool KC, int R, int BK, bool CLAMP>
+__device__ __forceinline__ unsigned dma_offset(int g, int lane, long long ld, int lim)
 {
     if (KC) {
         constexpr int CPR = BK / 8;
         const int r = (64 / CPR) * g + lane / CPR;
-        return (unsigned)(r * ld + 8 * ((lane % CPR) ^ swz_a<CPR>(r))) * 2u;
+        const int rr = (CLAMP && r >= lim) ? lim - 1 : r;
+        return (unsigned)(rr * ld + 8 * ((lane % CPR) ^ swz_a<CPR>(r))) * 2u;
     }
     constexpr int CPR = R / 8, RPL = 64 / CPR;   // chunks per row, rows per wave load
     const int k = RPL * g + lane / CPR;
-    return (unsigned)(k * ld + 8 * ((lane % CPR) ^ swz_b(k))) * 2u;
+    int ch = (lane % CPR) ^ swz_b(k);
+    if (CLAMP && 8 * ch >= lim) ch = 0;
+    return (unsigned)(k * ld + 8 * ch) * 2u;
 }
 
 // Fragment read address (bytes within a slot, substep 0, MFMA block 0) for the
@@ -430,8 +436,12 @@ __device__ __forceinline__ unsigned frag_offset(int first, int lane, int s)
     return (unsigned)(kq * R * 2 + 16 * ((n >> 3) ^ swz_b(kq)) + 2 * (n & 7));
 }
 
-// TA: A stored K x M; TB: B stored N x K.
-template <class Cfg, bool TA, bool TB>
+// TA: A stored K x M; TB: B stored N x K.  MASK: M and N need not be
+// multiples of the tile, nor K of BK (the loads clamp to valid rows and
+// columns, the K % BK tail is read straight from global memory after the last
+// slice, and stores outside C are skipped); an MN-contiguous operand then
+// needs its M or N to be a multiple of eight, so no 16-byte chunk straddles it.
+template <class Cfg, bool TA, bool TB, bool MASK>
 __global__ __launch_bounds__(Cfg::NT) void hgemm_dma_kernel(HgemmArgs p)
 {
     constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, S = Cfg::STAGES;
@@ -458,11 +468,16 @@ __global__ __launch_bounds__(Cfg::NT) void hgemm_dma_kernel(HgemmArgs p)
     const int uwave = __builtin_amdgcn_readfirstlane(wave);
     const bool loader = uwave >= Cfg::NW - Cfg::LW;
     const int lw = loader ? uwave - (Cfg::NW - Cfg::LW) : 0;
+    // rows / columns of the tile inside M and N
+    const int limA = MASK ? (int)(p.M - m0 < BM ? p.M - m0 : BM) : BM;
+    const int limB = MASK ? (int)(p.N - n0 < BN ? p.N - n0 : BN) : BN;
     unsigned offA[Cfg::A_LOADS], offB[Cfg::B_LOADS];
 #pragma unroll
-    for (int i = 0; i < Cfg::A_LOADS; ++i) offA[i] = dma_offset<A_KC, BM, BK>(lw * Cfg::A_LOADS + i, lane, lda);
+    for (int i = 0; i < Cfg::A_LOADS; ++i)
+        offA[i] = dma_offset<A_KC, BM, BK, MASK>(lw * Cfg::A_LOADS + i, lane, lda, limA);
 #pragma unroll
-    for (int i = 0; i < Cfg::B_LOADS; ++i) offB[i] = dma_offset<B_KC, BN, BK>(lw * Cfg::B_LOADS + i, lane, ldb);
+    for (int i = 0; i < Cfg::B_LOADS; ++i)
+        offB[i] = dma_offset<B_KC, BN, BK, MASK>(lw * Cfg::B_LOADS + i, lane, ldb, limB);
     auto issue_slice = [&](int kt, int slot) {
         if (!loader) return;
         const char *a = Ab + (long long)kt * stepA;
@@ -579,7 +594,7 @@ __global__ __launch_bounds__(Cfg::NT) void hgemm_dma_kernel(HgemmArgs p)
         }
     };
 
-    const int nk = p.K / BK;   // >= S (checked by the launcher)
+    const int nk = p.K / BK;   // whole slices, >= S (checked by the launcher)
     // Prologue: slices 0..S-1 in flight; slice 0 resident; substep 0 fragments read.
 #pragma unroll
     for (int st = 0; st < S; ++st) issue_slice(st, st);
@@ -608,6 +623,48 @@ __global__ __launch_bounds__(Cfg::NT) void hgemm_dma_kernel(HgemmArgs p)
             mfmas(fa[cur], fb[cur]);
         }
     }
+    if constexpr (MASK) {
+        // The K % BK tail, after the whole slices (k still ascends): each lane
+        // loads its eight k of each operand fragment straight from global
+        // memory, zero for k >= K, rows and columns clamped as for the slices.
+        const int K = p.K, k0 = nk * BK;
+        if (k0 < K) {
+            const uint16_t *Am = p.A + (long long)mb * p.sA;
+            const uint16_t *Bm = p.B + (long long)mb * p.sB;
+            long long ar[Cfg::FM], bc[Cfg::FN];
+#pragma unroll
+            for (int i = 0; i < Cfg::FM; ++i) {
+                const long long r = m0 + wm * Cfg::TM + 32 * i + lr;
+                ar[i] = r < p.M ? r : p.M - 1;
+            }
+#pragma unroll
+            for (int jj = 0; jj < Cfg::FN; ++jj) {
+                const long long c = n0 + wn * Cfg::TN + 32 * jj + lr;
+                bc[jj] = c < p.N ? c : p.N - 1;
+            }
+            // eight k from kq of a row (stride 1) or a column (stride ld)
+            auto eight = [&](const uint16_t *x, long long stride, int kq) -> half8 {
+                if (stride == 1 && kq + 7 < K) return __builtin_bit_cast(half8, *reinterpret_cast<const u32x4_g *>(x));
+                uint16_t h[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) h[e] = kq + e < K ? x[e * stride] : (uint16_t)0;
+                return __builtin_bit_cast(half8, h);
+            };
+#pragma unroll
+            for (int sub = 0; sub < NS; ++sub) {
+                if (k0 + 16 * sub >= K) break;
+                const int kq = k0 + 16 * sub + 8 * lk;   // this lane's eight k
+                half8 ta[Cfg::FM], tb[Cfg::FN];
+#pragma unroll
+                for (int i = 0; i < Cfg::FM; ++i)
+                    ta[i] = A_KC ? eight(Am + ar[i] * lda + kq, 1, kq) : eight(Am + (long long)kq * lda + ar[i], lda, kq);
+#pragma unroll
+                for (int jj = 0; jj < Cfg::FN; ++jj)
+                    tb[jj] = B_KC ? eight(Bm + bc[jj] * ldb + kq, 1, kq) : eight(Bm + (long long)kq * ldb + bc[jj], ldb, kq);
+                mfmas(ta, tb);
+            }
+        }
+    }
 
     const float alpha = p.alpha, beta = p.beta;
     auto epilogue = [&](auto with_c) {
@@ -621,7 +678,7 @@ __global__ __launch_bounds__(Cfg::NT) void hgemm_dma_kernel(HgemmArgs p)
                     const long long col = n0 + wn * Cfg::TN + 32 * jj + 8 * g + 4 * lk;
                     const f32x4_t v = {acc[i][jj][4 * g], acc[i][jj][4 * g + 1], acc[i][jj][4 * g + 2],
                                        acc[i][jj][4 * g + 3]};
-                    store_row4<false, decltype(with_c)::value>(C, ldc, row, col, v, alpha, beta, 0, 0);
+                    store_row4<MASK, decltype(with_c)::value>(C, ldc, row, col, v, alpha, beta, p.M, p.N);
                 }
             }
         }
@@ -633,6 +690,7 @@ __global__ __launch_bounds__(Cfg::NT) void hgemm_dma_kernel(HgemmArgs p)
 }
 
 using Hg128 = HgCfg<128, 128>;
+using Hg64 = HgCfg<64, 64>;   // for grids that 128x128 tiles would leave under-filled
 
 template <class Cfg, bool TA, bool TB>
 void launch_cfg_kernel(const HgemmArgs &a, bool whole, bool vec, dim3 grid, hipStream_t stream)
@@ -680,22 +738,38 @@ hipError_t launch_cfg(const GemmProblem &q, hipStream_t stream)
 
 // 256x256 tile, 8 waves (2 x 4) of 128x64, BK = 64, two LDS slots of 64 KB.
 using HgDma256 = HgDmaCfg<256, 256, 2, 2, 4, 64>;
-// 128x128 tile, 4 waves of 64x64, BK = 64, four slots of 32 KB: for grids that
-// 256x256 tiles would leave under-filled.
+// 128x128 tile, 8 waves (2 x 4) of 64x32, BK = 64, four slots of 32 KB: for
+// grids that 256x256 tiles would leave under-filled.
 using HgDma128 = HgDmaCfg<128, 128, 4, 2, 4, 64>;
 
+// The direct-to-LDS kernel applies: 16-byte aligned operand rows, at least
+// STAGES whole slices of k, no 16-byte chunk of an MN-contiguous operand
+// (A stored K x M, B stored K x N) straddling M or N, and 32-bit slice offsets.
 template <class Cfg>
 bool dma_ok(const GemmProblem &q)
 {
     const bool aligned = (q.lda % 8 == 0) && (q.ldb % 8 == 0) && (q.strideA % 8 == 0) &&
                          (q.strideB % 8 == 0) && (reinterpret_cast<uintptr_t>(q.A) % 16 == 0) &&
                          (reinterpret_cast<uintptr_t>(q.B) % 16 == 0);
-    const bool whole = q.M % Cfg::BM == 0 && q.N % Cfg::BN == 0 && q.K % Cfg::BK == 0 &&
-                       q.K >= Cfg::BK * Cfg::STAGES;
+    const bool shape = q.K >= Cfg::BK * Cfg::STAGES && (!q.transA || q.M % 8 == 0) && (q.transB || q.N % 8 == 0);
     // per-lane offsets within one slice are 32-bit: rows of the slice times ld
     const long long rows_a = q.transA ? Cfg::BK : Cfg::BM, rows_b = q.transB ? Cfg::BN : Cfg::BK;
     const bool fits = rows_a * q.lda * 2 < (1LL << 31) && rows_b * q.ldb * 2 < (1LL << 31);
-    return aligned && whole && fits;
+    return aligned && shape && fits;
+}
+
+template <class Cfg, bool MASK>
+void launch_dma_ops(const HgemmArgs &a, dim3 grid, bool tA, bool tB, hipStream_t stream)
+{
+    const dim3 block(Cfg::NT);
+    if (!tA && !tB)
+        hipLaunchKernelGGL((hgemm_dma_kernel<Cfg, false, false, MASK>), grid, block, 0, stream, a);
+    else if (!tA)
+        hipLaunchKernelGGL((hgemm_dma_kernel<Cfg, false, true, MASK>), grid, block, 0, stream, a);
+    else if (!tB)
+        hipLaunchKernelGGL((hgemm_dma_kernel<Cfg, true, false, MASK>), grid, block, 0, stream, a);
+    else
+        hipLaunchKernelGGL((hgemm_dma_kernel<Cfg, true, true, MASK>), grid, block, 0, stream, a);
 }
 
 template <class Cfg>
@@ -707,28 +781,38 @@ hipError_t launch_dma(const GemmProblem &q, hipStream_t stream)
     a.A = static_cast<const uint16_t *>(q.A); a.lda = q.lda; a.sA = q.strideA;
     a.B = static_cast<const uint16_t *>(q.B); a.ldb = q.ldb; a.sB = q.strideB;
     a.C = q.C; a.ldc = q.ldc; a.sC = q.strideC;
-    a.tiles_m = q.M / Cfg::BM;
-    a.tiles_n = q.N / Cfg::BN;
-    const dim3 grid(a.tiles_m * a.tiles_n, 1, q.batch), block(Cfg::NT);
-    if (!q.transA && !q.transB)
-        hipLaunchKernelGGL((hgemm_dma_kernel<Cfg, false, false>), grid, block, 0, stream, a);
-    else if (!q.transA)
-        hipLaunchKernelGGL((hgemm_dma_kernel<Cfg, false, true>), grid, block, 0, stream, a);
-    else if (!q.transB)
-        hipLaunchKernelGGL((hgemm_dma_kernel<Cfg, true, false>), grid, block, 0, stream, a);
+    a.tiles_m = (q.M + Cfg::BM - 1) / Cfg::BM;
+    a.tiles_n = (q.N + Cfg::BN - 1) / Cfg::BN;
+    const dim3 grid(a.tiles_m * a.tiles_n, 1, q.batch);
+    const bool whole = q.M % Cfg::BM == 0 && q.N % Cfg::BN == 0 && q.K % Cfg::BK == 0;
+    if (whole)
+        launch_dma_ops<Cfg, false>(a, grid, q.transA, q.transB, stream);
     else
-        hipLaunchKernelGGL((hgemm_dma_kernel<Cfg, true, true>), grid, block, 0, stream, a);
+        launch_dma_ops<Cfg, true>(a, grid, q.transA, q.transB, stream);
     return hipGetLastError();
 }
 
 hipError_t launch_hgemm(const GemmProblem &q, hipStream_t stream)
 {
-    // Direct-to-LDS 256x256 tiles when the problem is made of whole tiles and
-    // they give at least one tile per CU; 128x128 register-staged tiles (with
-    // bounds checks where needed) otherwise.
+    // Direct-to-LDS 256x256 tiles when they give at least one tile per CU,
+    // else 128x128 ones; 128x128 register-staged tiles (with bounds checks
+    // where needed) for operands the direct-to-LDS kernel cannot take.
+    //
+    // Both direct-to-LDS tiles run one workgroup per CU, so a grid runs in
+    // rounds of 256 workgroups.  A 128x128 tile does a quarter of a 256x256
+    // tile's work at about 0.6 of its rate (measured), i.e. takes 0.4 of its
+    // time: the 256x256 tile wins when 5 * its rounds <= 2 * the 128x128 rounds.
     const long long t256 = (long long)((q.M + 255) / 256) * ((q.N + 255) / 256) * q.batch;
-    if (t256 >= 256 && dma_ok<HgDma256>(q)) return launch_dma<HgDma256>(q, stream);
-    if (dma_ok<HgDma128>(q)) return launch_dma<HgDma128>(q, stream);
+    const long long t128 = (long long)((q.M + 127) / 128) * ((q.N + 127) / 128) * q.batch;
+    const bool ok256 = dma_ok<HgDma256>(q), ok128 = dma_ok<HgDma128>(q);
+    if (ok256 && ok128) {
+        const long long r256 = (t256 + 255) / 256, r128 = (t128 + 255) / 256;
+        if (5 * r256 <= 2 * r128) return launch_dma<HgDma256>(q, stream);
+        return launch_dma<HgDma128>(q, stream);
+    }
+    if (ok256 && t256 >= 256) return launch_dma<HgDma256>(q, stream);
+    if (ok128) return launch_dma<HgDma128>(q, stream);
+    if (t128 < 256) return launch_cfg<Hg64>(q, stream);
     return launch_cfg<Hg128>(q, stream);
 }
 

@@ -404,6 +404,34 @@ def test_sgemm_ragged_direct_to_lds_rows(tA, tB):
                   transA=tA, transB=tB, seed=41)
 
 
+def _ld8(cols, pad):
+    # a leading dimension that keeps rows 16-byte aligned (a multiple of eight halves)
+    return cols + (-cols) % 8 + pad
+
+
+@pytest.mark.parametrize("tA,tB", [(False, False)] + OPS)
+@pytest.mark.parametrize("M,N,K", [(1000, 1000, 300), (1000, 1000, 256), (2000, 2000, 2000), (4000, 4000, 1000),
+                                   (4104, 4104, 333)])
+def test_hgemm_ragged_direct_to_lds(M, N, K, tA, tB):
+    # M, N not multiples of the tile and K not of 64, 16-byte aligned rows: the
+    # direct-to-LDS kernels with clamped loads, the K tail from global memory and
+    # masked stores (128x128 tiles up to 2000^2, 256x256 above)
+    a_cols, b_cols = (M if tA else K), (K if tB else N)
+    sample = 64 if M * N > 2_000_000 else 128
+    run_and_check("f16", M, N, K, 1.5, -0.5, lda=_ld8(a_cols, 8), ldb=_ld8(b_cols, 16), ldc=N + 3, sample=sample,
+                  transA=tA, transB=tB)
+    run_and_check("f16", M, N, K, 1.0, 1.0, sample=sample, kind_vals="int4", exact=True, transA=tA, transB=tB,
+                  lda=_ld8(a_cols, 0), ldb=_ld8(b_cols, 0), seed=43)
+
+
+def test_hgemm_ragged_direct_to_lds_rows_and_batch():
+    # M not a multiple of eight with A K-contiguous; a ragged strided batch
+    run_and_check("f16", 1001, 1000, 500, 1.5, -0.5, lda=504, ldb=1008, ldc=1001, sample=128)
+    run_and_check("f16", 1001, 1000, 500, 1.0, 0.0, c_nan=True, kind_vals="int4", exact=True, sample=64, seed=47)
+    batched_check(200, 136, 304, 3, 1.5, -0.5)
+    batched_check(200, 136, 304, 3, 1.0, 1.0, kind_vals="int4", exact=True, seed=53)
+
+
 @pytest.mark.parametrize("tA,tB", OPS)
 def test_transposed_hgemm_register_whole_tiles(tA, tB):
     # whole 128x128 tiles but K too short for the direct-to-LDS ring: unmasked register kernel
