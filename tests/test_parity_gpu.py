@@ -410,12 +410,13 @@ def _ld8(cols, pad):
 
 
 @pytest.mark.parametrize("tA,tB", [(False, False)] + OPS)
-@pytest.mark.parametrize("M,N,K", [(1000, 1000, 300), (1000, 1000, 256), (2000, 2000, 2000), (4000, 4000, 1000),
-                                   (4104, 4104, 333)])
+@pytest.mark.parametrize("M,N,K", [(1000, 1000, 300), (1000, 1000, 256), (2000, 2000, 2000), (3000, 3000, 320),
+                                   (4000, 4000, 1000), (4104, 4104, 333)])
 def test_hgemm_ragged_direct_to_lds(M, N, K, tA, tB):
     # M, N not multiples of the tile and K not of 64, 16-byte aligned rows: the
     # direct-to-LDS kernels with clamped loads, the K tail from global memory and
-    # masked stores (128x128 tiles up to 2000^2, 256x256 above)
+    # masked stores (128x128 tiles up to 2000^2; 256x256 from 3000^2, where one
+    # round of 144 such tiles beats three rounds of 128x128 ones)
     a_cols, b_cols = (M if tA else K), (K if tB else N)
     sample = 64 if M * N > 2_000_000 else 128
     run_and_check("f16", M, N, K, 1.5, -0.5, lda=_ld8(a_cols, 8), ldb=_ld8(b_cols, 16), ldc=N + 3, sample=sample,
