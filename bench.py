@@ -415,18 +415,47 @@ def write_traffic(fetch_csv: str, write_csv: str) -> int:
     return 0
 
 
-def time_calls(fn, torch, stream, warmup=20, reps=30):
+def time_calls(fn, torch, stream, warmup=20, reps=30, graph_calls=20):
+    """Seconds per call of fn(s), which enqueues one library call on stream s.
+
+    Returns (median, min) over `reps` calls, each between its own pair of events on
+    `stream` (so a launch gap before the kernel counts), and the median over five
+    replays of one HIP graph holding `graph_calls` calls back to back, divided by
+    `graph_calls` (kernel time without launch gaps: what matters for kernels of a
+    few microseconds)."""
     for _ in range(warmup):
-        fn()
+        fn(stream)
     torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
     for a, b in evs:
         a.record(stream)
-        fn()
+        fn(stream)
         b.record(stream)
     torch.cuda.synchronize()
     ts = sorted(a.elapsed_time(b) * 1e-3 for a, b in evs)
-    return ts[len(ts) // 2], ts[0]
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    with torch.cuda.graph(g, stream=side):
+        for _ in range(graph_calls):
+            fn(side)
+    g.replay()
+    torch.cuda.synchronize()
+    tg = []
+    for _ in range(5):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        g.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+        tg.append(a.elapsed_time(b) * 1e-3 / graph_calls)
+    del g
+    return ts[len(ts) // 2], ts[0], sorted(tg)[2]
+
+
+def rates(med, graph, flop, peak):
+    """Extra-workload record: per-call median (launch-inclusive) and back-to-back graph time."""
+    return {"median_ms": med * 1e3, "tflops": flop / med / 1e12, "frac_of_peak": flop / med / 1e12 / peak,
+            "graph_ms_per_call": graph * 1e3, "graph_tflops": flop / graph / 1e12}
 
 
 def run_extra(dg, si, np, torch, dev, stream):
@@ -439,9 +468,8 @@ def run_extra(dg, si, np, torch, dev, stream):
         p = si.gemm_problem(M, N, K, seed=42, with_c=beta != 0)
         A, B = up(p["A"]), up(p["B"])
         C = up(p["C"]) if beta != 0 else torch.empty(M * N, dtype=torch.float32, device=dev)
-        med, mn = time_calls(lambda: dg.gemm_f32(M, N, K, alpha, A, K, B, N, beta, C, N, stream), torch, stream)
-        fl = 2.0 * M * N * K
-        out[name] = {"median_ms": med * 1e3, "tflops": fl / med / 1e12, "frac_of_peak": fl / med / 1e12 / PEAK_F32_TFLOPS}
+        med, _, gr = time_calls(lambda s: dg.gemm_f32(M, N, K, alpha, A, K, B, N, beta, C, N, s), torch, stream)
+        out[name] = rates(med, gr, 2.0 * M * N * K, PEAK_F32_TFLOPS)
 
     sg(512, 512, 512, 1.0, 0.0, "sgemm_512^3")
     sg(1001, 777, 513, 1.5, -0.5, "sgemm_1001x777x513_a1.5_b-0.5")
@@ -452,11 +480,9 @@ def run_extra(dg, si, np, torch, dev, stream):
     p = si.gemm_problem(2048, 2048, 2048, in_dtype=np.float16, seed=42, with_c=False)
     A, B = up(p["A"]), up(p["B"])
     C = torch.empty(2048 * 2048, dtype=torch.float32, device=dev)
-    med, _ = time_calls(lambda: dg.gemm_f16_f32acc(2048, 2048, 2048, 1.0, A, 2048, B, 2048, 0.0, C, 2048, stream),
-                        torch, stream)
-    fl = 2.0 * 2048 ** 3
-    out["hgemm_2048^3"] = {"median_ms": med * 1e3, "tflops": fl / med / 1e12,
-                           "frac_of_peak": fl / med / 1e12 / PEAK_F16_TFLOPS}
+    med, _, gr = time_calls(lambda s: dg.gemm_f16_f32acc(2048, 2048, 2048, 1.0, A, 2048, B, 2048, 0.0, C, 2048, s),
+                            torch, stream)
+    out["hgemm_2048^3"] = rates(med, gr, 2.0 * 2048 ** 3, PEAK_F16_TFLOPS)
 
     # op(A)op(B): the bench shapes with A stored K x M and/or B stored N x K
     for tA, tB in ((0, 1), (1, 0), (1, 1)):
@@ -468,25 +494,22 @@ def run_extra(dg, si, np, torch, dev, stream):
             C = torch.empty(M * N, dtype=torch.float32, device=dev)
             lda, ldb = (M if tA else K), (K if tB else N)
             fn = dg.gemm_f32_ex if kind == "sgemm" else dg.gemm_f16_f32acc_ex
-            med, _ = time_calls(lambda: fn(tA, tB, M, N, K, 1.0, A, lda, B, ldb, 0.0, C, N, stream), torch, stream)
-            fl = 2.0 * M * N * K
+            med, _, gr = time_calls(lambda s: fn(tA, tB, M, N, K, 1.0, A, lda, B, ldb, 0.0, C, N, s), torch, stream)
             peak = PEAK_F32_TFLOPS if kind == "sgemm" else PEAK_F16_TFLOPS
-            out[f"{kind}_{tag}_{M}x{N}x{K}"] = {"median_ms": med * 1e3, "tflops": fl / med / 1e12,
-                                                "frac_of_peak": fl / med / 1e12 / peak}
+            out[f"{kind}_{tag}_{M}x{N}x{K}"] = rates(med, gr, 2.0 * M * N * K, peak)
 
     # 16 x 1024^3 batched, beta = 1 (C is read and written: HBM-bound, ridge below the fp16 peak)
     nb, n = 16, 1024
     A = torch.empty(nb * n * n, dtype=torch.float16, device=dev).uniform_(-1, 1)
     B = torch.empty(nb * n * n, dtype=torch.float16, device=dev).uniform_(-1, 1)
     C = torch.empty(nb * n * n, dtype=torch.float32, device=dev).uniform_(-1, 1)
-    med, _ = time_calls(lambda: dg.gemm_batched_f16_f32acc(n, n, n, 1.0, A, n, n * n, B, n, n * n, 1.0, C, n, n * n,
-                                                           nb, stream), torch, stream)
+    med, _, gr = time_calls(lambda s: dg.gemm_batched_f16_f32acc(n, n, n, 1.0, A, n, n * n, B, n, n * n, 1.0, C, n,
+                                                                 n * n, nb, s), torch, stream)
     fl = 2.0 * nb * n ** 3
     bytes_alg = nb * n * n * (2 + 2 + 4 + 4)
-    out["batched_hgemm_16x1024^3_b1"] = {
-        "median_ms": med * 1e3, "tflops": fl / med / 1e12, "frac_of_peak": fl / med / 1e12 / PEAK_F16_TFLOPS,
-        "hbm_roofline_tflops": min(PEAK_F16_TFLOPS, fl / bytes_alg * PEAK_HBM_GBS / 1e3),
-        "warm_buffers": True}
+    out["batched_hgemm_16x1024^3_b1"] = dict(rates(med, gr, fl, PEAK_F16_TFLOPS),
+                                             hbm_roofline_tflops=min(PEAK_F16_TFLOPS, fl / bytes_alg * PEAK_HBM_GBS / 1e3),
+                                             warm_buffers=True)
     # cold: three operand sets (384 MB, more than the 256 MB last-level cache) used in turn,
     # so each call finds its inputs in HBM
     sets = [(torch.empty(nb * n * n, dtype=torch.float16, device=dev).uniform_(-1, 1),
@@ -494,17 +517,16 @@ def run_extra(dg, si, np, torch, dev, stream):
              torch.empty(nb * n * n, dtype=torch.float32, device=dev).uniform_(-1, 1)) for _ in range(3)]
     turn = [0]
 
-    def cold_call():
+    def cold_call(s):
         a, b, c = sets[turn[0] % 3]
         turn[0] += 1
-        dg.gemm_batched_f16_f32acc(n, n, n, 1.0, a, n, n * n, b, n, n * n, 1.0, c, n, n * n, nb, stream)
+        dg.gemm_batched_f16_f32acc(n, n, n, 1.0, a, n, n * n, b, n, n * n, 1.0, c, n, n * n, nb, s)
 
-    med, _ = time_calls(cold_call, torch, stream)
-    out["batched_hgemm_16x1024^3_b1_cold"] = {
-        "median_ms": med * 1e3, "tflops": fl / med / 1e12, "frac_of_peak": fl / med / 1e12 / PEAK_F16_TFLOPS,
-        "hbm_roofline_tflops": min(PEAK_F16_TFLOPS, fl / bytes_alg * PEAK_HBM_GBS / 1e3),
-        "frac_of_hbm_roofline": fl / med / 1e12 / min(PEAK_F16_TFLOPS, fl / bytes_alg * PEAK_HBM_GBS / 1e3),
-        "warm_buffers": False, "operand_sets": 3}
+    med, _, gr = time_calls(cold_call, torch, stream, graph_calls=21)
+    hbm_roof = min(PEAK_F16_TFLOPS, fl / bytes_alg * PEAK_HBM_GBS / 1e3)
+    out["batched_hgemm_16x1024^3_b1_cold"] = dict(rates(med, gr, fl, PEAK_F16_TFLOPS), hbm_roofline_tflops=hbm_roof,
+                                                  frac_of_hbm_roofline=fl / med / 1e12 / hbm_roof,
+                                                  warm_buffers=False, operand_sets=3)
     del sets
     return out
 
