@@ -7,44 +7,41 @@
 // against bank conflicts, and the larger 128x128 block tile), rebuilt for
 // gfx950 rather than translated:
 //   * matrix-core op: v_mfma_f32_32x32x16_f16 (a 32x32 fp32 block, 16 k per op,
-//     8 fp16 values of A and of B per lane);
-//   * a workgroup of 4 waves in a 2x2 grid; each wave owns a (BM/2) x (BN/2)
-//     tile of (BM/64) x (BN/64) MFMA blocks whose accumulators stay in
-//     registers for the whole K loop;
-//   * A is staged in LDS as [m][k] (K contiguous, 128-byte rows of eight
-//     16-byte chunks whose chunk index is XOR-swizzled with bits of the row --
-//     the MindNotes page's swizzling idea applied to 16-byte chunks), so an A
-//     operand is one 16-byte LDS read per lane;
-//   * B is staged in LDS in its own row-major [k][n] layout (rows padded so the
-//     four rows a transposed read touches fall in different banks -- the
-//     dandandamowang page's padding).  The K-packed B operand is assembled by
-//     two ds_read_b64_tr_b16 transposed LDS reads: within each 16-lane group,
-//     lane i receives element i%4 of the four-element vectors addressed by
-//     lanes i/4, i/4+4, i/4+8 and i/4+12, so lanes pointing at four
-//     consecutive n of rows k..k+3 hand each lane one column's four k values;
-//   * LDS is double-buffered with one barrier per K step; the next step's
-//     global loads are issued before the current step's MFMAs and written to
-//     the other buffer after them;
+//     8 fp16 values of A and of B per lane); each wave owns a grid of such
+//     blocks whose accumulators stay in registers for the whole K loop;
+//   * a K-contiguous operand tile (A stored M x K, B stored N x K) sits in LDS
+//     as rows of 16-byte chunks whose chunk index is XOR-swizzled with bits of
+//     the row (the MindNotes page's swizzling idea applied to 16-byte chunks),
+//     so an operand fragment is one 16-byte LDS read per lane;
+//   * an MN-contiguous tile (A stored K x M, B stored K x N) keeps its [k][mn]
+//     layout, swizzled or padded so that the rows one transposed read touches
+//     fall in different banks (the dandandamowang page's padding), and the
+//     K-packed fragment is assembled by two ds_read_b64_tr_b16 transposed LDS
+//     reads: within each 16-lane group, lane i receives element i%4 of the
+//     four-element vectors addressed by lanes i/4, i/4+4, i/4+8 and i/4+12, so
+//     lanes pointing at four consecutive n of rows k..k+3 hand each lane one
+//     column's four k values;
+//   * both reads hand lane l the same eight k (8*(l/32) .. +7 of the 16-k
+//     substep), so the four storage combinations (C = alpha*op(A)op(B) +
+//     beta*C, the MindNotes 'GEMM' page, section "core problem and arithmetic
+//     characteristics") add the same products in the same order;
 //   * workgroups are mapped to tiles so that the tiles one XCD (one L2) runs
 //     form a compact block of C;
 //   * epilogue C = alpha*acc + beta*C (C not read when beta == 0).
-// Instantiations per tile shape: MASK = false for problems made of whole
-// tiles whose rows start 4-byte aligned (no bounds checks anywhere), MASK =
-// true for everything else (out-of-range elements load as zero, stores are
-// masked; VEC says whether rows start 4-byte aligned, which allows 16-byte
-// loads -- CDNA's multi-dword global loads need only dword alignment).
 //
-// Transposed operands (C = alpha*op(A)op(B) + beta*C, the MindNotes 'GEMM'
-// page, section "core problem and arithmetic characteristics"): each kernel is
-// instantiated for the four storage combinations.  An operand tile is copied
-// to LDS in its stored orientation (16-byte loads along the contiguous
-// dimension), and the operand fragment is read in the way that layout calls
-// for: a K-contiguous operand (A stored M x K, B stored N x K) in swizzled
-// 128-byte rows read with one ds_read_b128 per lane, an MN-contiguous operand
-// (A stored K x M, B stored K x N) in [k][mn] rows read with two
-// ds_read_b64_tr_b16.  Both reads hand lane l the same eight k
-// (8*(l/32) .. +7 of the 16-k substep), so the four combinations add the same
-// products in the same order.
+// Two kernels; launch_hgemm picks one per problem:
+//   * hgemm_dma_kernel -- operands whose rows start 16-byte aligned.  K slices
+//     go from global memory straight into an LDS ring (direct-to-LDS loads, the
+//     gfx950 form of the page's asynchronous double buffering): 256x256 tiles
+//     with two slots of 64 k, or 128x128 tiles with four.  Ragged M, N and K
+//     are handled by clamped slice loads, a K tail read from global memory and
+//     masked stores;
+//   * hgemm_mfma_kernel -- everything else: 128x128 (64x64 for small grids)
+//     tiles of four waves in a 2 x 2 grid, read into registers with 16-byte
+//     loads (row starts 4-byte aligned: CDNA's multi-dword global loads need
+//     only dword alignment) or element loads, and written to a double-buffered
+//     LDS with one barrier per K step.  MASK = false for whole tiles, true
+//     otherwise (out-of-range elements load as zero, stores are masked).
 #include "gemm_internal.h"
 #include "tile_order.h"
 #include "epilogue.h"

@@ -1,31 +1,31 @@
 // sgemm_mfma.hip -- fp32 row-major GEMM on the CDNA4 fp32 matrix cores.
 //
-// Structure (the hierarchy of the ssxxe.cn V100 SGEMM article, section 3 and
-// its kernels of sections 2.1-2.3, and the MindNotes 'GEMM' page's
-// register-tiling sections, rebuilt for gfx950):
-//   * each workgroup owns one BM x BN tile of C and walks K in BK-wide steps;
-//   * each step's A (BM x BK) and B (BK x BN) tiles are read from HBM with
-//     coalesced 128-bit loads into registers, then written to LDS; LDS is
-//     double-buffered, so the loads of step t+1 are in flight while step t is
-//     computed and one barrier per step suffices (the article's section 2.3
-//     double buffering);
-//   * A is stored transposed in LDS, [k][m] (the pages store A as [BK][BM] so
-//     that one k gives consecutive m); B keeps its [k][n] layout;
-//   * the 2D register tile of outer products is executed by the matrix core:
-//     v_mfma_f32_32x32x2_f32 adds, for a 32x32 block of C held in 16 fp32
-//     registers per lane, the outer products of a 32-row column pair of A and a
-//     32-column row pair of B.  The four waves of a workgroup form a 2 x 2 grid
-//     of 64 x 64 wave tiles (2 x 2 MFMA blocks each).
-//   * the epilogue applies C = alpha*acc + beta*C (C not read when beta == 0)
-//     with per-element masks, so any M, N, K and leading dimension work;
-//     out-of-range A/B elements are loaded as zero.
-// Why MFMA and not VALU: fp32 VALU FMA without the packed form reaches half of
-// the chip's fp32 rate; the fp32 MFMA path has the full rate.
-// Two instantiations per tile shape: MASK = false for problems made of whole
-// tiles (no bounds checks anywhere), MASK = true for everything else.  Global
-// accesses are 16 bytes wide at any leading dimension: multi-dword global
-// loads and stores need only dword alignment on CDNA.  Workgroups are mapped
-// to tiles XCD by XCD (tile_order.h).
+// The 2D register tile of outer products (the MindNotes 'GEMM' page's
+// register-tiling sections; the tile hierarchy of section 3 of the ssxxe.cn
+// V100 SGEMM article) is executed by the matrix core: v_mfma_f32_32x32x2_f32
+// adds, for a 32x32 block of C held in 16 fp32 registers per lane, the outer
+// products of a 32-row column pair of A and a 32-column row pair of B.  Why
+// MFMA and not VALU: fp32 VALU FMA without the packed form reaches half of the
+// chip's fp32 rate; the fp32 MFMA path has the full rate.
+//
+// Three kernels; launch_sgemm picks one per problem:
+//   * sgemm_dma_kernel -- operands whose rows start 16-byte aligned.  Each
+//     K slice of A and B goes from global memory straight into a two-slot LDS
+//     ring (direct-to-LDS loads: the gfx950 form of the article's section 2.3
+//     double buffering, with no register staging), in 256x256, 128x128 or
+//     64x64 tiles.  Ragged M, N and K are handled by clamped slice loads, a K
+//     tail read from global memory and masked stores;
+//   * sgemm_mfma_kernel -- other operands when there are enough tiles:
+//     128x128 tiles read with 16-byte loads into registers and written to a
+//     double-buffered LDS (one barrier per step), zero outside the matrix;
+//   * sgemm_small_kernel -- grids of fewer than 256 tiles of 128x128 that the
+//     64x64 direct-to-LDS tiles cannot take: the waves of a workgroup split K,
+//     and their partial tiles are summed in a fixed order.
+// Every kernel applies C = alpha*acc + beta*C (C not read when beta == 0),
+// masked where the tile crosses the edge of C, and maps workgroups to tiles XCD
+// by XCD (tile_order.h).  Global accesses are 16 bytes wide at any leading
+// dimension: multi-dword global loads and stores need only dword alignment on
+// CDNA.
 //
 // Transposed operands (C = alpha*op(A)op(B) + beta*C, the MindNotes 'GEMM'
 // page, section "core problem and arithmetic characteristics"): every kernel
@@ -91,10 +91,13 @@ __device__ __forceinline__ f32x4_t load4(const float *X, long long ld, long long
     return v;
 }
 
-// TA: A stored K x M; TB: B stored N x K.  In LDS both operands are kept
-// MN-contiguous ([k][m] and [k][n]); a K-contiguous operand is transposed on
-// its way in by four scalar LDS writes, an MN-contiguous one is written as
-// 16-byte rows.
+// ---------------------------------------------------------------------------
+// Register-staged kernel (operands the direct-to-LDS kernel cannot take).
+// MASK = false for problems made of whole tiles (no bounds checks anywhere),
+// MASK = true for everything else.  TA: A stored K x M; TB: B stored N x K.
+// In LDS both operands are kept MN-contiguous ([k][m] and [k][n], the pages'
+// [BK][BM] layout of A); a K-contiguous operand is transposed on its way in by
+// four scalar LDS writes, an MN-contiguous one is written as 16-byte rows.
 template <class Cfg, bool MASK, bool TA, bool TB>
 __global__ __launch_bounds__(Cfg::NT) void sgemm_mfma_kernel(SgemmArgs p)
 {
@@ -234,9 +237,8 @@ __global__ __launch_bounds__(Cfg::NT) void sgemm_mfma_kernel(SgemmArgs p)
 }
 
 // ---------------------------------------------------------------------------
-// Whole-tile kernel fed by direct-to-LDS loads (global_load_lds_dwordx4: lane
-// l's 16 bytes land at M0 + 16*l, no register staging, no LDS-write
-// instructions).  Two LDS slots of BK = 32 k; slice t+2 is fetched while
+// Kernel fed by direct-to-LDS loads (global_load_lds_dwordx4: lane l's 16
+// bytes land at M0 + 16*l, no register staging, no LDS-write instructions).  Two LDS slots of BK = 32 k; slice t+2 is fetched while
 // slice t+1 waits and slice t is computed, which at fp32-MFMA speed (64
 // cycles per 32x32x2 op) leaves a whole slice of compute to hide the fetch.
 //
