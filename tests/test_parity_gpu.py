@@ -425,6 +425,16 @@ def test_hgemm_ragged_direct_to_lds(M, N, K, tA, tB):
                   lda=_ld8(a_cols, 0), ldb=_ld8(b_cols, 0), seed=43)
 
 
+@pytest.mark.parametrize("tA,tB", [(False, False), (True, True)])
+def test_hgemm_256_short_k(tA, tB):
+    # 256x256 direct-to-LDS tiles with the shortest rings: three whole slices of 64, and
+    # two plus a 32-k tail on a ragged grid (too short for the 128x128 four-slot ring)
+    for M, N, K in [(4096, 4096, 192), (4000, 4000, 160)]:
+        run_and_check("f16", M, N, K, 1.5, -0.5, sample=64, transA=tA, transB=tB)
+        run_and_check("f16", M, N, K, 1.0, 1.0, sample=32, kind_vals="int4", exact=True, transA=tA, transB=tB,
+                      seed=59)
+
+
 def test_hgemm_ragged_direct_to_lds_rows_and_batch():
     # M not a multiple of eight with A K-contiguous; a ragged strided batch
     run_and_check("f16", 1001, 1000, 500, 1.5, -0.5, lda=504, ldb=1008, ldc=1001, sample=128)
