@@ -645,9 +645,9 @@ hipError_t launch_sg_dma(const GemmProblem &q, hipStream_t stream)
 // A transposed operand changes only the loads: a K-contiguous operand (A
 // stored M x K, B stored N x K) is read as 16-byte quads of four k, an
 // MN-contiguous one as one float per lane and k (coalesced across the lanes).
-template <int FM_, int FN_, int KW_ = 4>
+template <int FM_, int FN_, int KW_, int P_>
 struct SgSmallCfg {
-    static constexpr int FM = FM_, FN = FN_, KW = KW_, NT = 64 * KW, P = 4;
+    static constexpr int FM = FM_, FN = FN_, KW = KW_, NT = 64 * KW, P = P_;   // P: steps of 8 k in flight
     static constexpr int TM = 32 * FM, TN = 32 * FN;
     static_assert(KW * FM * FN * 4 * 64 * 16 <= 160 * 1024, "partial tiles exceed LDS");
 };
@@ -800,8 +800,10 @@ hipError_t launch_small(const GemmProblem &q, hipStream_t stream)
 }
 
 // eight waves, two per SIMD, so that one wave's loads overlap the other's MFMAs
-using SgSmall64 = SgSmallCfg<2, 2, 8>;
-using SgSmall32 = SgSmallCfg<1, 1, 8>;
+// Eight waves each.  The 32x32 tile keeps two steps in flight: fewer registers
+// (52 against 68) let four work-groups share a CU instead of three.
+using SgSmall64 = SgSmallCfg<2, 2, 8, 4>;
+using SgSmall32 = SgSmallCfg<1, 1, 8, 2>;
 
 using SgBig = SgCfg<128, 128, 16, 2, 2>;
 
