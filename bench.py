@@ -11,8 +11,9 @@ reported beside it, with the roofline of the dominant (longest) kernel taken
 from HIP events recorded on the stream the kernels run on.  The CPU oracle is
 timed on a bounded sample of the same workload as a baseline.  The other
 benchmark configurations (SGEMM 512^3, the 1001x777x513 and 1024x1024x512
-SGEMMs, HGEMM 2048^3 and 16 batched 1024^3 HGEMMs with beta = 1) are timed
-after the main run and reported under "extra" (not part of the value).
+SGEMMs, HGEMM 2048^3 and 16 batched 1024^3 HGEMMs with beta = 1), two ragged
+shapes and the transposed storage combinations are timed after the main run
+and reported under "extra" (not part of the value).
 
 Warm-up: under this load the clocks take about 40 ms (about 100 steps) to
 settle; the default 200 untimed steps cover that, and 50 steps are timed.
@@ -483,6 +484,18 @@ def run_extra(dg, si, np, torch, dev, stream):
     med, _, gr = time_calls(lambda s: dg.gemm_f16_f32acc(2048, 2048, 2048, 1.0, A, 2048, B, 2048, 0.0, C, 2048, s),
                             torch, stream)
     out["hgemm_2048^3"] = rates(med, gr, 2.0 * 2048 ** 3, PEAK_F16_TFLOPS)
+
+    # ragged shapes (M, N not multiples of the tile, K not of the slice): the masked
+    # direct-to-LDS kernels
+    for kind, (M, N, K) in (("sgemm", (4000, 4000, 1000)), ("hgemm", (4000, 4000, 4000))):
+        dt = torch.float32 if kind == "sgemm" else torch.float16
+        A = torch.empty(M * K, dtype=dt, device=dev).uniform_(-1, 1)
+        B = torch.empty(K * N, dtype=dt, device=dev).uniform_(-1, 1)
+        C = torch.empty(M * N, dtype=torch.float32, device=dev)
+        fn = dg.gemm_f32 if kind == "sgemm" else dg.gemm_f16_f32acc
+        med, _, gr = time_calls(lambda s: fn(M, N, K, 1.0, A, K, B, N, 0.0, C, N, s), torch, stream)
+        peak = PEAK_F32_TFLOPS if kind == "sgemm" else PEAK_F16_TFLOPS
+        out[f"{kind}_ragged_{M}x{N}x{K}"] = rates(med, gr, 2.0 * M * N * K, peak)
 
     # op(A)op(B): the bench shapes with A stored K x M and/or B stored N x K
     for tA, tB in ((0, 1), (1, 0), (1, 1)):
