@@ -311,6 +311,40 @@ def test_runs_on_the_given_stream():
         assert oracle.normalized_error(rows_of(dC, 256, 192, 192), ref, bound) <= TOL
 
 
+def test_concurrent_streams():
+    # the library keeps no state between calls: four different kernels enqueued on four
+    # streams at once (SGEMM 256x256 direct-to-LDS, HGEMM 128x128 direct-to-LDS, the
+    # split-K SGEMM, a batched HGEMM) each give their own oracle result
+    note("four kernels on four streams at once")
+    cases = [("f32", 4096, 4096, 512, 64), ("f16", 2048, 2048, 512, 64), ("f32", 300, 260, 700, None)]
+    probs, devs = [], []
+    for i, (kind, M, N, K, sample) in enumerate(cases):
+        p = si.gemm_problem(M, N, K, in_dtype=np.float32 if kind == "f32" else np.float16, seed=80 + i)
+        probs.append(p)
+        devs.append((to_dev(p["A"]), to_dev(p["B"]), to_dev(p["C"])))
+    nb, bm, bn, bk = 3, 128, 136, 320
+    bp = [si.gemm_problem(bm, bn, bk, in_dtype=np.float16, seed=90, batch=b) for b in range(nb)]
+    bA = to_dev(np.concatenate([q["A"] for q in bp]))
+    bB = to_dev(np.concatenate([q["B"] for q in bp]))
+    bC = to_dev(np.concatenate([q["C"] for q in bp]))
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream() for _ in range(4)]
+    for s, (kind, M, N, K, _), p, (dA, dB, dC) in zip(streams, cases, probs, devs):
+        call(kind, p, 1.5, -0.5, dA, dB, dC, stream=s)
+    dg.gemm_batched_f16_f32acc(bm, bn, bk, 1.0, bA, bk, bm * bk, bB, bn, bk * bn, 1.0, bC, bn, bm * bn, nb,
+                               streams[3])
+    torch.cuda.synchronize()
+    for i, ((kind, M, N, K, sample), p, (_, _, dC)) in enumerate(zip(cases, probs, devs)):
+        rows = si.sample_rows(80 + i, M, sample) if sample else None
+        ref, bound = oracle.gemm_ref(M, N, K, 1.5, p["A"], p["lda"], p["B"], p["ldb"], -0.5, p["C"], p["ldc"],
+                                     rows=rows)
+        assert oracle.normalized_error(rows_of(dC, M, N, p["ldc"], rows), ref, bound) <= TOL, kind
+    for b in range(nb):
+        q = bp[b]
+        ref, bound = oracle.gemm_ref(bm, bn, bk, 1.0, q["A"], bk, q["B"], bn, 1.0, q["C"], bn)
+        assert oracle.normalized_error(rows_of(bC[b * bm * bn:], bm, bn, bn), ref, bound) <= TOL, f"member {b}"
+
+
 # ------------------------------------------------------------------ op(A) / op(B)
 # C = alpha*op(A)op(B) + beta*C with A stored K x M (transA) and/or B stored
 # N x K (transB).  Each case names the kernel it reaches; the int4 runs are
