@@ -612,6 +612,43 @@ def test_random_sweep(case):
                   transA=c["tA"], transB=c["tB"], seed=c["seed"], c_nan=(c["beta"] == 0.0))
 
 
+def _dma_sweep_cases(n):
+    """n problems large enough for the direct-to-LDS kernels (grids of 64x64 to 256x256 tiles),
+    with 16-byte aligned rows, ragged M, N, K and random storage orientations."""
+    u = si.splitmix64(4242, 16 * n)
+    pick = lambda k, lo, hi: lo + int(u[k] % np.uint64(hi - lo + 1))
+    alphas, betas = [1.0, 1.5, -0.75], [0.0, 1.0, -0.5]
+    cases = []
+    for c in range(n):
+        b = 16 * c
+        kind = "f32" if u[b] % np.uint64(2) == 0 else "f16"
+        lo, hi = [(900, 2000), (2000, 3500), (3900, 4400)][int(u[b + 12] % np.uint64(3))]
+        M, N = pick(b + 1, lo, hi), pick(b + 2, lo, hi)
+        if u[b + 13] % np.uint64(2) == 0:   # MN-contiguous operands can take the direct-to-LDS kernels
+            M, N = M - M % 8, N - N % 8
+        cases.append(dict(kind=kind, M=M, N=N, K=pick(b + 3, 64, 700),
+                          pa=pick(b + 4, 0, 3), pb=pick(b + 5, 0, 3), pc=pick(b + 6, 0, 9),
+                          tA=bool(u[b + 7] % np.uint64(2)), tB=bool(u[b + 8] % np.uint64(2)),
+                          alpha=alphas[int(u[b + 9] % np.uint64(3))], beta=betas[int(u[b + 10] % np.uint64(3))],
+                          ints=bool(u[b + 11] % np.uint64(3) == 0), seed=700 + c))
+    return cases
+
+
+@pytest.mark.parametrize("case", _dma_sweep_cases(24), ids=lambda c: f"{c['kind']}-{c['M']}x{c['N']}x{c['K']}"
+                         f"-t{int(c['tA'])}{int(c['tB'])}")
+def test_random_sweep_direct_to_lds(case):
+    # leading dimensions rounded up to whole 16-byte chunks plus 0-3 chunks of padding
+    c = case
+    q = 4 if c["kind"] == "f32" else 8
+    a_cols, b_cols = (c["M"] if c["tA"] else c["K"]), (c["K"] if c["tB"] else c["N"])
+    lda = a_cols + (-a_cols) % q + q * c["pa"]
+    ldb = b_cols + (-b_cols) % q + q * c["pb"]
+    run_and_check(c["kind"], c["M"], c["N"], c["K"], c["alpha"], c["beta"],
+                  kind_vals="int4" if c["ints"] else "pm1", exact=c["ints"], lda=lda, ldb=ldb,
+                  ldc=c["N"] + c["pc"], transA=c["tA"], transB=c["tB"], seed=c["seed"], sample=64,
+                  c_nan=(c["beta"] == 0.0))
+
+
 # ------------------------------------------------------------------ graph capture
 def test_graph_capture_replays_match_eager():
     # the library enqueues plain kernel launches on the caller's stream (no memset,
