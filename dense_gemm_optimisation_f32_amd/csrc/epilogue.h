@@ -17,7 +17,10 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 // four consecutive floats in global memory at dword (not 16-byte) alignment
 typedef float f32x4_g __attribute__((ext_vector_type(4), aligned(4)));
 
-// C[row][col..col+3] = alpha*acc + beta*C (beta term only when WITH_C).
+// C[row][col..col+3] = alpha*acc + beta*C (beta term only when WITH_C), as
+// fma(beta, c, alpha*acc) written out: left to the compiler, the contraction
+// of alpha*acc + beta*c may come out either way round in different kernels,
+// and the storage orientations of one product must give the same bits.
 // MASK: rows >= M and columns >= N are skipped (a row whose four columns are
 // all inside is still written with one 16-byte access).
 template <bool MASK, bool WITH_C>
@@ -28,7 +31,11 @@ __device__ __forceinline__ void store_row4(float *C, long long ldc, long long ro
     float *dst = C + row * ldc + col;
     if (!MASK || col + 3 < N) {
         f32x4_t v = alpha * acc;
-        if (WITH_C) v += beta * f32x4_t(*reinterpret_cast<const f32x4_g *>(dst));
+        if (WITH_C) {
+            const f32x4_t c = *reinterpret_cast<const f32x4_g *>(dst);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = __builtin_fmaf(beta, c[e], v[e]);
+        }
         *reinterpret_cast<f32x4_g *>(dst) = v;
         return;
     }
@@ -36,7 +43,7 @@ __device__ __forceinline__ void store_row4(float *C, long long ldc, long long ro
     for (int e = 0; e < 4; ++e) {
         if (MASK && col + e >= N) break;
         float v = alpha * acc[e];
-        if (WITH_C) v += beta * dst[e];
+        if (WITH_C) v = __builtin_fmaf(beta, dst[e], v);
         dst[e] = v;
     }
 }

@@ -290,7 +290,9 @@ __device__ __forceinline__ void sg_dma16(const void *sbase, unsigned voff, unsig
 }
 
 typedef float f32x4v __attribute__((ext_vector_type(4)));
+typedef float f32x2v __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) f32x4v lds_f32x4;
+typedef __attribute__((address_space(3))) f32x2v lds_f32x2;
 typedef __attribute__((address_space(3))) float lds_f32;
 
 // Per-lane byte offset (within one slice of global memory) of the 16-byte
@@ -365,32 +367,47 @@ __global__ __launch_bounds__(Cfg::NT) void sgemm_dma_kernel(SgemmArgs p)
 
     const int wm = wave / Cfg::WN, wn = wave % Cfg::WN;
     const int lr = lane & 31, lk = lane >> 5;
+    // Rows of the wave's A blocks.  With a K-contiguous A, block i holds rows
+    // 32i .. 32i+31 of the wave tile.  With an MN-contiguous A, the rows of
+    // IA consecutive blocks interleave (block i of a group holds rows IA*r + i),
+    // so that one LDS read of IA consecutive m gives a lane its operand for
+    // all IA blocks: four 16-byte reads per step instead of sixteen 4-byte ones.
+    // The k order of every MFMA is unchanged.
+    constexpr int IA = A_KC ? 1 : (Cfg::FM % 4 == 0 ? 4 : (Cfg::FM % 2 == 0 ? 2 : 1));
+    auto arow = [&](int i) { return wm * Cfg::TM + 32 * IA * (i / IA) + IA * lr + (i % IA); };
+    // Likewise the columns of an MN-contiguous B interleave over pairs of blocks
+    // (block j of a pair holds columns 2c + j), read with one 8-byte read per k.
+    // The accumulator of MFMA block (i, j) gives a lane four consecutive rows of
+    // D = C^T, i.e. columns 2c + j for four consecutive c: across the pair the
+    // lane then owns eight consecutive columns, stored as two 16-byte rows.
+    constexpr int IB = (B_KC || Cfg::FN % 2 != 0) ? 1 : 2;
+    auto bcol = [&](int j) { return wn * Cfg::TN + 32 * IB * (j / IB) + IB * lr + (j % IB); };
     // Operand read addresses (bytes within a slot).  K-contiguous: the row and
     // the lane part of its chunk index (logical chunk 2u+lk).  MN-contiguous:
-    // row 4*lk (plus 8u+e), logical chunk (32-column block + lr)/4, physical
-    // chunk flipped by 8 when lk = 1.
+    // row 4*lk (plus 8u+e), logical chunk m/4 of the lane's first m, physical
+    // chunk flipped by 8 when lk = 1 (for A, one address per group of IA blocks).
     unsigned rowA[Cfg::FM], tA[Cfg::FM], rowB[Cfg::FN], tB[Cfg::FN];
 #pragma unroll
     for (int i = 0; i < Cfg::FM; ++i) {
-        const int r = wm * Cfg::TM + 32 * i + lr;
+        const int r = arow(i);
         if (A_KC) {
             rowA[i] = (unsigned)(r * BK * 4);
             tA[i] = (unsigned)(lk ^ sg_swz_a(r));
         } else {
             const int q = r >> 2;
-            rowA[i] = (unsigned)(4 * lk * BM * 4 + 16 * (q ^ (8 * lk)) + 4 * (lr & 3));
+            rowA[i] = (unsigned)(4 * lk * BM * 4 + 16 * (q ^ (8 * lk)) + 4 * (r & 3));
             tA[i] = 0;
         }
     }
 #pragma unroll
     for (int j = 0; j < Cfg::FN; ++j) {
-        const int c = wn * Cfg::TN + 32 * j + lr;
+        const int c = bcol(j);
         if (B_KC) {
             rowB[j] = (unsigned)(Cfg::A_BYTES + c * BK * 4);
             tB[j] = (unsigned)(lk ^ sg_swz_a(c));
         } else {
             const int q = c >> 2;
-            rowB[j] = (unsigned)(Cfg::A_BYTES + 4 * lk * BN * 4 + 16 * (q ^ (8 * lk)) + 4 * (lr & 3));
+            rowB[j] = (unsigned)(Cfg::A_BYTES + 4 * lk * BN * 4 + 16 * (q ^ (8 * lk)) + 4 * (c & 3));
             tB[j] = 0;
         }
     }
@@ -405,27 +422,50 @@ __global__ __launch_bounds__(Cfg::NT) void sgemm_dma_kernel(SgemmArgs p)
 
     // Operand fragments of one eight-k step u: element e of fa[i] / fb[j] is the
     // operand of MFMA (u, e) for block i / j.  A K-contiguous fragment is one
-    // 16-byte read, an MN-contiguous one four 4-byte reads.
+    // 16-byte read; an MN-contiguous B fragment is four 4-byte reads, and an
+    // MN-contiguous A group of IA blocks four reads of IA floats.
     auto read_frags = [&](int slot, int u, f32x4v *fa, f32x4v *fb) {
         const unsigned base = lds0 + slot * Cfg::SLOT_BYTES;
+        if constexpr (A_KC) {
 #pragma unroll
-        for (int i = 0; i < Cfg::FM; ++i) {
-            if constexpr (A_KC) {
+            for (int i = 0; i < Cfg::FM; ++i)
                 fa[i] = *(const lds_f32x4 *)(uintptr_t)(base + rowA[i] + 16 * (tA[i] ^ (2u * u)));
-            } else {
+        } else {
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    fa[i][e] = *(const lds_f32 *)(uintptr_t)(base + rowA[i] + (8 * u + e) * BM * 4);
+            for (int g = 0; g < Cfg::FM; g += IA) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const unsigned at = base + rowA[g] + (8 * u + e) * BM * 4;
+                    if constexpr (IA == 4) {
+                        const f32x4v v = *(const lds_f32x4 *)(uintptr_t)at;
+#pragma unroll
+                        for (int x = 0; x < 4; ++x) fa[g + x][e] = v[x];
+                    } else if constexpr (IA == 2) {
+                        const f32x2v v = *(const lds_f32x2 *)(uintptr_t)at;
+                        fa[g][e] = v[0];
+                        fa[g + 1][e] = v[1];
+                    } else {
+                        fa[g][e] = *(const lds_f32 *)(uintptr_t)at;
+                    }
+                }
             }
         }
 #pragma unroll
-        for (int j = 0; j < Cfg::FN; ++j) {
+        for (int j = 0; j < Cfg::FN; j += IB) {
             if constexpr (B_KC) {
                 fb[j] = *(const lds_f32x4 *)(uintptr_t)(base + rowB[j] + 16 * (tB[j] ^ (2u * u)));
             } else {
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    fb[j][e] = *(const lds_f32 *)(uintptr_t)(base + rowB[j] + (8 * u + e) * BN * 4);
+                for (int e = 0; e < 4; ++e) {
+                    const unsigned at = base + rowB[j] + (8 * u + e) * BN * 4;
+                    if constexpr (IB == 2) {
+                        const f32x2v v = *(const lds_f32x2 *)(uintptr_t)at;
+                        fb[j][e] = v[0];
+                        fb[j + 1][e] = v[1];
+                    } else {
+                        fb[j][e] = *(const lds_f32 *)(uintptr_t)at;
+                    }
+                }
             }
         }
     };
@@ -440,7 +480,7 @@ __global__ __launch_bounds__(Cfg::NT) void sgemm_dma_kernel(SgemmArgs p)
     };
     // Issue the LDS reads of the next step one after each of this step's first
     // MFMAs, so they have the rest of the step to land.
-    constexpr int READS = Cfg::FM * (A_KC ? 1 : 4) + Cfg::FN * (B_KC ? 1 : 4);
+    constexpr int READS = (A_KC ? Cfg::FM : Cfg::FM / IA * 4) + (B_KC ? Cfg::FN : Cfg::FN / IB * 4);
     constexpr int PAIRS = READS < 4 * Cfg::FM * Cfg::FN ? READS : 4 * Cfg::FM * Cfg::FN;
     auto interleave = [&]() {
 #pragma unroll
@@ -511,12 +551,12 @@ __global__ __launch_bounds__(Cfg::NT) void sgemm_dma_kernel(SgemmArgs p)
             long long ar[Cfg::FM], bc[Cfg::FN];
 #pragma unroll
             for (int i = 0; i < Cfg::FM; ++i) {
-                const long long r = m0 + wm * Cfg::TM + 32 * i + lr;
+                const long long r = m0 + arow(i);
                 ar[i] = r < p.M ? r : p.M - 1;
             }
 #pragma unroll
             for (int j = 0; j < Cfg::FN; ++j) {
-                const long long c = n0 + wn * Cfg::TN + 32 * j + lr;
+                const long long c = n0 + bcol(j);
                 bc[j] = c < p.N ? c : p.N - 1;
             }
             // four k from kq of a row (stride 1) or a column (stride ld)
@@ -551,15 +591,32 @@ __global__ __launch_bounds__(Cfg::NT) void sgemm_dma_kernel(SgemmArgs p)
     auto epilogue = [&](auto with_c) {
 #pragma unroll
         for (int i = 0; i < Cfg::FM; ++i) {
-            const long long row = m0 + wm * Cfg::TM + 32 * i + lr;
+            const long long row = m0 + arow(i);
+            if constexpr (IB == 1) {
 #pragma unroll
-            for (int jj = 0; jj < Cfg::FN; ++jj) {
+                for (int jj = 0; jj < Cfg::FN; ++jj) {
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const long long col = n0 + wn * Cfg::TN + 32 * jj + 8 * g + 4 * lk;
-                    const f32x4_t v = {acc[i][jj][4 * g], acc[i][jj][4 * g + 1], acc[i][jj][4 * g + 2],
-                                       acc[i][jj][4 * g + 3]};
-                    store_row4<MASK, decltype(with_c)::value>(C, ldc, row, col, v, alpha, beta, p.M, p.N);
+                    for (int g = 0; g < 4; ++g) {
+                        const long long col = n0 + wn * Cfg::TN + 32 * jj + 8 * g + 4 * lk;
+                        const f32x4_t v = {acc[i][jj][4 * g], acc[i][jj][4 * g + 1], acc[i][jj][4 * g + 2],
+                                           acc[i][jj][4 * g + 3]};
+                        store_row4<MASK, decltype(with_c)::value>(C, ldc, row, col, v, alpha, beta, p.M, p.N);
+                    }
+                }
+            } else {
+                // blocks jj, jj+1: columns 2c + 0/1 for c = 8g + 4lk + e, i.e. eight
+                // consecutive columns from 16g + 8lk
+#pragma unroll
+                for (int jj = 0; jj < Cfg::FN; jj += 2) {
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const long long col = n0 + wn * Cfg::TN + 32 * jj + 16 * g + 8 * lk;
+                        const f32x16 &a0 = acc[i][jj], &a1 = acc[i][jj + 1];
+                        const f32x4_t lo = {a0[4 * g], a1[4 * g], a0[4 * g + 1], a1[4 * g + 1]};
+                        const f32x4_t hi = {a0[4 * g + 2], a1[4 * g + 2], a0[4 * g + 3], a1[4 * g + 3]};
+                        store_row4<MASK, decltype(with_c)::value>(C, ldc, row, col, lo, alpha, beta, p.M, p.N);
+                        store_row4<MASK, decltype(with_c)::value>(C, ldc, row, col + 4, hi, alpha, beta, p.M, p.N);
+                    }
                 }
             }
         }
