@@ -376,7 +376,9 @@ __device__ __forceinline__ lds_void *lds_ptr(unsigned byte)
 // wave's 1 KB lands contiguously at LDS byte lds_addr (lane l at +16*l).  It is
 // issued through inline asm so that the compiler neither reorders LDS accesses
 // around it (memory clobber) nor adds its own conservative vmcnt(0) before
-// every later LDS read: completion is tracked explicitly with wait_vmcnt.
+// every later LDS read: completion is tracked explicitly with wait_vmcnt.  M0
+// (the LDS destination) is set inside the statement; the compiler does not
+// track that clobber, which is safe because these kernels give M0 no other use.
 __device__ __forceinline__ void dma16(const void *sbase, unsigned voff, unsigned lds_addr)
 {
     asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"

@@ -281,6 +281,10 @@ struct SgDmaCfg {
 __device__ __forceinline__ int sg_swz_a(int r) { return (r ^ (r >> 3)) & 7; }
 __device__ __forceinline__ int sg_swz_b(int k) { return 8 * ((k >> 2) & 1); }
 
+// One direct-to-LDS load (16 bytes per lane, the wave's 1 KB contiguous at LDS
+// byte lds_addr).  M0 (the LDS destination) is set inside the statement; the
+// compiler does not track that clobber, which is safe because these kernels
+// give M0 no other use.
 __device__ __forceinline__ void sg_dma16(const void *sbase, unsigned voff, unsigned lds_addr)
 {
     asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
@@ -316,6 +320,20 @@ __device__ __forceinline__ unsigned sg_dma_offset(int g, int lane, long long ld,
     return (unsigned)(k * ld + 4 * ch) * 4u;
 }
 
+// Per-lane part of the offset of an MN-contiguous slice load g (R floats per
+// row, RPL = 256 / R rows per wave load): the load reads rows RPL*g ..
+// RPL*g + RPL-1, which share one chunk swizzle because RPL divides four, so the
+// per-lane part depends on g only through that swizzle s (0 or 8) and the row
+// part RPL*g*ld is uniform.  Two registers then serve every load of a slice.
+template <int R, bool CLAMP>
+__device__ __forceinline__ unsigned sg_mc_lane_offset(int lane, long long ld, int lim, int s)
+{
+    constexpr int CPR = R / 4;
+    int ch = (lane % CPR) ^ s;
+    if (CLAMP && 4 * ch >= lim) ch = 0;
+    return (unsigned)((lane / CPR) * ld + 4 * ch) * 4u;
+}
+
 // TA: A stored K x M; TB: B stored N x K.  MASK: M and N need not be
 // multiples of the tile, nor K of BK (the loads clamp to valid rows and
 // columns, the K % BK tail is read straight from global memory after the last
@@ -348,11 +366,27 @@ __global__ __launch_bounds__(Cfg::NT) void sgemm_dma_kernel(SgemmArgs p)
     // rows / columns of the tile inside M and N
     const int limA = MASK ? (int)(p.M - m0 < BM ? p.M - m0 : BM) : BM;
     const int limB = MASK ? (int)(p.N - n0 < BN ? p.N - n0 : BN) : BN;
-    unsigned offA[Cfg::A_LOADS], offB[Cfg::B_LOADS];
+    // K-contiguous operands keep one offset per load; MN-contiguous ones two
+    // per-lane parts (swizzle 0 or 8) and a uniform row part per load.
+    constexpr int NOA = A_KC ? Cfg::A_LOADS : 2, NOB = B_KC ? Cfg::B_LOADS : 2;
+    unsigned offA[NOA], offB[NOB];
 #pragma unroll
-    for (int i = 0; i < Cfg::A_LOADS; ++i) offA[i] = sg_dma_offset<A_KC, BM, MASK>(lw * Cfg::A_LOADS + i, lane, lda, limA);
+    for (int i = 0; i < NOA; ++i)
+        offA[i] = A_KC ? sg_dma_offset<true, BM, MASK>(lw * Cfg::A_LOADS + i, lane, lda, limA)
+                       : sg_mc_lane_offset<BM, MASK>(lane, lda, limA, 8 * i);
 #pragma unroll
-    for (int i = 0; i < Cfg::B_LOADS; ++i) offB[i] = sg_dma_offset<B_KC, BN, MASK>(lw * Cfg::B_LOADS + i, lane, ldb, limB);
+    for (int i = 0; i < NOB; ++i)
+        offB[i] = B_KC ? sg_dma_offset<true, BN, MASK>(lw * Cfg::B_LOADS + i, lane, ldb, limB)
+                       : sg_mc_lane_offset<BN, MASK>(lane, ldb, limB, 8 * i);
+    auto issue_one = [&](auto kc, auto rr, const char *base, const unsigned *off, long long ld, int g, int i,
+                         unsigned lds_addr) {
+        if constexpr (decltype(kc)::value) {
+            sg_dma16(base, off[i], lds_addr);
+        } else {
+            constexpr int RPL = 256 / decltype(rr)::value;
+            sg_dma16(base + (long long)RPL * g * ld * 4, off[sg_swz_b(RPL * g) ? 1 : 0], lds_addr);
+        }
+    };
     auto issue_slice = [&](int kt, int slot) {
         if (!loader) return;
         const char *a = Ab + (long long)kt * stepA;
@@ -360,9 +394,13 @@ __global__ __launch_bounds__(Cfg::NT) void sgemm_dma_kernel(SgemmArgs p)
         const unsigned la = lds0 + slot * Cfg::SLOT_BYTES + lw * Cfg::A_LOADS * 1024;
         const unsigned lb = lds0 + slot * Cfg::SLOT_BYTES + Cfg::A_BYTES + lw * Cfg::B_LOADS * 1024;
 #pragma unroll
-        for (int i = 0; i < Cfg::A_LOADS; ++i) sg_dma16(a, offA[i], la + 1024 * i);
+        for (int i = 0; i < Cfg::A_LOADS; ++i)
+            issue_one(std::bool_constant<A_KC>{}, std::integral_constant<int, BM>{}, a, offA, lda,
+                      lw * Cfg::A_LOADS + i, i, la + 1024 * i);
 #pragma unroll
-        for (int i = 0; i < Cfg::B_LOADS; ++i) sg_dma16(b, offB[i], lb + 1024 * i);
+        for (int i = 0; i < Cfg::B_LOADS; ++i)
+            issue_one(std::bool_constant<B_KC>{}, std::integral_constant<int, BN>{}, b, offB, ldb,
+                      lw * Cfg::B_LOADS + i, i, lb + 1024 * i);
     };
 
     const int wm = wave / Cfg::WN, wn = wave % Cfg::WN;
