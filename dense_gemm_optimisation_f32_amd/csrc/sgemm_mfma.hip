@@ -320,18 +320,48 @@ __device__ __forceinline__ unsigned sg_dma_offset(int g, int lane, long long ld,
     return (unsigned)(k * ld + 4 * ch) * 4u;
 }
 
-// Per-lane part of the offset of an MN-contiguous slice load g (R floats per
-// row, RPL = 256 / R rows per wave load): the load reads rows RPL*g ..
-// RPL*g + RPL-1, which share one chunk swizzle because RPL divides four, so the
-// per-lane part depends on g only through that swizzle s (0 or 8) and the row
-// part RPL*g*ld is uniform.  Two registers then serve every load of a slice.
-template <int R, bool CLAMP>
-__device__ __forceinline__ unsigned sg_mc_lane_offset(int lane, long long ld, int lim, int s)
+// A slice load g splits into a uniform row part (bytes, added to the base
+// pointer) and a per-lane part.  The per-lane part depends on g only through
+// the chunk swizzle: g % 8 for a K-contiguous operand (rows 8g .. 8g+7), bit 2
+// of RPL*g for an MN-contiguous one (rows RPL*g .. RPL*g + RPL-1 share one
+// swizzle since RPL divides four).  Masked K-contiguous loads clamp their rows,
+// which depends on g, so they keep the whole offset in the per-lane part.
+template <bool KC, int R, bool MASK>
+__device__ __forceinline__ long long sg_row_part(int g, long long ld)
 {
-    constexpr int CPR = R / 4;
-    int ch = (lane % CPR) ^ s;
-    if (CLAMP && 4 * ch >= lim) ch = 0;
+    if (KC) return MASK ? 0 : 32LL * g * ld;
+    return (long long)(256 / R) * g * ld * 4;
+}
+
+template <bool KC, int R, bool MASK>
+__device__ __forceinline__ unsigned sg_lane_part(int g, int lane, long long ld, int lim)
+{
+    if (KC) {
+        if (MASK) return sg_dma_offset<true, R, true>(g, lane, ld, lim);
+        const int l3 = lane >> 3;
+        return (unsigned)(l3 * ld + 4 * ((lane & 7) ^ l3 ^ (g & 7))) * 4u;
+    }
+    constexpr int CPR = R / 4, RPL = 256 / R;
+    int ch = (lane % CPR) ^ sg_swz_b(RPL * g);
+    if (MASK && 4 * ch >= lim) ch = 0;
     return (unsigned)((lane / CPR) * ld + 4 * ch) * 4u;
+}
+
+// How many distinct per-lane parts the loads g = lw + LW*i (i < LOADS) of one
+// loading wave have: the swizzle's period in g (8, or 8/RPL) divided by its gcd
+// with LW is the period in i.
+template <bool KC, bool MASK, int R, int LOADS, int LW>
+constexpr int sg_lane_parts()
+{
+    if (KC && MASK) return LOADS;
+    const int per_g = KC ? 8 : 8 / (256 / R);
+    int a = per_g, b = LW;
+    while (b) {
+        const int t = a % b;
+        a = b;
+        b = t;
+    }
+    return per_g / a < LOADS ? per_g / a : LOADS;
 }
 
 // TA: A stored K x M; TB: B stored N x K.  MASK: M and N need not be
@@ -366,44 +396,35 @@ __global__ __launch_bounds__(Cfg::NT) void sgemm_dma_kernel(SgemmArgs p)
     // rows / columns of the tile inside M and N
     const int limA = MASK ? (int)(p.M - m0 < BM ? p.M - m0 : BM) : BM;
     const int limB = MASK ? (int)(p.N - n0 < BN ? p.N - n0 : BN) : BN;
-    // K-contiguous operands keep one offset per load; MN-contiguous ones two
-    // per-lane parts (swizzle 0 or 8) and a uniform row part per load.
-    constexpr int NOA = A_KC ? Cfg::A_LOADS : 2, NOB = B_KC ? Cfg::B_LOADS : 2;
-    unsigned offA[NOA], offB[NOB];
+    // Loading wave lw issues loads g = lw + LW*i, so the loaders fetch
+    // neighbouring rows, and load g lands at byte 1024*g of the operand's part
+    // of the slot.  Load i uses per-lane part i % P.
+    constexpr int LW = Cfg::LW;
+    constexpr int PA = sg_lane_parts<A_KC, MASK, BM, Cfg::A_LOADS, LW>();
+    constexpr int PB = sg_lane_parts<B_KC, MASK, BN, Cfg::B_LOADS, LW>();
+    unsigned offA[PA], offB[PB];
 #pragma unroll
-    for (int i = 0; i < NOA; ++i)
-        offA[i] = A_KC ? sg_dma_offset<true, BM, MASK>(lw * Cfg::A_LOADS + i, lane, lda, limA)
-                       : sg_mc_lane_offset<BM, MASK>(lane, lda, limA, 8 * i);
+    for (int d = 0; d < PA; ++d) offA[d] = sg_lane_part<A_KC, BM, MASK>(lw + LW * d, lane, lda, limA);
 #pragma unroll
-    for (int i = 0; i < NOB; ++i)
-        offB[i] = B_KC ? sg_dma_offset<true, BN, MASK>(lw * Cfg::B_LOADS + i, lane, ldb, limB)
-                       : sg_mc_lane_offset<BN, MASK>(lane, ldb, limB, 8 * i);
-    auto issue_one = [&](auto kc, auto rr, const char *base, const unsigned *off, long long ld, int g, int i,
-                         unsigned lds_addr) {
-        if constexpr (decltype(kc)::value) {
-            sg_dma16(base, off[i], lds_addr);
-        } else {
-            constexpr int RPL = 256 / decltype(rr)::value;
-            sg_dma16(base + (long long)RPL * g * ld * 4, off[sg_swz_b(RPL * g) ? 1 : 0], lds_addr);
-        }
-    };
+    for (int d = 0; d < PB; ++d) offB[d] = sg_lane_part<B_KC, BN, MASK>(lw + LW * d, lane, ldb, limB);
     auto issue_slice = [&](int kt, int slot) {
         if (!loader) return;
         const char *a = Ab + (long long)kt * stepA;
         const char *b = Bb + (long long)kt * stepB;
-        const unsigned la = lds0 + slot * Cfg::SLOT_BYTES + lw * Cfg::A_LOADS * 1024;
-        const unsigned lb = lds0 + slot * Cfg::SLOT_BYTES + Cfg::A_BYTES + lw * Cfg::B_LOADS * 1024;
+        const unsigned sa = lds0 + slot * Cfg::SLOT_BYTES, sb = sa + Cfg::A_BYTES;
 #pragma unroll
-        for (int i = 0; i < Cfg::A_LOADS; ++i)
-            issue_one(std::bool_constant<A_KC>{}, std::integral_constant<int, BM>{}, a, offA, lda,
-                      lw * Cfg::A_LOADS + i, i, la + 1024 * i);
+        for (int i = 0; i < Cfg::A_LOADS; ++i) {
+            const int g = lw + LW * i;
+            sg_dma16(a + sg_row_part<A_KC, BM, MASK>(g, lda), offA[i % PA], sa + 1024 * g);
+        }
 #pragma unroll
-        for (int i = 0; i < Cfg::B_LOADS; ++i)
-            issue_one(std::bool_constant<B_KC>{}, std::integral_constant<int, BN>{}, b, offB, ldb,
-                      lw * Cfg::B_LOADS + i, i, lb + 1024 * i);
+        for (int i = 0; i < Cfg::B_LOADS; ++i) {
+            const int g = lw + LW * i;
+            sg_dma16(b + sg_row_part<B_KC, BN, MASK>(g, ldb), offB[i % PB], sb + 1024 * g);
+        }
     };
 
-    const int wm = wave / Cfg::WN, wn = wave % Cfg::WN;
+    const int wm = uwave / Cfg::WN, wn = uwave % Cfg::WN;
     const int lr = lane & 31, lk = lane >> 5;
     // Rows of the wave's A blocks.  With a K-contiguous A, block i holds rows
     // 32i .. 32i+31 of the wave tile.  With an MN-contiguous A, the rows of
@@ -412,14 +433,14 @@ __global__ __launch_bounds__(Cfg::NT) void sgemm_dma_kernel(SgemmArgs p)
     // all IA blocks: four 16-byte reads per step instead of sixteen 4-byte ones.
     // The k order of every MFMA is unchanged.
     constexpr int IA = A_KC ? 1 : (Cfg::FM % 4 == 0 ? 4 : (Cfg::FM % 2 == 0 ? 2 : 1));
-    auto arow = [&](int i) { return wm * Cfg::TM + 32 * IA * (i / IA) + IA * lr + (i % IA); };
+    auto arow = [&](int i, int l) { return wm * Cfg::TM + 32 * IA * (i / IA) + IA * l + (i % IA); };
     // Likewise the columns of an MN-contiguous B interleave over pairs of blocks
     // (block j of a pair holds columns 2c + j), read with one 8-byte read per k.
     // The accumulator of MFMA block (i, j) gives a lane four consecutive rows of
     // D = C^T, i.e. columns 2c + j for four consecutive c: across the pair the
     // lane then owns eight consecutive columns, stored as two 16-byte rows.
     constexpr int IB = (B_KC || Cfg::FN % 2 != 0) ? 1 : 2;
-    auto bcol = [&](int j) { return wn * Cfg::TN + 32 * IB * (j / IB) + IB * lr + (j % IB); };
+    auto bcol = [&](int j, int l) { return wn * Cfg::TN + 32 * IB * (j / IB) + IB * l + (j % IB); };
     // Operand read addresses (bytes within a slot).  K-contiguous: the row and
     // the lane part of its chunk index (logical chunk 2u+lk).  MN-contiguous:
     // row 4*lk (plus 8u+e), logical chunk m/4 of the lane's first m, physical
@@ -427,7 +448,7 @@ __global__ __launch_bounds__(Cfg::NT) void sgemm_dma_kernel(SgemmArgs p)
     unsigned rowA[Cfg::FM], tA[Cfg::FM], rowB[Cfg::FN], tB[Cfg::FN];
 #pragma unroll
     for (int i = 0; i < Cfg::FM; ++i) {
-        const int r = arow(i);
+        const int r = arow(i, lr);
         if (A_KC) {
             rowA[i] = (unsigned)(r * BK * 4);
             tA[i] = (unsigned)(lk ^ sg_swz_a(r));
@@ -439,7 +460,7 @@ __global__ __launch_bounds__(Cfg::NT) void sgemm_dma_kernel(SgemmArgs p)
     }
 #pragma unroll
     for (int j = 0; j < Cfg::FN; ++j) {
-        const int c = bcol(j);
+        const int c = bcol(j, lr);
         if (B_KC) {
             rowB[j] = (unsigned)(Cfg::A_BYTES + c * BK * 4);
             tB[j] = (unsigned)(lk ^ sg_swz_a(c));
@@ -578,6 +599,11 @@ __global__ __launch_bounds__(Cfg::NT) void sgemm_dma_kernel(SgemmArgs p)
             mfmas(fa[cur], fb[cur]);
         }
     }
+    // The tail and the epilogue take the lane's row and k half from a lane id
+    // read afresh, so that no address derived from it stays live (and spills)
+    // across the K loop.
+    const int elane = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    const int elr = elane & 31, elk = elane >> 5;
     if constexpr (MASK) {
         // The K % BK tail, after the whole slices (k still ascends): each lane
         // loads its operand quads (four k) straight from global memory, zero
@@ -589,12 +615,12 @@ __global__ __launch_bounds__(Cfg::NT) void sgemm_dma_kernel(SgemmArgs p)
             long long ar[Cfg::FM], bc[Cfg::FN];
 #pragma unroll
             for (int i = 0; i < Cfg::FM; ++i) {
-                const long long r = m0 + arow(i);
+                const long long r = m0 + arow(i, elr);
                 ar[i] = r < p.M ? r : p.M - 1;
             }
 #pragma unroll
             for (int j = 0; j < Cfg::FN; ++j) {
-                const long long c = n0 + bcol(j);
+                const long long c = n0 + bcol(j, elr);
                 bc[j] = c < p.N ? c : p.N - 1;
             }
             // four k from kq of a row (stride 1) or a column (stride ld)
@@ -612,7 +638,7 @@ __global__ __launch_bounds__(Cfg::NT) void sgemm_dma_kernel(SgemmArgs p)
 #pragma unroll
             for (int u = 0; u < NU; ++u) {
                 if (k0 + 8 * u >= K) break;
-                const int kq = k0 + 8 * u + 4 * lk;   // this lane's quad
+                const int kq = k0 + 8 * u + 4 * elk;   // this lane's quad
                 f32x4v qa[Cfg::FM], qb[Cfg::FN];
 #pragma unroll
                 for (int i = 0; i < Cfg::FM; ++i)
@@ -629,13 +655,13 @@ __global__ __launch_bounds__(Cfg::NT) void sgemm_dma_kernel(SgemmArgs p)
     auto epilogue = [&](auto with_c) {
 #pragma unroll
         for (int i = 0; i < Cfg::FM; ++i) {
-            const long long row = m0 + arow(i);
+            const long long row = m0 + arow(i, elr);
             if constexpr (IB == 1) {
 #pragma unroll
                 for (int jj = 0; jj < Cfg::FN; ++jj) {
 #pragma unroll
                     for (int g = 0; g < 4; ++g) {
-                        const long long col = n0 + wn * Cfg::TN + 32 * jj + 8 * g + 4 * lk;
+                        const long long col = n0 + wn * Cfg::TN + 32 * jj + 8 * g + 4 * elk;
                         const f32x4_t v = {acc[i][jj][4 * g], acc[i][jj][4 * g + 1], acc[i][jj][4 * g + 2],
                                            acc[i][jj][4 * g + 3]};
                         store_row4<MASK, decltype(with_c)::value>(C, ldc, row, col, v, alpha, beta, p.M, p.N);
@@ -648,7 +674,7 @@ __global__ __launch_bounds__(Cfg::NT) void sgemm_dma_kernel(SgemmArgs p)
                 for (int jj = 0; jj < Cfg::FN; jj += 2) {
 #pragma unroll
                     for (int g = 0; g < 4; ++g) {
-                        const long long col = n0 + wn * Cfg::TN + 32 * jj + 16 * g + 8 * lk;
+                        const long long col = n0 + wn * Cfg::TN + 32 * jj + 16 * g + 8 * elk;
                         const f32x16 &a0 = acc[i][jj], &a1 = acc[i][jj + 1];
                         const f32x4_t lo = {a0[4 * g], a1[4 * g], a0[4 * g + 1], a1[4 * g + 1]};
                         const f32x4_t hi = {a0[4 * g + 2], a1[4 * g + 2], a0[4 * g + 3], a1[4 * g + 3]};
