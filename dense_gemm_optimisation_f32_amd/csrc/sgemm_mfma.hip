@@ -798,30 +798,42 @@ __global__ __launch_bounds__(Cfg::NT) void sgemm_small_kernel(SgemmArgs p)
     // Row i of op(A) starts at arow[i] and its k-th element is arow[i][k * sa];
     // column j of op(B) likewise with bcol[j] and sb.
     const long long sa = TA ? lda : 1, sb = TB ? 1 : ldb;
-    bool rowok[FM], colok[FN];
+    // Rows and columns past M or N read row or column 0.
     const float *arow[FM];
     const float *bcol[FN];
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
         const long long r = m0 + 32 * i + lr;
-        rowok[i] = r < M;
-        arow[i] = A + (rowok[i] ? r : 0) * (TA ? 1 : lda);
+        arow[i] = A + (r < M ? r : 0) * (TA ? 1 : lda);
     }
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
         const long long c = n0 + 32 * j + lr;
-        colok[j] = c < N;
-        bcol[j] = B + (colok[j] ? c : 0) * (TB ? ldb : 1);
+        bcol[j] = B + (c < N ? c : 0) * (TB ? ldb : 1);
     }
 
-    // Four k of one operand row or column starting at kq (zero outside).
-    auto quad = [&](const float *x, long long stride, bool ok, int kq, bool kcontig) {
+    // Four k of one operand row or column starting at kq, zero for k >= ke
+    // (the masked form, for a wave's last partial step of eight k).
+    auto quad = [&](const float *x, long long stride, int kq, bool kcontig) {
         f32x4_t v;
-        if (kcontig && ok && kq + 3 < ke) {
+        if (kcontig && kq + 3 < ke) {
             v = *reinterpret_cast<const f32x4_g *>(x + kq);
         } else {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) v[e] = (ok && kq + e < ke) ? x[(long long)(kq + e) * stride] : 0.f;
+            for (int e = 0; e < 4; ++e) v[e] = kq + e < ke ? x[(long long)(kq + e) * stride] : 0.f;
+        }
+        return v;
+    };
+    // The same for a whole step (kq + 3 < ke), with no branch: out-of-range
+    // rows and columns read row or column 0 instead, and their products reach
+    // only entries of C that are never stored.
+    auto quad_full = [&](const float *x, long long stride, int kq, bool kcontig) {
+        f32x4_t v;
+        if (kcontig) {
+            v = *reinterpret_cast<const f32x4_g *>(x + kq);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = x[(long long)(kq + e) * stride];
         }
         return v;
     };
@@ -829,9 +841,9 @@ __global__ __launch_bounds__(Cfg::NT) void sgemm_small_kernel(SgemmArgs p)
     auto load_step = [&](int k, f32x4_t *a, f32x4_t *b) {
         const int kq = k + 4 * lk;   // this lane's k quad starts here
 #pragma unroll
-        for (int i = 0; i < FM; ++i) a[i] = quad(arow[i], sa, rowok[i], kq, !TA);
+        for (int i = 0; i < FM; ++i) a[i] = quad_full(arow[i], sa, kq, !TA);
 #pragma unroll
-        for (int j = 0; j < FN; ++j) b[j] = quad(bcol[j], sb, colok[j], kq, TB);
+        for (int j = 0; j < FN; ++j) b[j] = quad_full(bcol[j], sb, kq, TB);
     };
 
     f32x16 acc[FM][FN];
@@ -841,25 +853,45 @@ __global__ __launch_bounds__(Cfg::NT) void sgemm_small_kernel(SgemmArgs p)
         for (int j = 0; j < FN; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+    auto mfmas = [&](const f32x4_t *a, const f32x4_t *b) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(b[j][e], a[i][e], acc[i][j], 0, 0, 0);
+    };
 
-    const int nsteps = (ke > kb) ? (ke - kb + 7) / 8 : 0;
+    // Whole steps of eight k, P in flight.  The loads are unconditional so the
+    // compiler waits only for the step about to be used; a load past the last
+    // whole step re-reads that step and is never used.
+    const int nfull = (ke > kb) ? (ke - kb) / 8 : 0;
+    if (nfull > 0) {
+        const int last = kb + 8 * (nfull - 1);
 #pragma unroll
-    for (int s = 0; s < P; ++s)
-        if (s < nsteps) load_step(kb + 8 * s, ra[s], rb[s]);
-    for (int s0 = 0; s0 < nsteps; s0 += P) {
+        for (int s = 0; s < P; ++s) load_step(min(kb + 8 * s, last), ra[s], rb[s]);
+        int s0 = 0;
+        for (; s0 + P <= nfull; s0 += P) {
 #pragma unroll
-        for (int s = 0; s < P; ++s) {
-            if (s0 + s < nsteps) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-#pragma unroll
-                    for (int i = 0; i < FM; ++i)
-#pragma unroll
-                        for (int j = 0; j < FN; ++j)
-                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(rb[s][j][e], ra[s][i][e], acc[i][j], 0, 0, 0);
-                if (s0 + s + P < nsteps) load_step(kb + 8 * (s0 + s + P), ra[s], rb[s]);
+            for (int s = 0; s < P; ++s) {
+                mfmas(ra[s], rb[s]);
+                load_step(min(kb + 8 * (s0 + s + P), last), ra[s], rb[s]);
+                __builtin_amdgcn_sched_barrier(0);   // keep each refill right after its step
             }
         }
+#pragma unroll
+        for (int s = 0; s < P; ++s)
+            if (s0 + s < nfull) mfmas(ra[s], rb[s]);
+    }
+    if (kb + 8 * nfull < ke) {   // the partial step (K not a multiple of 8)
+        const int kq = kb + 8 * nfull + 4 * lk;
+        f32x4_t a[FM], b[FN];
+#pragma unroll
+        for (int i = 0; i < FM; ++i) a[i] = quad(arow[i], sa, kq, !TA);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) b[j] = quad(bcol[j], sb, kq, TB);
+        mfmas(a, b);
     }
 
     // Partial tiles to LDS: quad g of block (i, j) of wave w at
