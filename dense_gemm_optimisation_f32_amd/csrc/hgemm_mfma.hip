@@ -30,7 +30,7 @@
 //   * epilogue C = alpha*acc + beta*C (C not read when beta == 0).
 //
 // Two kernels; launch_hgemm picks one per problem:
-//   * hgemm_dma_kernel -- operands whose rows start 16-byte aligned.  K slices
+//   * hgemm_dma_kernel -- operands whose rows start 4-byte aligned.  K slices
 //     go from global memory straight into an LDS ring (direct-to-LDS loads, the
 //     gfx950 form of the page's asynchronous double buffering): 256x256 tiles
 //     with two slots of 64 k, or 128x128 tiles with four.  Ragged M, N and K
@@ -741,15 +741,17 @@ using HgDma256 = HgDmaCfg<256, 256, 2, 2, 4, 64>;
 // grids that 256x256 tiles would leave under-filled.
 using HgDma128 = HgDmaCfg<128, 128, 4, 2, 4, 64>;
 
-// The direct-to-LDS kernel applies: 16-byte aligned operand rows, at least
+// The direct-to-LDS kernel applies: 4-byte aligned operand rows, at least
 // STAGES whole slices of k, no 16-byte chunk of an MN-contiguous operand
 // (A stored K x M, B stored K x N) straddling M or N, and 32-bit slice offsets.
 template <class Cfg>
 bool dma_ok(const GemmProblem &q)
 {
-    const bool aligned = (q.lda % 8 == 0) && (q.ldb % 8 == 0) && (q.strideA % 8 == 0) &&
-                         (q.strideB % 8 == 0) && (reinterpret_cast<uintptr_t>(q.A) % 16 == 0) &&
-                         (reinterpret_cast<uintptr_t>(q.B) % 16 == 0);
+    // 16-byte chunks start a multiple of eight halves into a row, so 4-byte
+    // aligned rows keep them dword aligned, which is all the 16-byte loads need
+    const bool aligned = (q.lda % 2 == 0) && (q.ldb % 2 == 0) && (q.strideA % 2 == 0) &&
+                         (q.strideB % 2 == 0) && (reinterpret_cast<uintptr_t>(q.A) % 4 == 0) &&
+                         (reinterpret_cast<uintptr_t>(q.B) % 4 == 0);
     const bool shape = q.K >= Cfg::BK * Cfg::STAGES && (!q.transA || q.M % 8 == 0) && (q.transB || q.N % 8 == 0);
     // per-lane offsets within one slice are 32-bit: rows of the slice times ld
     const long long rows_a = q.transA ? Cfg::BK : Cfg::BM, rows_b = q.transB ? Cfg::BN : Cfg::BK;

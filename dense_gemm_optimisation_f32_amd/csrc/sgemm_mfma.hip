@@ -9,13 +9,15 @@
 // chip's fp32 rate; the fp32 MFMA path has the full rate.
 //
 // Three kernels; launch_sgemm picks one per problem:
-//   * sgemm_dma_kernel -- operands whose rows start 16-byte aligned.  Each
+//   * sgemm_dma_kernel -- the main kernel (any leading dimension).  Each
 //     K slice of A and B goes from global memory straight into a two-slot LDS
 //     ring (direct-to-LDS loads: the gfx950 form of the article's section 2.3
 //     double buffering, with no register staging), in 256x256, 128x128 or
 //     64x64 tiles.  Ragged M, N and K are handled by clamped slice loads, a K
 //     tail read from global memory and masked stores;
-//   * sgemm_mfma_kernel -- other operands when there are enough tiles:
+//   * sgemm_mfma_kernel -- problems the direct-to-LDS kernel cannot take (K
+//     below two slices, or an MN-contiguous operand whose M or N is not a
+//     multiple of four) when there are enough tiles:
 //     128x128 tiles read with 16-byte loads into registers and written to a
 //     double-buffered LDS (one barrier per step), zero outside the matrix;
 //   * sgemm_small_kernel -- grids of fewer than 256 tiles of 128x128 that the
@@ -699,15 +701,15 @@ using SgDma256 = SgDmaCfg<256, 256, 2, 4>;
 using SgDma128 = SgDmaCfg<128, 128, 2, 4>;
 using SgDma64 = SgDmaCfg<64, 64, 2, 2>;
 
-// The direct-to-LDS kernel applies: 16-byte aligned operand rows, at least two
+// The direct-to-LDS kernel applies: 4-byte aligned operands, at least two
 // whole slices of k, no 16-byte chunk of an MN-contiguous operand (A stored
 // K x M, B stored K x N) straddling M or N, and 32-bit slice offsets.
 template <class Cfg>
 bool sg_dma_ok(const GemmProblem &q)
 {
-    const bool aligned = (q.lda % 4 == 0) && (q.ldb % 4 == 0) && (q.strideA % 4 == 0) &&
-                         (q.strideB % 4 == 0) && (reinterpret_cast<uintptr_t>(q.A) % 16 == 0) &&
-                         (reinterpret_cast<uintptr_t>(q.B) % 16 == 0);
+    // 16-byte chunks start a multiple of four floats into a row, so they are
+    // dword aligned, which is all the 16-byte loads need
+    const bool aligned = (reinterpret_cast<uintptr_t>(q.A) % 4 == 0) && (reinterpret_cast<uintptr_t>(q.B) % 4 == 0);
     const bool shape = q.K >= 2 * Cfg::BK && (!q.transA || q.M % 4 == 0) && (q.transB || q.N % 4 == 0);
     // per-lane offsets within one slice are 32-bit: rows of the slice times ld
     const long long rows_a = q.transA ? Cfg::BK : Cfg::BM, rows_b = q.transB ? Cfg::BN : Cfg::BK;

@@ -65,14 +65,23 @@ def rows_of(dC, M, N, ldc, rows=None):
     return full.cpu().numpy()
 
 
+def to_dev_offset(buf, offset):
+    """``buf`` on the device starting ``offset`` elements into a fresh allocation
+    (offset 1 puts an fp32 array, offset 2 an fp16 one, 4 bytes past a 16-byte
+    boundary)."""
+    if offset == 0:
+        return to_dev(buf)
+    return to_dev(np.concatenate([np.zeros(offset, buf.dtype), buf]))[offset:]
+
+
 def run_and_check(kind, M, N, K, alpha, beta, *, kind_vals="pm1", lda=None, ldb=None, ldc=None,
-                  sample=None, exact=False, seed=42, c_nan=False, transA=False, transB=False):
+                  sample=None, exact=False, seed=42, c_nan=False, transA=False, transB=False, offset=0):
     in_dtype = np.float32 if kind == "f32" else np.float16
     note(f"{kind} M={M} N={N} K={K} alpha={alpha} beta={beta} vals={kind_vals} lda={lda} ldb={ldb} "
-         f"ldc={ldc} sample={sample} seed={seed} transA={int(transA)} transB={int(transB)}")
+         f"ldc={ldc} sample={sample} seed={seed} transA={int(transA)} transB={int(transB)} offset={offset}")
     p = si.gemm_problem(M, N, K, lda=lda, ldb=ldb, ldc=ldc, in_dtype=in_dtype, kind=kind_vals, seed=seed,
                         with_c=not c_nan, transA=transA, transB=transB)
-    dA, dB = to_dev(p["A"]), to_dev(p["B"])
+    dA, dB = to_dev_offset(p["A"], offset), to_dev_offset(p["B"], offset)
     if c_nan:   # beta = 0: C must be written without being read
         dC = torch.full((M * p["ldc"],), float("nan"), dtype=torch.float32, device="cuda")
     else:
@@ -363,14 +372,32 @@ def test_transposed_ragged(kind, tA, tB, M, N, K):
                   exact=True, transA=tA, transB=tB, seed=13)
 
 
-@pytest.mark.parametrize("tA,tB", OPS)
-def test_transposed_sgemm_register_kernel(tA, tB):
-    # >= 256 tiles of 128x128: ragged edges -> masked register kernel; whole tiles
-    # with K % 32 != 0 -> unmasked register kernel
-    run_and_check("f32", 2100, 2100, 100, 1.5, -0.5, sample=64, transA=tA, transB=tB)
-    run_and_check("f32", 2100, 2100, 100, 1.0, 1.0, sample=64, kind_vals="int4", exact=True, transA=tA,
+@pytest.mark.parametrize("tA,tB", [(False, False)] + OPS)
+def test_sgemm_register_kernel(tA, tB):
+    # >= 256 tiles of 128x128 that the direct-to-LDS kernel cannot take: K below
+    # two slices (ragged edges -> masked register kernel, whole tiles -> unmasked),
+    # or an MN-contiguous operand whose M or N is not a multiple of four
+    run_and_check("f32", 2100, 2100, 40, 1.5, -0.5, sample=64, transA=tA, transB=tB)
+    run_and_check("f32", 2100, 2100, 40, 1.0, 1.0, sample=64, kind_vals="int4", exact=True, transA=tA,
                   transB=tB, seed=5)
     run_and_check("f32", 2048, 2048, 48, 1.0, 0.0, sample=64, c_nan=True, transA=tA, transB=tB)
+    run_and_check("f32", 2050, 2046, 300, 1.5, -0.5, sample=64, transA=tA, transB=tB, seed=6)
+
+
+@pytest.mark.parametrize("tA,tB", [(False, False)] + OPS)
+def test_direct_to_lds_dword_aligned_rows(tA, tB):
+    # rows that start 4-byte but not 16-byte aligned (odd fp32 leading dimensions,
+    # fp16 ones of 2 or 6 mod 8, base pointers 4 bytes past a 16-byte boundary)
+    # still take the direct-to-LDS kernels: whole 256x256 tiles, then ragged tiles
+    for kind, pa, pb, off, ragged in [("f32", 1, 3, 1, (1000, 1000, 300)), ("f16", 2, 6, 2, (3000, 3000, 320))]:
+        M, N, K = 4096, 4096, 256
+        a_cols, b_cols = (M if tA else K), (K if tB else N)
+        run_and_check(kind, M, N, K, 1.5, -0.5, lda=a_cols + pa, ldb=b_cols + pb, ldc=N + 1, sample=64,
+                      transA=tA, transB=tB, offset=off)
+        M, N, K = ragged
+        a_cols, b_cols = (M if tA else K), (K if tB else N)
+        run_and_check(kind, M, N, K, 1.0, 1.0, lda=a_cols + pb, ldb=b_cols + pa, ldc=N + 2, sample=96,
+                      kind_vals="int4", exact=True, transA=tA, transB=tB, offset=off, seed=29)
 
 
 @pytest.mark.parametrize("kind", ["f32", "f16"])
@@ -475,6 +502,9 @@ def test_hgemm_ragged_direct_to_lds_rows_and_batch():
     run_and_check("f16", 1001, 1000, 500, 1.0, 0.0, c_nan=True, kind_vals="int4", exact=True, sample=64, seed=47)
     batched_check(200, 136, 304, 3, 1.5, -0.5)
     batched_check(200, 136, 304, 3, 1.0, 1.0, kind_vals="int4", exact=True, seed=53)
+    # leading dimensions and batch strides of 2 or 6 mod 8 halves (4-byte aligned rows)
+    batched_check(256, 264, 320, 3, 1.5, -0.5, pad=2)
+    batched_check(200, 136, 304, 3, 1.0, 1.0, kind_vals="int4", exact=True, pad=6, seed=59)
 
 
 @pytest.mark.parametrize("tA,tB", OPS)
