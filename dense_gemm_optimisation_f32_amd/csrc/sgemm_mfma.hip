@@ -240,9 +240,10 @@ __global__ __launch_bounds__(Cfg::NT) void sgemm_mfma_kernel(SgemmArgs p)
 
 // ---------------------------------------------------------------------------
 // Kernel fed by direct-to-LDS loads (global_load_lds_dwordx4: lane l's 16
-// bytes land at M0 + 16*l, no register staging, no LDS-write instructions).  Two LDS slots of BK = 32 k; slice t+2 is fetched while
-// slice t+1 waits and slice t is computed, which at fp32-MFMA speed (64
-// cycles per 32x32x2 op) leaves a whole slice of compute to hide the fetch.
+// bytes land at M0 + 16*l, no register staging, no LDS-write instructions).
+// Two LDS slots of BK = 32 k; slice t+2 is fetched while slice t+1 waits and
+// slice t is computed, which at fp32-MFMA speed (64 cycles per 32x32x2 op)
+// leaves a whole slice of compute to hide the fetch.
 //
 // Each operand slice is kept in LDS in its stored orientation:
 //   * K-contiguous (A stored M x K, B stored N x K): R rows (R = BM or BN) of
@@ -256,8 +257,9 @@ __global__ __launch_bounds__(Cfg::NT) void sgemm_mfma_kernel(SgemmArgs p)
 //     chunk at physical position p of row k holds logical chunk
 //     p ^ (8 * ((k >> 2) & 1)), which puts rows k and k+4 (read by the two
 //     half-waves of one MFMA operand) on different banks.  The operand of
-//     MFMA (u, e) is row 8u+e+4*(lane/32), column lane%32 -- one ds_read_b32
-//     per lane.
+//     MFMA (u, e) is row 8u+e+4*(lane/32), at the lane's column; where a wave
+//     has two or four blocks of that operand their columns interleave, so one
+//     8- or 16-byte read serves them all (see the kernel).
 // Either way lane l of MFMA (u, e) holds k = 8u + 4*(l/32) + e, so the op's k
 // pair is {8u+e, 8u+4+e} -- one fixed reordering of the sum over k for all
 // four storage combinations.
@@ -301,61 +303,54 @@ typedef __attribute__((address_space(3))) f32x4v lds_f32x4;
 typedef __attribute__((address_space(3))) f32x2v lds_f32x2;
 typedef __attribute__((address_space(3))) float lds_f32;
 
-// Per-lane byte offset (within one slice of global memory) of the 16-byte
-// chunk that lane `lane` of wave load g fetches for an operand slice of R rows
-// or columns; see the layouts above.  `lim` is how many of the R rows
-// (K-contiguous) or columns (MN-contiguous) lie inside M or N: a chunk past
-// it re-reads a valid one (row lim-1, or chunk 0 of its row), whose products
-// only reach C entries that are never stored.
-template <bool KC, int R, bool CLAMP>
-__device__ __forceinline__ unsigned sg_dma_offset(int g, int lane, long long ld, int lim)
-{
-    if (KC) {
-        const int r = 8 * g + (lane >> 3);
-        const int rr = (CLAMP && r >= lim) ? lim - 1 : r;
-        return (unsigned)(rr * ld + 4 * ((lane & 7) ^ sg_swz_a(r))) * 4u;
-    }
-    constexpr int CPR = R / 4, RPL = 256 / R;   // chunks per row, rows per wave load
-    const int k = RPL * g + lane / CPR;
-    int ch = (lane % CPR) ^ sg_swz_b(k);
-    if (CLAMP && 4 * ch >= lim) ch = 0;
-    return (unsigned)(k * ld + 4 * ch) * 4u;
-}
-
-// A slice load g splits into a uniform row part (bytes, added to the base
-// pointer) and a per-lane part.  The per-lane part depends on g only through
-// the chunk swizzle: g % 8 for a K-contiguous operand (rows 8g .. 8g+7), bit 2
-// of RPL*g for an MN-contiguous one (rows RPL*g .. RPL*g + RPL-1 share one
-// swizzle since RPL divides four).  Masked K-contiguous loads clamp their rows,
-// which depends on g, so they keep the whole offset in the per-lane part.
-template <bool KC, int R, bool MASK>
+// Byte offset (within one slice of global memory) of the 16-byte chunk that
+// lane `lane` of wave load g fetches for an operand slice of R rows or
+// columns (see the layouts above), split into a uniform row part, added to the
+// base pointer, and a per-lane part.  The per-lane part depends on g only
+// through the chunk swizzle: g % 8 for a K-contiguous operand (rows 8g ..
+// 8g+7), bit 2 of RPL*g for an MN-contiguous one (rows RPL*g .. RPL*g + RPL-1
+// share one swizzle since RPL divides four).
+//
+// MASK: `lim` is how many of the R rows (K-contiguous) or columns
+// (MN-contiguous) lie inside M or N, and a chunk past it re-reads a valid one
+// (row lim-1, or chunk 0 of its row), whose products only reach C entries that
+// are never stored.  A masked K-contiguous load whose rows reach lim takes its
+// whole clamped offset from sg_kc_clamped instead.
+template <bool KC, int R>
 __device__ __forceinline__ long long sg_row_part(int g, long long ld)
 {
-    if (KC) return MASK ? 0 : 32LL * g * ld;
-    return (long long)(256 / R) * g * ld * 4;
+    return KC ? 32LL * g * ld : (long long)(256 / R) * g * ld * 4;
 }
 
 template <bool KC, int R, bool MASK>
 __device__ __forceinline__ unsigned sg_lane_part(int g, int lane, long long ld, int lim)
 {
     if (KC) {
-        if (MASK) return sg_dma_offset<true, R, true>(g, lane, ld, lim);
-        const int l3 = lane >> 3;
-        return (unsigned)(l3 * ld + 4 * ((lane & 7) ^ l3 ^ (g & 7))) * 4u;
+        const int l3 = lane >> 3, ch = (lane & 7) ^ l3 ^ (g & 7);   // (r ^ r>>3) & 7 for r = 8g + l3
+        return (unsigned)(l3 * ld + 4 * ch) * 4u;
     }
-    constexpr int CPR = R / 4, RPL = 256 / R;
+    constexpr int CPR = R / 4, RPL = 256 / R;   // chunks per row, rows per wave load
     int ch = (lane % CPR) ^ sg_swz_b(RPL * g);
     if (MASK && 4 * ch >= lim) ch = 0;
     return (unsigned)((lane / CPR) * ld + 4 * ch) * 4u;
 }
 
+// Whole offset of K-contiguous load g with its rows clamped to `lim`: rows
+// past it re-read row lim-1.  The lane id is read afresh so that it need not
+// stay live across the K loop.
+__device__ __forceinline__ unsigned sg_kc_clamped(int g, long long ld, int lim)
+{
+    const int lane = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    const int l3 = lane >> 3, r = 8 * g + l3, ch = (lane & 7) ^ l3 ^ (g & 7);
+    return (unsigned)((r >= lim ? lim - 1 : r) * ld + 4 * ch) * 4u;
+}
+
 // How many distinct per-lane parts the loads g = lw + LW*i (i < LOADS) of one
 // loading wave have: the swizzle's period in g (8, or 8/RPL) divided by its gcd
 // with LW is the period in i.
-template <bool KC, bool MASK, int R, int LOADS, int LW>
+template <bool KC, int R, int LOADS, int LW>
 constexpr int sg_lane_parts()
 {
-    if (KC && MASK) return LOADS;
     const int per_g = KC ? 8 : 8 / (256 / R);
     int a = per_g, b = LW;
     while (b) {
@@ -402,28 +397,62 @@ __global__ __launch_bounds__(Cfg::NT) void sgemm_dma_kernel(SgemmArgs p)
     // neighbouring rows, and load g lands at byte 1024*g of the operand's part
     // of the slot.  Load i uses per-lane part i % P.
     constexpr int LW = Cfg::LW;
-    constexpr int PA = sg_lane_parts<A_KC, MASK, BM, Cfg::A_LOADS, LW>();
-    constexpr int PB = sg_lane_parts<B_KC, MASK, BN, Cfg::B_LOADS, LW>();
+    //
+    // Masked K-contiguous loads clamp rows past the edge.  The 256x256 tile has
+    // no registers to spare: it keeps the shared per-lane parts and computes a
+    // clamped offset at issue for the loads whose rows reach the edge (tested
+    // only in tiles that the edge crosses).  The smaller tiles keep one clamped
+    // offset per load and no test in the loop.
+    constexpr bool CLAMP_AT_ISSUE = BM * BN >= 256 * 256;
+    constexpr bool PER_LOAD_A = MASK && A_KC && !CLAMP_AT_ISSUE, PER_LOAD_B = MASK && B_KC && !CLAMP_AT_ISSUE;
+    constexpr int PA = PER_LOAD_A ? Cfg::A_LOADS : sg_lane_parts<A_KC, BM, Cfg::A_LOADS, LW>();
+    constexpr int PB = PER_LOAD_B ? Cfg::B_LOADS : sg_lane_parts<B_KC, BN, Cfg::B_LOADS, LW>();
     unsigned offA[PA], offB[PB];
 #pragma unroll
-    for (int d = 0; d < PA; ++d) offA[d] = sg_lane_part<A_KC, BM, MASK>(lw + LW * d, lane, lda, limA);
+    for (int d = 0; d < PA; ++d)
+        offA[d] = PER_LOAD_A ? sg_kc_clamped(lw + LW * d, lda, limA)
+                             : sg_lane_part<A_KC, BM, MASK>(lw + LW * d, lane, lda, limA);
 #pragma unroll
-    for (int d = 0; d < PB; ++d) offB[d] = sg_lane_part<B_KC, BN, MASK>(lw + LW * d, lane, ldb, limB);
+    for (int d = 0; d < PB; ++d)
+        offB[d] = PER_LOAD_B ? sg_kc_clamped(lw + LW * d, ldb, limB)
+                             : sg_lane_part<B_KC, BN, MASK>(lw + LW * d, lane, ldb, limB);
+    // one operand's loads of a slice: base pointer, per-lane offsets, rows or
+    // columns inside the tile, and the slot's LDS address for the operand
+    auto issue_operand = [&](auto kc, auto rr, auto per_load, auto nloads, auto np, const char *x,
+                             const unsigned *off, long long ld, int lim, unsigned dst) {
+        constexpr bool KC = decltype(kc)::value;
+        constexpr int R = decltype(rr)::value, NL = decltype(nloads)::value, NP = decltype(np)::value;
+        if constexpr (decltype(per_load)::value) {
+#pragma unroll
+            for (int i = 0; i < NL; ++i) sg_dma16(x, off[i], dst + 1024 * (lw + LW * i));
+        } else if (MASK && KC && lim < R) {   // an edge tile (wave-uniform): test each load
+#pragma unroll
+            for (int i = 0; i < NL; ++i) {
+                const int g = lw + LW * i;
+                if (8 * g + 8 > lim)
+                    sg_dma16(x, sg_kc_clamped(g, ld, lim), dst + 1024 * g);
+                else
+                    sg_dma16(x + sg_row_part<KC, R>(g, ld), off[i % NP], dst + 1024 * g);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < NL; ++i) {
+                const int g = lw + LW * i;
+                sg_dma16(x + sg_row_part<KC, R>(g, ld), off[i % NP], dst + 1024 * g);
+            }
+        }
+    };
     auto issue_slice = [&](int kt, int slot) {
         if (!loader) return;
         const char *a = Ab + (long long)kt * stepA;
         const char *b = Bb + (long long)kt * stepB;
         const unsigned sa = lds0 + slot * Cfg::SLOT_BYTES, sb = sa + Cfg::A_BYTES;
-#pragma unroll
-        for (int i = 0; i < Cfg::A_LOADS; ++i) {
-            const int g = lw + LW * i;
-            sg_dma16(a + sg_row_part<A_KC, BM, MASK>(g, lda), offA[i % PA], sa + 1024 * g);
-        }
-#pragma unroll
-        for (int i = 0; i < Cfg::B_LOADS; ++i) {
-            const int g = lw + LW * i;
-            sg_dma16(b + sg_row_part<B_KC, BN, MASK>(g, ldb), offB[i % PB], sb + 1024 * g);
-        }
+        issue_operand(std::bool_constant<A_KC>{}, std::integral_constant<int, BM>{},
+                      std::bool_constant<PER_LOAD_A>{}, std::integral_constant<int, Cfg::A_LOADS>{},
+                      std::integral_constant<int, PA>{}, a, offA, lda, limA, sa);
+        issue_operand(std::bool_constant<B_KC>{}, std::integral_constant<int, BN>{},
+                      std::bool_constant<PER_LOAD_B>{}, std::integral_constant<int, Cfg::B_LOADS>{},
+                      std::integral_constant<int, PB>{}, b, offB, ldb, limB, sb);
     };
 
     const int wm = uwave / Cfg::WN, wn = uwave % Cfg::WN;
