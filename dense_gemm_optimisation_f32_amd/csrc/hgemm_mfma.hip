@@ -593,7 +593,13 @@ __global__ __launch_bounds__(Cfg::NT) void hgemm_dma_kernel(HgemmArgs p)
         }
     };
 
-    const int nk = p.K / BK;   // whole slices, >= S (checked by the launcher)
+    // An MN-contiguous operand whose M or N is not a multiple of eight has a
+    // chunk that straddles that edge.  Its halves past the edge only reach C
+    // entries that are never stored, and in any row but the matrix's last they
+    // lie in the next row.  The slices then stop before row K-1 and the K tail
+    // below takes the rest, so no slice load reads past the operand.
+    const bool straddle = MASK && ((!A_KC && p.M % 8 != 0) || (!B_KC && p.N % 8 != 0));
+    const int nk = (p.K - (straddle ? 1 : 0)) / BK;   // whole slices, >= S (checked by the launcher)
     // Prologue: slices 0..S-1 in flight; slice 0 resident; substep 0 fragments read.
 #pragma unroll
     for (int st = 0; st < S; ++st) issue_slice(st, st);
@@ -742,8 +748,9 @@ using HgDma256 = HgDmaCfg<256, 256, 2, 2, 4, 64>;
 using HgDma128 = HgDmaCfg<128, 128, 4, 2, 4, 64>;
 
 // The direct-to-LDS kernel applies: 4-byte aligned operand rows, at least
-// STAGES whole slices of k, no 16-byte chunk of an MN-contiguous operand
-// (A stored K x M, B stored K x N) straddling M or N, and 32-bit slice offsets.
+// STAGES whole slices of k, an MN-contiguous operand (A stored K x M, B stored
+// K x N) at least eight wide where M or N is not a multiple of eight, and
+// 32-bit slice offsets.
 template <class Cfg>
 bool dma_ok(const GemmProblem &q)
 {
@@ -752,7 +759,11 @@ bool dma_ok(const GemmProblem &q)
     const bool aligned = (q.lda % 2 == 0) && (q.ldb % 2 == 0) && (q.strideA % 2 == 0) &&
                          (q.strideB % 2 == 0) && (reinterpret_cast<uintptr_t>(q.A) % 4 == 0) &&
                          (reinterpret_cast<uintptr_t>(q.B) % 4 == 0);
-    const bool shape = q.K >= Cfg::BK * Cfg::STAGES && (!q.transA || q.M % 8 == 0) && (q.transB || q.N % 8 == 0);
+    // a chunk straddling M or N (see the kernel) needs M or N >= 8, so that its
+    // overflow stays in the next row, and one row of K left to the tail
+    const bool straddle = (q.transA && q.M % 8 != 0) || (!q.transB && q.N % 8 != 0);
+    const bool shape = q.K - (straddle ? 1 : 0) >= Cfg::BK * Cfg::STAGES && (!q.transA || q.M % 8 == 0 || q.M >= 8) &&
+                       (q.transB || q.N % 8 == 0 || q.N >= 8);
     // per-lane offsets within one slice are 32-bit: rows of the slice times ld
     const long long rows_a = q.transA ? Cfg::BK : Cfg::BM, rows_b = q.transB ? Cfg::BN : Cfg::BK;
     const bool fits = rows_a * q.lda * 2 < (1LL << 31) && rows_b * q.ldb * 2 < (1LL << 31);

@@ -613,7 +613,13 @@ __global__ __launch_bounds__(Cfg::NT) void sgemm_dma_kernel(SgemmArgs p)
         }
     };
 
-    const int nk = p.K / BK;   // whole slices, >= 2 (checked by the launcher)
+    // An MN-contiguous operand whose M or N is not a multiple of four has a
+    // chunk that straddles that edge.  Its floats past the edge only reach C
+    // entries that are never stored, and in any row but the matrix's last they
+    // lie in the next row.  The slices then stop before row K-1 and the K tail
+    // below takes the rest, so no slice load reads past the operand.
+    const bool straddle = MASK && ((!A_KC && p.M % 4 != 0) || (!B_KC && p.N % 4 != 0));
+    const int nk = (p.K - (straddle ? 1 : 0)) / BK;   // whole slices, >= 2 (checked by the launcher)
     issue_slice(0, 0);
     issue_slice(1, 1);
     __builtin_amdgcn_s_waitcnt((LOADS & 15) | ((LOADS >> 4) << 14) | (7 << 4) | (15 << 8));   // slice 0 done
@@ -731,15 +737,20 @@ using SgDma128 = SgDmaCfg<128, 128, 2, 4>;
 using SgDma64 = SgDmaCfg<64, 64, 2, 2>;
 
 // The direct-to-LDS kernel applies: 4-byte aligned operands, at least two
-// whole slices of k, no 16-byte chunk of an MN-contiguous operand (A stored
-// K x M, B stored K x N) straddling M or N, and 32-bit slice offsets.
+// whole slices of k, an MN-contiguous operand (A stored K x M, B stored K x N)
+// at least eight wide where M or N is not a multiple of four, and 32-bit slice
+// offsets.
 template <class Cfg>
 bool sg_dma_ok(const GemmProblem &q)
 {
     // 16-byte chunks start a multiple of four floats into a row, so they are
     // dword aligned, which is all the 16-byte loads need
     const bool aligned = (reinterpret_cast<uintptr_t>(q.A) % 4 == 0) && (reinterpret_cast<uintptr_t>(q.B) % 4 == 0);
-    const bool shape = q.K >= 2 * Cfg::BK && (!q.transA || q.M % 4 == 0) && (q.transB || q.N % 4 == 0);
+    // a chunk straddling M or N (see the kernel) needs M or N >= 8, so that its
+    // overflow stays in the next row, and one row of K left to the tail
+    const bool straddle = (q.transA && q.M % 4 != 0) || (!q.transB && q.N % 4 != 0);
+    const bool shape = q.K - (straddle ? 1 : 0) >= 2 * Cfg::BK && (!q.transA || q.M % 4 == 0 || q.M >= 8) &&
+                       (q.transB || q.N % 4 == 0 || q.N >= 8);
     // per-lane offsets within one slice are 32-bit: rows of the slice times ld
     const long long rows_a = q.transA ? Cfg::BK : Cfg::BM, rows_b = q.transB ? Cfg::BN : Cfg::BK;
     const bool fits = rows_a * q.lda * 4 < (1LL << 31) && rows_b * q.ldb * 4 < (1LL << 31);
@@ -1029,20 +1040,31 @@ hipError_t launch_cfg(const GemmProblem &q, hipStream_t stream)
 
 hipError_t launch_sgemm(const GemmProblem &q, hipStream_t stream)
 {
-    // Direct-to-LDS tiles: 256x256 when that still gives one tile per CU,
-    // else 128x128, else 64x64 while those fill the CUs; the split-K kernel
-    // for smaller grids; register-staged 128x128 tiles with bounds checks for
-    // operands the direct-to-LDS kernel cannot take.
+    // Direct-to-LDS tiles: 256x256 or 128x128 (cost model below), else 64x64
+    // while those fill the CUs; the split-K kernel for smaller grids;
+    // register-staged 128x128 tiles with bounds checks for operands the
+    // direct-to-LDS kernel cannot take.
+    //
+    // A 256x256 tile takes a CU's whole LDS, so a grid of them runs in rounds
+    // of 256 work-groups.  128x128 tiles run two per CU and spread evenly; 1024
+    // of them take about 1.05 rounds of 256x256 tiles (measured).  So the
+    // 256x256 tile wins when 1024 * its rounds <= 1.05 * the 128x128 tiles.
+    //
+    // With exactly one round of 64x64 tiles and A stored K x M, the split-K
+    // kernel beats the 64x64 direct-to-LDS tile, whose 32x32 wave tiles read an
+    // MN-contiguous A with 4-byte LDS reads (measured at 1024^3).
     const long long t256 = (long long)((q.M + 255) / 256) * ((q.N + 255) / 256) * q.batch;
     const long long t128 = (long long)((q.M + 127) / 128) * ((q.N + 127) / 128) * q.batch;
     const long long t64 = (long long)((q.M + 63) / 64) * ((q.N + 63) / 64) * q.batch;
-    if (t128 < 256 && t64 >= 256 && sg_dma_ok<SgDma64>(q)) return launch_sg_dma<SgDma64>(q, stream);
+    if (t128 < 256 && t64 >= 256 && !(q.transA && t64 <= 256) && sg_dma_ok<SgDma64>(q))
+        return launch_sg_dma<SgDma64>(q, stream);
     if (t128 < 256) {
         // fewer 128x128 tiles than CUs: split K inside smaller workgroup tiles
         if (t64 >= 256) return launch_small<SgSmall64>(q, stream);
         return launch_small<SgSmall32>(q, stream);
     }
-    if (t256 >= 256 && sg_dma_ok<SgDma256>(q)) return launch_sg_dma<SgDma256>(q, stream);
+    const long long r256 = (t256 + 255) / 256;
+    if (20 * 1024 * r256 <= 21 * t128 && sg_dma_ok<SgDma256>(q)) return launch_sg_dma<SgDma256>(q, stream);
     if (sg_dma_ok<SgDma128>(q)) return launch_sg_dma<SgDma128>(q, stream);
     return launch_cfg<SgBig>(q, stream);
 }

@@ -374,14 +374,30 @@ def test_transposed_ragged(kind, tA, tB, M, N, K):
 
 @pytest.mark.parametrize("tA,tB", [(False, False)] + OPS)
 def test_sgemm_register_kernel(tA, tB):
-    # >= 256 tiles of 128x128 that the direct-to-LDS kernel cannot take: K below
-    # two slices (ragged edges -> masked register kernel, whole tiles -> unmasked),
-    # or an MN-contiguous operand whose M or N is not a multiple of four
+    # >= 256 tiles of 128x128 with K below two slices, which the direct-to-LDS
+    # kernel cannot take (ragged edges -> masked register kernel, whole tiles ->
+    # unmasked)
     run_and_check("f32", 2100, 2100, 40, 1.5, -0.5, sample=64, transA=tA, transB=tB)
     run_and_check("f32", 2100, 2100, 40, 1.0, 1.0, sample=64, kind_vals="int4", exact=True, transA=tA,
                   transB=tB, seed=5)
     run_and_check("f32", 2048, 2048, 48, 1.0, 0.0, sample=64, c_nan=True, transA=tA, transB=tB)
-    run_and_check("f32", 2050, 2046, 300, 1.5, -0.5, sample=64, transA=tA, transB=tB, seed=6)
+
+
+@pytest.mark.parametrize("kind", ["f32", "f16"])
+@pytest.mark.parametrize("tA,tB", [(False, False)] + OPS)
+def test_direct_to_lds_straddling_chunks(kind, tA, tB):
+    # an MN-contiguous operand whose M or N is not a multiple of the 16-byte
+    # chunk (4 floats, 8 halves): the direct-to-LDS slices stop before row K-1
+    # and the K tail takes up to a whole slice; int4 runs prove that no element
+    # comes from the wrong place
+    if kind == "f32":
+        cases = [(2050, 2046, 300), (1001, 1003, 1024), (4095, 4093, 256), (1002, 998, 65)]
+    else:
+        cases = [(1500, 1500, 1536), (2050, 2046, 320), (1001, 1003, 1024), (4100, 4092, 512), (1500, 1500, 257)]
+    for idx, (M, N, K) in enumerate(cases):
+        run_and_check(kind, M, N, K, 1.5, -0.5, ldc=N + 1, sample=48, transA=tA, transB=tB, seed=61 + idx)
+        run_and_check(kind, M, N, K, 1.0, 1.0, sample=48, kind_vals="int4", exact=True, transA=tA, transB=tB,
+                      seed=71 + idx)
 
 
 @pytest.mark.parametrize("tA,tB", [(False, False)] + OPS)
@@ -442,11 +458,12 @@ def _ld4(cols, pad):
 
 @pytest.mark.parametrize("tA,tB", [(False, False)] + OPS)
 @pytest.mark.parametrize("M,N,K", [(1000, 1000, 1000), (1000, 1000, 64), (996, 1204, 2000), (2052, 2100, 333),
-                                   (4100, 4100, 95), (4000, 4000, 1024)])
+                                   (4000, 4000, 95), (4000, 4000, 1024)])
 def test_sgemm_ragged_direct_to_lds(M, N, K, tA, tB):
     # M, N not multiples of the tile and K not of 32, 16-byte aligned rows: the
     # direct-to-LDS kernels with clamped loads, the K tail from global memory and
-    # masked stores (64x64 tiles up to 1000^2, 128x128 at 2052x2100, 256x256 above)
+    # masked stores (64x64 tiles up to 1000^2, 128x128 at 2052x2100, 256x256 at
+    # 4000^2, one round of 256 such tiles)
     a_cols, b_cols = (M if tA else K), (K if tB else N)
     sample = 64 if M * N > 2_000_000 else 128
     run_and_check("f32", M, N, K, 1.5, -0.5, lda=_ld4(a_cols, 4), ldb=_ld4(b_cols, 8), ldc=N + 3, sample=sample,
@@ -505,6 +522,9 @@ def test_hgemm_ragged_direct_to_lds_rows_and_batch():
     # leading dimensions and batch strides of 2 or 6 mod 8 halves (4-byte aligned rows)
     batched_check(256, 264, 320, 3, 1.5, -0.5, pad=2)
     batched_check(200, 136, 304, 3, 1.0, 1.0, kind_vals="int4", exact=True, pad=6, seed=59)
+    # N not a multiple of eight (a chunk of B straddles N), the last member ending the buffer
+    batched_check(200, 140, 320, 3, 1.0, 1.0, kind_vals="int4", exact=True, seed=67)
+    batched_check(200, 140, 320, 3, 1.5, -0.5, pad=2, seed=68)
 
 
 @pytest.mark.parametrize("tA,tB", OPS)
