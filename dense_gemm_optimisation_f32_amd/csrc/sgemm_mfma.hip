@@ -263,10 +263,16 @@ __global__ __launch_bounds__(Cfg::NT) void sgemm_mfma_kernel(SgemmArgs p)
 // Either way lane l of MFMA (u, e) holds k = 8u + 4*(l/32) + e, so the op's k
 // pair is {8u+e, 8u+4+e} -- one fixed reordering of the sum over k for all
 // four storage combinations.
-template <int BM_, int BN_, int WM_, int WN_>
+// KS > 1: KS groups of WM x WN waves split each slice's eight-k steps (group
+// ks takes steps ks, ks + KS, ...) and their partial tiles are summed at the end.
+template <int BM_, int BN_, int WM_, int WN_, int KS_ = 1>
 struct SgDmaCfg {
-    static constexpr int BM = BM_, BN = BN_, BK = 32, WM = WM_, WN = WN_, SLOTS = 2;
-    static constexpr int NW = WM * WN, NT = 64 * NW;
+    static constexpr int BM = BM_, BN = BN_, BK = 32, WM = WM_, WN = WN_, KS = KS_, SLOTS = 2;
+    static constexpr int NW = WM * WN * KS, NT = 64 * NW;
+    // Waves per SIMD the register budget must allow: the 64x64 tile's grids can
+    // hold two work-groups per CU, which its masked instantiations would
+    // otherwise exceed (142 VGPRs against 126 with the bound, no spills)
+    static constexpr int WPE = BM * BN <= 64 * 64 ? 4 : 1;
     static constexpr int TM = BM / WM, TN = BN / WN;
     static constexpr int FM = TM / 32, FN = TN / 32;
     static constexpr int A_BYTES = BM * BK * 4;
@@ -280,6 +286,11 @@ struct SgDmaCfg {
     static_assert(A_BYTES % (1024 * LW) == 0 && B_BYTES % (1024 * LW) == 0, "slices must split over the loaders");
     static_assert(BM >= 64 && BN >= 64, "MN-contiguous slices need at least 16 chunks per row");
     static_assert(SLOTS * SLOT_BYTES <= 160 * 1024, "LDS slots too large");
+    static_assert((BK / 8) % KS == 0 && (KS & (KS - 1)) == 0, "K groups must split the slice's steps");
+    // the partial tiles of groups 1 .. KS-1 pass through the LDS of the ring
+    static constexpr int PART_BYTES = (KS - 1) * WM * WN * FM * FN * 16 * 64 * 4;
+    static constexpr int LDS_BYTES = SLOTS * SLOT_BYTES > PART_BYTES ? SLOTS * SLOT_BYTES : PART_BYTES;
+    static_assert(LDS_BYTES <= 160 * 1024, "partial tiles exceed the LDS");
 };
 
 __device__ __forceinline__ int sg_swz_a(int r) { return (r ^ (r >> 3)) & 7; }
@@ -367,11 +378,11 @@ constexpr int sg_lane_parts()
 // slice, and stores outside C are skipped); an MN-contiguous operand then
 // needs its M or N to be a multiple of four, so no 16-byte chunk straddles it.
 template <class Cfg, bool TA, bool TB, bool MASK>
-__global__ __launch_bounds__(Cfg::NT) void sgemm_dma_kernel(SgemmArgs p)
+__global__ __launch_bounds__(Cfg::NT) __attribute__((amdgpu_waves_per_eu(Cfg::WPE))) void sgemm_dma_kernel(SgemmArgs p)
 {
     constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK;
     constexpr bool A_KC = !TA, B_KC = TB;
-    __shared__ __attribute__((aligned(1024))) unsigned char lds[Cfg::SLOTS * Cfg::SLOT_BYTES];
+    __shared__ __attribute__((aligned(1024))) unsigned char lds[Cfg::LDS_BYTES];
     const unsigned lds0 = (unsigned)(uintptr_t)lds;
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -455,7 +466,11 @@ __global__ __launch_bounds__(Cfg::NT) void sgemm_dma_kernel(SgemmArgs p)
                       std::integral_constant<int, PB>{}, b, offB, ldb, limB, sb);
     };
 
-    const int wm = uwave / Cfg::WN, wn = uwave % Cfg::WN;
+    // Wave uwave owns part mn = uwave % (WM*WN) of the tile and, in K group
+    // ks = uwave / (WM*WN), the eight-k steps ks, ks + KS, ... of every slice.
+    constexpr int KS = Cfg::KS;
+    const int mn = uwave % (Cfg::WM * Cfg::WN), ks = uwave / (Cfg::WM * Cfg::WN);
+    const int wm = mn / Cfg::WN, wn = mn % Cfg::WN;
     const int lr = lane & 31, lk = lane >> 5;
     // Rows of the wave's A blocks.  With a K-contiguous A, block i holds rows
     // 32i .. 32i+31 of the wave tile.  With an MN-contiguous A, the rows of
@@ -476,16 +491,18 @@ __global__ __launch_bounds__(Cfg::NT) void sgemm_dma_kernel(SgemmArgs p)
     // the lane part of its chunk index (logical chunk 2u+lk).  MN-contiguous:
     // row 4*lk (plus 8u+e), logical chunk m/4 of the lane's first m, physical
     // chunk flipped by 8 when lk = 1 (for A, one address per group of IA blocks).
+    // The wave's first step ks is folded in: step u = ks + KS*j adds 2*ks to
+    // the chunk index (no carry, as KS is a power of two) and 8*ks rows.
     unsigned rowA[Cfg::FM], tA[Cfg::FM], rowB[Cfg::FN], tB[Cfg::FN];
 #pragma unroll
     for (int i = 0; i < Cfg::FM; ++i) {
         const int r = arow(i, lr);
         if (A_KC) {
             rowA[i] = (unsigned)(r * BK * 4);
-            tA[i] = (unsigned)(lk ^ sg_swz_a(r));
+            tA[i] = (unsigned)(lk ^ sg_swz_a(r) ^ (2 * ks));
         } else {
             const int q = r >> 2;
-            rowA[i] = (unsigned)(4 * lk * BM * 4 + 16 * (q ^ (8 * lk)) + 4 * (r & 3));
+            rowA[i] = (unsigned)((4 * lk + 8 * ks) * BM * 4 + 16 * (q ^ (8 * lk)) + 4 * (r & 3));
             tA[i] = 0;
         }
     }
@@ -494,10 +511,10 @@ __global__ __launch_bounds__(Cfg::NT) void sgemm_dma_kernel(SgemmArgs p)
         const int c = bcol(j, lr);
         if (B_KC) {
             rowB[j] = (unsigned)(Cfg::A_BYTES + c * BK * 4);
-            tB[j] = (unsigned)(lk ^ sg_swz_a(c));
+            tB[j] = (unsigned)(lk ^ sg_swz_a(c) ^ (2 * ks));
         } else {
             const int q = c >> 2;
-            rowB[j] = (unsigned)(Cfg::A_BYTES + 4 * lk * BN * 4 + 16 * (q ^ (8 * lk)) + 4 * (c & 3));
+            rowB[j] = (unsigned)(Cfg::A_BYTES + (4 * lk + 8 * ks) * BN * 4 + 16 * (q ^ (8 * lk)) + 4 * (c & 3));
             tB[j] = 0;
         }
     }
@@ -510,11 +527,13 @@ __global__ __launch_bounds__(Cfg::NT) void sgemm_dma_kernel(SgemmArgs p)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    // Operand fragments of one eight-k step u: element e of fa[i] / fb[j] is the
-    // operand of MFMA (u, e) for block i / j.  A K-contiguous fragment is one
+    // Operand fragments of the wave's j-th eight-k step of a slice (step
+    // u = ks + KS*j): element e of fa[i] / fb[j] is the operand of MFMA (u, e)
+    // for block i / j.  A K-contiguous fragment is one
     // 16-byte read; an MN-contiguous B fragment is four 4-byte reads, and an
     // MN-contiguous A group of IA blocks four reads of IA floats.
-    auto read_frags = [&](int slot, int u, f32x4v *fa, f32x4v *fb) {
+    auto read_frags = [&](int slot, int jstep, f32x4v *fa, f32x4v *fb) {
+        const int u = KS * jstep;   // the ks part is in rowA/tA, rowB/tB
         const unsigned base = lds0 + slot * Cfg::SLOT_BYTES;
         if constexpr (A_KC) {
 #pragma unroll
@@ -592,14 +611,17 @@ __global__ __launch_bounds__(Cfg::NT) void sgemm_dma_kernel(SgemmArgs p)
     // landed for every wave (own loads drained, then the barrier) and every
     // wave holds its slice-t fragments, the slot of slice t is refilled with
     // slice t+2 and the first fragments of slice t+1 are read.
-    constexpr int NU = BK / 8;
+    constexpr int NU = BK / 8, NUW = NU / KS;   // steps per slice, per wave
+    // With an odd step count per slice the buffers alternate from slice to
+    // slice: slice t starts in buffer (t * NUW) & 1, passed as PAR.
     f32x4v fa[2][Cfg::FM], fb[2][Cfg::FN];
-    auto step = [&](int t, auto refill) {
+    auto step = [&](int t, auto refill, auto par) {
+        constexpr int PAR = decltype(par)::value;
         const int slot = t & 1;
 #pragma unroll
-        for (int u = 0; u < NU; ++u) {
-            const int cur = u & 1, nxt = cur ^ 1;
-            if (u + 1 < NU) {
+        for (int u = 0; u < NUW; ++u) {
+            const int cur = (u + PAR) & 1, nxt = cur ^ 1;
+            if (u + 1 < NUW) {
                 read_frags(slot, u + 1, fa[nxt], fb[nxt]);
             } else {
                 __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): slice t+1 done for this lane
@@ -620,20 +642,41 @@ __global__ __launch_bounds__(Cfg::NT) void sgemm_dma_kernel(SgemmArgs p)
     // below takes the rest, so no slice load reads past the operand.
     const bool straddle = MASK && ((!A_KC && p.M % 4 != 0) || (!B_KC && p.N % 4 != 0));
     const int nk = (p.K - (straddle ? 1 : 0)) / BK;   // whole slices, >= 2 (checked by the launcher)
+    // the last slice: resident, nothing left to fetch
+    auto last_slice = [&](auto par) {
+        constexpr int PAR = decltype(par)::value;
+        const int slot = (nk - 1) & 1;
+#pragma unroll
+        for (int u = 0; u < NUW; ++u) {
+            const int cur = (u + PAR) & 1, nxt = cur ^ 1;
+            if (u + 1 < NUW) read_frags(slot, u + 1, fa[nxt], fb[nxt]);
+            mfmas(fa[cur], fb[cur]);
+        }
+    };
     issue_slice(0, 0);
     issue_slice(1, 1);
     __builtin_amdgcn_s_waitcnt((LOADS & 15) | ((LOADS >> 4) << 14) | (7 << 4) | (15 << 8));   // slice 0 done
     lds_barrier();
     read_frags(0, 0, fa[0], fb[0]);
-    for (int t = 0; t + 2 < nk; ++t) step(t, std::true_type{});
-    step(nk - 2, std::false_type{});
-    {   // last slice: resident, nothing left to fetch
-        const int slot = (nk - 1) & 1;
-#pragma unroll
-        for (int u = 0; u < NU; ++u) {
-            const int cur = u & 1, nxt = cur ^ 1;
-            if (u + 1 < NU) read_frags(slot, u + 1, fa[nxt], fb[nxt]);
-            mfmas(fa[cur], fb[cur]);
+    using P0 = std::integral_constant<int, 0>;
+    using P1 = std::integral_constant<int, 1>;
+    if constexpr (NUW % 2 == 0) {
+        for (int t = 0; t + 2 < nk; ++t) step(t, std::true_type{}, P0{});
+        step(nk - 2, std::false_type{}, P0{});
+        last_slice(P0{});
+    } else {   // slices in pairs, so that each call knows its buffer
+        int t = 0;
+        for (; t + 3 < nk; t += 2) {
+            step(t, std::true_type{}, P0{});
+            step(t + 1, std::true_type{}, P1{});
+        }
+        if (t + 3 == nk) {
+            step(t, std::true_type{}, P0{});
+            step(t + 1, std::false_type{}, P1{});
+            last_slice(P0{});
+        } else {
+            step(t, std::false_type{}, P0{});
+            last_slice(P1{});
         }
     }
     // The tail and the epilogue take the lane's row and k half from a lane id
@@ -673,7 +716,8 @@ __global__ __launch_bounds__(Cfg::NT) void sgemm_dma_kernel(SgemmArgs p)
                 return v;
             };
 #pragma unroll
-            for (int u = 0; u < NU; ++u) {
+            for (int jstep = 0; jstep < NUW; ++jstep) {
+                const int u = ks + KS * jstep;   // this wave's steps, as in the slices
                 if (k0 + 8 * u >= K) break;
                 const int kq = k0 + 8 * u + 4 * elk;   // this lane's quad
                 f32x4v qa[Cfg::FM], qb[Cfg::FN];
@@ -686,6 +730,35 @@ __global__ __launch_bounds__(Cfg::NT) void sgemm_dma_kernel(SgemmArgs p)
                 mfmas(qa, qb);
             }
         }
+    }
+
+    if constexpr (KS > 1) {
+        // Groups 1 .. KS-1 hand their partial tiles to group 0 through the LDS
+        // of the ring, which no wave reads any more; group 0 adds them in group order
+        // (a fixed order, so results are deterministic) and runs the epilogue.
+        constexpr int PART = Cfg::WM * Cfg::WN * Cfg::FM * Cfg::FN * 16 * 64;   // floats per group
+        lds_barrier();
+        lds_f32 *part = (lds_f32 *)(uintptr_t)lds0;
+        if (ks > 0) {
+#pragma unroll
+            for (int i = 0; i < Cfg::FM; ++i)
+#pragma unroll
+                for (int j = 0; j < Cfg::FN; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        part[(ks - 1) * PART + (((mn * Cfg::FM + i) * Cfg::FN + j) * 16 + r) * 64 + elane] = acc[i][j][r];
+        }
+        lds_barrier();
+        if (ks > 0) return;
+#pragma unroll
+        for (int g = 1; g < KS; ++g)
+#pragma unroll
+            for (int i = 0; i < Cfg::FM; ++i)
+#pragma unroll
+                for (int j = 0; j < Cfg::FN; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        acc[i][j][r] += part[(g - 1) * PART + (((mn * Cfg::FM + i) * Cfg::FN + j) * 16 + r) * 64 + elane];
     }
 
     const float alpha = p.alpha, beta = p.beta;
@@ -730,11 +803,13 @@ __global__ __launch_bounds__(Cfg::NT) void sgemm_dma_kernel(SgemmArgs p)
 
 // Eight waves, two per SIMD (one wave's MFMAs cover the other's LDS and barrier
 // latency): 256x256 tiles as 2 x 4 waves of 128x64, 128x128 tiles as 2 x 4 of
-// 64x32.  64x64 tiles (four waves of 32x32) serve grids that 128x128 tiles
-// would leave under-filled.
+// 64x32.  64x64 tiles serve grids that 128x128 tiles would leave under-filled:
+// four K groups of 2 x 1 waves of 32x64, each group taking one eight-k step of
+// every slice, so that each SIMD runs two waves with two accumulator chains
+// each, and an MN-contiguous B is read for both blocks at once.
 using SgDma256 = SgDmaCfg<256, 256, 2, 4>;
 using SgDma128 = SgDmaCfg<128, 128, 2, 4>;
-using SgDma64 = SgDmaCfg<64, 64, 2, 2>;
+using SgDma64 = SgDmaCfg<64, 64, 2, 1, 4>;
 
 // The direct-to-LDS kernel applies: 4-byte aligned operands, at least two
 // whole slices of k, an MN-contiguous operand (A stored K x M, B stored K x N)
@@ -1050,14 +1125,10 @@ hipError_t launch_sgemm(const GemmProblem &q, hipStream_t stream)
     // of them take about 1.05 rounds of 256x256 tiles (measured).  So the
     // 256x256 tile wins when 1024 * its rounds <= 1.05 * the 128x128 tiles.
     //
-    // With exactly one round of 64x64 tiles and A stored K x M, the split-K
-    // kernel beats the 64x64 direct-to-LDS tile, whose 32x32 wave tiles read an
-    // MN-contiguous A with 4-byte LDS reads (measured at 1024^3).
     const long long t256 = (long long)((q.M + 255) / 256) * ((q.N + 255) / 256) * q.batch;
     const long long t128 = (long long)((q.M + 127) / 128) * ((q.N + 127) / 128) * q.batch;
     const long long t64 = (long long)((q.M + 63) / 64) * ((q.N + 63) / 64) * q.batch;
-    if (t128 < 256 && t64 >= 256 && !(q.transA && t64 <= 256) && sg_dma_ok<SgDma64>(q))
-        return launch_sg_dma<SgDma64>(q, stream);
+    if (t128 < 256 && t64 >= 256 && sg_dma_ok<SgDma64>(q)) return launch_sg_dma<SgDma64>(q, stream);
     if (t128 < 256) {
         // fewer 128x128 tiles than CUs: split K inside smaller workgroup tiles
         if (t64 >= 256) return launch_small<SgSmall64>(q, stream);
