@@ -442,8 +442,12 @@ def test_transposed_fast_paths(kind, tA, tB):
 @pytest.mark.parametrize("tA,tB", [(False, False)] + OPS)
 def test_sgemm_64_tiles_direct_to_lds(tA, tB):
     # fewer than 256 tiles of 128x128 but at least 256 whole 64x64 tiles: the
-    # four-wave 64x64 direct-to-LDS kernel (K = 64 is its shortest ring)
-    for M, N, K in [(1024, 1024, 64), (1024, 2048, 416)]:
+    # 64x64 direct-to-LDS kernel, whose four K groups take one eight-k step of
+    # each slice and run the slices in pairs.  K = 64, 96, 128, 160 give two to
+    # five slices (both pair endings); 120 and 136 add tails of three steps and
+    # of one, split over the groups; 416 is a longer even run.
+    for M, N, K in [(1024, 1024, 64), (1024, 1024, 96), (1024, 1024, 128), (1024, 1024, 160),
+                    (1024, 1024, 120), (1024, 1024, 136), (1024, 2048, 416)]:
         a_cols, b_cols = (M if tA else K), (K if tB else N)
         run_and_check("f32", M, N, K, 1.5, -0.5, lda=a_cols + 4, ldb=b_cols + 12, ldc=N + 3, sample=128,
                       transA=tA, transB=tB)
