@@ -1116,7 +1116,9 @@ hipError_t launch_cfg(const GemmProblem &q, hipStream_t stream)
 hipError_t launch_sgemm(const GemmProblem &q, hipStream_t stream)
 {
     // Direct-to-LDS tiles: 256x256 or 128x128 (cost model below), else 64x64
-    // while those fill the CUs; the split-K kernel for smaller grids;
+    // while those fill at least five eighths of the CUs (below that the
+    // split-K kernel's eight-way K split wins: measured crossover between 144
+    // and 196 tiles); the split-K kernel for smaller grids;
     // register-staged 128x128 tiles with bounds checks for operands the
     // direct-to-LDS kernel cannot take.
     //
@@ -1124,11 +1126,10 @@ hipError_t launch_sgemm(const GemmProblem &q, hipStream_t stream)
     // of 256 work-groups.  128x128 tiles run two per CU and spread evenly; 1024
     // of them take about 1.05 rounds of 256x256 tiles (measured).  So the
     // 256x256 tile wins when 1024 * its rounds <= 1.05 * the 128x128 tiles.
-    //
     const long long t256 = (long long)((q.M + 255) / 256) * ((q.N + 255) / 256) * q.batch;
     const long long t128 = (long long)((q.M + 127) / 128) * ((q.N + 127) / 128) * q.batch;
     const long long t64 = (long long)((q.M + 63) / 64) * ((q.N + 63) / 64) * q.batch;
-    if (t128 < 256 && t64 >= 256 && sg_dma_ok<SgDma64>(q)) return launch_sg_dma<SgDma64>(q, stream);
+    if (t128 < 256 && 8 * t64 >= 5 * 256 && sg_dma_ok<SgDma64>(q)) return launch_sg_dma<SgDma64>(q, stream);
     if (t128 < 256) {
         // fewer 128x128 tiles than CUs: split K inside smaller workgroup tiles
         if (t64 >= 256) return launch_small<SgSmall64>(q, stream);
