@@ -809,6 +809,10 @@ __global__ __launch_bounds__(Cfg::NT) __attribute__((amdgpu_waves_per_eu(Cfg::WP
 // each, and an MN-contiguous B is read for both blocks at once.
 using SgDma256 = SgDmaCfg<256, 256, 2, 4>;
 using SgDma128 = SgDmaCfg<128, 128, 2, 4>;
+// Whole 128x128 tiles: two K groups of 2 x 2 waves of 64x64 (3-6% faster than
+// 2 x 4 waves of 64x32 on whole tiles; the masked form of this split needs
+// more registers and loses on ragged grids, which keep SgDma128).
+using SgDma128K = SgDmaCfg<128, 128, 2, 2, 2>;
 using SgDma64 = SgDmaCfg<64, 64, 2, 1, 4>;
 
 // The direct-to-LDS kernel applies: 4-byte aligned operands, at least two
@@ -846,7 +850,9 @@ void launch_sg_dma_ops(const SgemmArgs &a, dim3 grid, bool tA, bool tB, hipStrea
         hipLaunchKernelGGL((sgemm_dma_kernel<Cfg, true, true, MASK>), grid, block, 0, stream, a);
 }
 
-template <class Cfg>
+// WHOLE_ONLY: the caller has checked that the problem is made of whole tiles,
+// so only the unmasked kernels are instantiated.
+template <class Cfg, bool WHOLE_ONLY = false>
 hipError_t launch_sg_dma(const GemmProblem &q, hipStream_t stream)
 {
     SgemmArgs a;
@@ -859,10 +865,14 @@ hipError_t launch_sg_dma(const GemmProblem &q, hipStream_t stream)
     a.tiles_n = (q.N + Cfg::BN - 1) / Cfg::BN;
     const dim3 grid(a.tiles_m * a.tiles_n, 1, q.batch);
     const bool whole = q.M % Cfg::BM == 0 && q.N % Cfg::BN == 0 && q.K % Cfg::BK == 0;
-    if (whole)
+    if constexpr (WHOLE_ONLY) {
+        if (!whole) return hipErrorInvalidValue;
         launch_sg_dma_ops<Cfg, false>(a, grid, q.transA, q.transB, stream);
-    else
+    } else if (whole) {
+        launch_sg_dma_ops<Cfg, false>(a, grid, q.transA, q.transB, stream);
+    } else {
         launch_sg_dma_ops<Cfg, true>(a, grid, q.transA, q.transB, stream);
+    }
     return hipGetLastError();
 }
 
@@ -1137,6 +1147,8 @@ hipError_t launch_sgemm(const GemmProblem &q, hipStream_t stream)
     }
     const long long r256 = (t256 + 255) / 256;
     if (20 * 1024 * r256 <= 21 * t128 && sg_dma_ok<SgDma256>(q)) return launch_sg_dma<SgDma256>(q, stream);
+    if (q.M % 128 == 0 && q.N % 128 == 0 && q.K % 32 == 0 && sg_dma_ok<SgDma128K>(q))
+        return launch_sg_dma<SgDma128K, true>(q, stream);
     if (sg_dma_ok<SgDma128>(q)) return launch_sg_dma<SgDma128>(q, stream);
     return launch_cfg<SgBig>(q, stream);
 }
