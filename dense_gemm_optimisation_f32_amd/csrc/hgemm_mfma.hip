@@ -438,8 +438,8 @@ __device__ __forceinline__ unsigned frag_offset(int first, int lane, int s)
 // TA: A stored K x M; TB: B stored N x K.  MASK: M and N need not be
 // multiples of the tile, nor K of BK (the loads clamp to valid rows and
 // columns, the K % BK tail is read straight from global memory after the last
-// slice, and stores outside C are skipped); an MN-contiguous operand then
-// needs its M or N to be a multiple of eight, so no 16-byte chunk straddles it.
+// slice, and stores outside C are skipped); a 16-byte chunk of an
+// MN-contiguous operand may straddle M or N (see the slice count below).
 template <class Cfg, bool TA, bool TB, bool MASK>
 __global__ __launch_bounds__(Cfg::NT) void hgemm_dma_kernel(HgemmArgs p)
 {

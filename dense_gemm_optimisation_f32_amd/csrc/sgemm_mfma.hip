@@ -13,16 +13,18 @@
 //     K slice of A and B goes from global memory straight into a two-slot LDS
 //     ring (direct-to-LDS loads: the gfx950 form of the article's section 2.3
 //     double buffering, with no register staging), in 256x256, 128x128 or
-//     64x64 tiles.  Ragged M, N and K are handled by clamped slice loads, a K
+//     64x64 tiles; the 64x64 tiles and whole 128x128 tiles split each slice's
+//     eight-k steps over K groups of waves and sum their partial tiles in a
+//     fixed order.  Ragged M, N and K are handled by clamped slice loads, a K
 //     tail read from global memory and masked stores;
 //   * sgemm_mfma_kernel -- problems the direct-to-LDS kernel cannot take (K
 //     below two slices, or an MN-contiguous operand whose M or N is not a
 //     multiple of four) when there are enough tiles:
 //     128x128 tiles read with 16-byte loads into registers and written to a
 //     double-buffered LDS (one barrier per step), zero outside the matrix;
-//   * sgemm_small_kernel -- grids of fewer than 256 tiles of 128x128 that the
-//     64x64 direct-to-LDS tiles cannot take: the waves of a workgroup split K,
-//     and their partial tiles are summed in a fixed order.
+//   * sgemm_small_kernel -- grids of fewer than 256 tiles of 128x128 whose
+//     64x64 tiles would fill fewer than five eighths of the CUs: the waves of a
+//     workgroup split K, and their partial tiles are summed in a fixed order.
 // Every kernel applies C = alpha*acc + beta*C (C not read when beta == 0),
 // masked where the tile crosses the edge of C, and maps workgroups to tiles XCD
 // by XCD (tile_order.h).  Global accesses are 16 bytes wide at any leading
@@ -375,8 +377,8 @@ constexpr int sg_lane_parts()
 // TA: A stored K x M; TB: B stored N x K.  MASK: M and N need not be
 // multiples of the tile, nor K of BK (the loads clamp to valid rows and
 // columns, the K % BK tail is read straight from global memory after the last
-// slice, and stores outside C are skipped); an MN-contiguous operand then
-// needs its M or N to be a multiple of four, so no 16-byte chunk straddles it.
+// slice, and stores outside C are skipped); a 16-byte chunk of an
+// MN-contiguous operand may straddle M or N (see the slice count below).
 template <class Cfg, bool TA, bool TB, bool MASK>
 __global__ __launch_bounds__(Cfg::NT) __attribute__((amdgpu_waves_per_eu(Cfg::WPE))) void sgemm_dma_kernel(SgemmArgs p)
 {
