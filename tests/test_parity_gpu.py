@@ -195,7 +195,7 @@ def test_batched_small_full_and_shared_operand():
 def test_fast_paths_with_padded_leading_dimensions(kind):
     # whole tiles and 16-byte aligned rows, but every leading dimension larger than
     # the logical width: the direct-to-LDS kernels must honour lda/ldb/ldc
-    # (SGEMM needs >= 256 tiles of 128x128 before it leaves the split-K small-problem kernel)
+    # (the SGEMM case needs enough tiles to leave the split-K small-problem kernel)
     if kind == "f32":
         run_and_check(kind, 2048, 2048, 320, 1.5, -0.5, lda=328, ldb=2056, ldc=2060, sample=128)
     else:
@@ -205,8 +205,9 @@ def test_fast_paths_with_padded_leading_dimensions(kind):
 
 @pytest.mark.parametrize("M,N,K", [(512, 512, 512), (64, 64, 4096), (1000, 100, 3000), (96, 1024, 40)])
 def test_small_problem_split_k(M, N, K):
-    # fewer 128x128 tiles than CUs: the four waves of a workgroup split K and their
-    # partial tiles are summed in a fixed order -- check values, bits and determinism
+    # grids too small for the 64x64 direct-to-LDS tile: the eight waves of a
+    # workgroup split K and their partial tiles are summed in a fixed order --
+    # check values and bits
     run_and_check("f32", M, N, K, 1.5, -0.5, lda=K + 1)
     run_and_check("f32", M, N, K, 1.0, 1.0, kind_vals="int4", exact=True, seed=11)
 
