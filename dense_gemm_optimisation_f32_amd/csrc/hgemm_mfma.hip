@@ -116,9 +116,25 @@ __device__ __forceinline__ u32x4 load8_masked(const uint16_t *p, int valid)
     return v;
 }
 
+// Eight halves at p, which may start 2 bytes past a dword: a 16-byte load from
+// the dword holding p[0] and a 4-byte load of the dword holding p[7], joined by
+// a funnel shift of 0 or 16 bits.  Every dword read holds one of the eight
+// halves, so no load leaves the words the matrix occupies.
+__device__ __forceinline__ u32x4 load8_words(const uint16_t *p)
+{
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+    const unsigned sh = (unsigned)(a & 2) * 8;
+    const unsigned *w = reinterpret_cast<const unsigned *>(a & ~(uintptr_t)3);
+    const u32x4 lo = *reinterpret_cast<const u32x4_g *>(w);
+    const unsigned hi = w[sh ? 4 : 3];
+    return u32x4{__builtin_amdgcn_alignbit(lo.y, lo.x, sh), __builtin_amdgcn_alignbit(lo.z, lo.y, sh),
+                 __builtin_amdgcn_alignbit(lo.w, lo.z, sh), __builtin_amdgcn_alignbit(hi, lo.w, sh)};
+}
+
 // Eight consecutive halves (r, c..c+7) of a row-major rows x cols matrix X;
 // with MASK, elements outside it read as zero.  VEC: row starts are 4-byte
-// aligned, so eight halves inside the matrix are one 16-byte load.
+// aligned, so eight halves inside the matrix are one 16-byte load; otherwise
+// they are two dword-aligned loads and a shift.
 template <bool MASK, bool VEC>
 __device__ __forceinline__ u32x4 load8(const uint16_t *X, long long ld, long long r, long long c, long long rows,
                                        long long cols)
@@ -126,7 +142,7 @@ __device__ __forceinline__ u32x4 load8(const uint16_t *X, long long ld, long lon
     const uint16_t *src = X + r * ld + c;
     if (!MASK) return *reinterpret_cast<const u32x4_g *>(src);
     if (r >= rows || c >= cols) return u32x4{0u, 0u, 0u, 0u};
-    if (VEC && c + 8 <= cols) return *reinterpret_cast<const u32x4_g *>(src);
+    if (c + 8 <= cols) return VEC ? *reinterpret_cast<const u32x4_g *>(src) : load8_words(src);
     return load8_masked(src, (int)(cols - c));
 }
 

@@ -532,6 +532,19 @@ def test_hgemm_ragged_direct_to_lds_rows_and_batch():
     batched_check(200, 140, 320, 3, 1.5, -0.5, pad=2, seed=68)
 
 
+@pytest.mark.parametrize("tA,tB", [(False, False)] + OPS)
+def test_hgemm_odd_leading_dimensions(tA, tB):
+    # odd fp16 leading dimensions (rows alternately 2 bytes past a dword) and a
+    # base pointer one half past a dword: the register-staged kernel's eight-half
+    # loads from two dword-aligned loads and a shift, edges element by element
+    M, N, K = 1000, 1001, 1003
+    a_cols, b_cols = (M if tA else K), (K if tB else N)
+    run_and_check("f16", M, N, K, 1.5, -0.5, lda=a_cols + 1 - a_cols % 2 + 2, ldb=b_cols + 1 - b_cols % 2,
+                  ldc=N, sample=64, transA=tA, transB=tB)
+    run_and_check("f16", M, N, K, 1.0, 1.0, lda=a_cols + 1 - a_cols % 2, ldb=b_cols + 3 - b_cols % 2,
+                  sample=64, kind_vals="int4", exact=True, transA=tA, transB=tB, offset=1, seed=97)
+
+
 @pytest.mark.parametrize("tA,tB", OPS)
 def test_transposed_hgemm_register_whole_tiles(tA, tB):
     # whole 128x128 tiles but K too short for the direct-to-LDS ring: unmasked register kernel
