@@ -267,9 +267,11 @@ __global__ __launch_bounds__(Cfg::NT) void sgemm_mfma_kernel(SgemmArgs p)
 // four storage combinations.
 // KS > 1: KS groups of WM x WN waves split each slice's eight-k steps (group
 // ks takes steps ks, ks + KS, ...) and their partial tiles are summed at the end.
-template <int BM_, int BN_, int WM_, int WN_, int KS_ = 1>
+// SLOTS: LDS ring depth (2 or 4 slices in flight).
+template <int BM_, int BN_, int WM_, int WN_, int KS_ = 1, int SLOTS_ = 2>
 struct SgDmaCfg {
-    static constexpr int BM = BM_, BN = BN_, BK = 32, WM = WM_, WN = WN_, KS = KS_, SLOTS = 2;
+    static constexpr int BM = BM_, BN = BN_, BK = 32, WM = WM_, WN = WN_, KS = KS_, SLOTS = SLOTS_;
+    static_assert(SLOTS == 2 || SLOTS == 4, "ring of two or four slices");
     static constexpr int NW = WM * WN * KS, NT = 64 * NW;
     // Waves per SIMD the register budget must allow: the 64x64 tile's grids can
     // hold two work-groups per CU, which its masked instantiations would
@@ -610,27 +612,31 @@ __global__ __launch_bounds__(Cfg::NT) __attribute__((amdgpu_waves_per_eu(Cfg::WP
 
     // Fragments are double-buffered in registers: step u+1's are read while
     // step u's MFMAs run.  Before the last step of slice t, once slice t+1 has
-    // landed for every wave (own loads drained, then the barrier) and every
-    // wave holds its slice-t fragments, the slot of slice t is refilled with
-    // slice t+2 and the first fragments of slice t+1 are read.
+    // landed for every wave (own loads counted down to PENDING outstanding
+    // slices, then the barrier) and every wave holds its slice-t fragments, the
+    // slot of slice t is refilled with slice t+S and the first fragments of
+    // slice t+1 are read.
+    constexpr int S = Cfg::SLOTS;
     constexpr int NU = BK / 8, NUW = NU / KS;   // steps per slice, per wave
     // With an odd step count per slice the buffers alternate from slice to
     // slice: slice t starts in buffer (t * NUW) & 1, passed as PAR.
     f32x4v fa[2][Cfg::FM], fb[2][Cfg::FN];
-    auto step = [&](int t, auto refill, auto par) {
-        constexpr int PAR = decltype(par)::value;
-        const int slot = t & 1;
+    auto step = [&](int t, auto refill, auto pending, auto par) {
+        constexpr int PAR = decltype(par)::value, PEND = LOADS * decltype(pending)::value;
+        const int slot = t & (S - 1);
 #pragma unroll
         for (int u = 0; u < NUW; ++u) {
             const int cur = (u + PAR) & 1, nxt = cur ^ 1;
             if (u + 1 < NUW) {
                 read_frags(slot, u + 1, fa[nxt], fb[nxt]);
             } else {
-                __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): slice t+1 done for this lane
-                __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's slice-t reads are done
+                // vmcnt(PEND): slice t+1 done for this lane; lgkmcnt(0): this
+                // wave's slice-t reads are done
+                __builtin_amdgcn_s_waitcnt((PEND & 15) | ((PEND >> 4) << 14) | (7 << 4) | (15 << 8));
+                __builtin_amdgcn_s_waitcnt(0xC07F);
                 lds_barrier();
-                if (decltype(refill)::value) issue_slice(t + 2, slot);
-                read_frags(slot ^ 1, 0, fa[nxt], fb[nxt]);
+                if (decltype(refill)::value) issue_slice(t + S, slot);
+                read_frags((t + 1) & (S - 1), 0, fa[nxt], fb[nxt]);
             }
             mfmas(fa[cur], fb[cur]);
             interleave();
@@ -643,11 +649,11 @@ __global__ __launch_bounds__(Cfg::NT) __attribute__((amdgpu_waves_per_eu(Cfg::WP
     // lie in the next row.  The slices then stop before row K-1 and the K tail
     // below takes the rest, so no slice load reads past the operand.
     const bool straddle = MASK && ((!A_KC && p.M % 4 != 0) || (!B_KC && p.N % 4 != 0));
-    const int nk = (p.K - (straddle ? 1 : 0)) / BK;   // whole slices, >= 2 (checked by the launcher)
+    const int nk = (p.K - (straddle ? 1 : 0)) / BK;   // whole slices, >= S (checked by the launcher)
     // the last slice: resident, nothing left to fetch
     auto last_slice = [&](auto par) {
         constexpr int PAR = decltype(par)::value;
-        const int slot = (nk - 1) & 1;
+        const int slot = (nk - 1) & (S - 1);
 #pragma unroll
         for (int u = 0; u < NUW; ++u) {
             const int cur = (u + PAR) & 1, nxt = cur ^ 1;
@@ -655,31 +661,46 @@ __global__ __launch_bounds__(Cfg::NT) __attribute__((amdgpu_waves_per_eu(Cfg::WP
             mfmas(fa[cur], fb[cur]);
         }
     };
-    issue_slice(0, 0);
-    issue_slice(1, 1);
-    __builtin_amdgcn_s_waitcnt((LOADS & 15) | ((LOADS >> 4) << 14) | (7 << 4) | (15 << 8));   // slice 0 done
+    // Prologue: slices 0 .. S-1 in flight, slice 0 resident, its first
+    // fragments read.
+#pragma unroll
+    for (int st = 0; st < S; ++st) issue_slice(st, st);
+    constexpr int FIRST = LOADS * (S - 1);
+    __builtin_amdgcn_s_waitcnt((FIRST & 15) | ((FIRST >> 4) << 14) | (7 << 4) | (15 << 8));   // slice 0 done
     lds_barrier();
     read_frags(0, 0, fa[0], fb[0]);
     using P0 = std::integral_constant<int, 0>;
     using P1 = std::integral_constant<int, 1>;
+    using Steady = std::integral_constant<int, S - 2>;   // slices after t+1 in flight
+    // The last S-1 steps issue nothing and drain the ring; p0 is the buffer
+    // parity of slice nk-S.
+    auto tail = [&](auto p0) {
+        constexpr int A0 = decltype(p0)::value, A1 = A0 ^ (NUW & 1);
+        const int t0 = nk - S;
+        if constexpr (S == 4) {
+            step(t0, std::false_type{}, std::integral_constant<int, 2>{}, std::integral_constant<int, A0>{});
+            step(t0 + 1, std::false_type{}, std::integral_constant<int, 1>{}, std::integral_constant<int, A1>{});
+            step(t0 + 2, std::false_type{}, std::integral_constant<int, 0>{}, std::integral_constant<int, A0>{});
+            last_slice(std::integral_constant<int, A1>{});
+        } else {
+            step(t0, std::false_type{}, std::integral_constant<int, 0>{}, std::integral_constant<int, A0>{});
+            last_slice(std::integral_constant<int, A1>{});
+        }
+    };
     if constexpr (NUW % 2 == 0) {
-        for (int t = 0; t + 2 < nk; ++t) step(t, std::true_type{}, P0{});
-        step(nk - 2, std::false_type{}, P0{});
-        last_slice(P0{});
+        for (int t = 0; t + S < nk; ++t) step(t, std::true_type{}, Steady{}, P0{});
+        tail(P0{});
     } else {   // slices in pairs, so that each call knows its buffer
         int t = 0;
-        for (; t + 3 < nk; t += 2) {
-            step(t, std::true_type{}, P0{});
-            step(t + 1, std::true_type{}, P1{});
+        for (; t + 1 + S < nk; t += 2) {
+            step(t, std::true_type{}, Steady{}, P0{});
+            step(t + 1, std::true_type{}, Steady{}, P1{});
         }
-        if (t + 3 == nk) {
-            step(t, std::true_type{}, P0{});
-            step(t + 1, std::false_type{}, P1{});
-            last_slice(P0{});
-        } else {
-            step(t, std::false_type{}, P0{});
-            last_slice(P1{});
-        }
+        if (t + S < nk) step(t, std::true_type{}, Steady{}, P0{});
+        if ((nk - S) & 1)
+            tail(P1{});
+        else
+            tail(P0{});
     }
     // The tail and the epilogue take the lane's row and k half from a lane id
     // read afresh, so that no address derived from it stays live (and spills)
@@ -816,9 +837,15 @@ using SgDma128 = SgDmaCfg<128, 128, 2, 4>;
 // more registers and loses on ragged grids, which keep SgDma128).
 using SgDma128K = SgDmaCfg<128, 128, 2, 2, 2>;
 using SgDma64 = SgDmaCfg<64, 64, 2, 1, 4>;
+// The same with a four-slice ring (64 KB of LDS, still two work-groups per
+// CU): each slice holds only about 0.2 us of MFMA work, so two slots prefetch
+// less than a load's latency.  Measured 20-30% faster at long K with A stored
+// M x K (1024^2 x 4096: 88 -> 68 us), but 8-14% slower with A stored K x M, so
+// it is built for A stored M x K only.
+using SgDma64D = SgDmaCfg<64, 64, 2, 1, 4, 4>;
 
-// The direct-to-LDS kernel applies: 4-byte aligned operands, at least two
-// whole slices of k, an MN-contiguous operand (A stored K x M, B stored K x N)
+// The direct-to-LDS kernel applies: 4-byte aligned operands, at least a ring
+// of whole slices of k, an MN-contiguous operand (A stored K x M, B stored K x N)
 // at least eight wide where M or N is not a multiple of four, and 32-bit slice
 // offsets.
 template <class Cfg>
@@ -830,7 +857,7 @@ bool sg_dma_ok(const GemmProblem &q)
     // a chunk straddling M or N (see the kernel) needs M or N >= 8, so that its
     // overflow stays in the next row, and one row of K left to the tail
     const bool straddle = (q.transA && q.M % 4 != 0) || (!q.transB && q.N % 4 != 0);
-    const bool shape = q.K - (straddle ? 1 : 0) >= 2 * Cfg::BK && (!q.transA || q.M % 4 == 0 || q.M >= 8) &&
+    const bool shape = q.K - (straddle ? 1 : 0) >= Cfg::SLOTS * Cfg::BK && (!q.transA || q.M % 4 == 0 || q.M >= 8) &&
                        (q.transB || q.N % 4 == 0 || q.N >= 8);
     // per-lane offsets within one slice are 32-bit: rows of the slice times ld
     const long long rows_a = q.transA ? Cfg::BK : Cfg::BM, rows_b = q.transB ? Cfg::BN : Cfg::BK;
@@ -838,25 +865,30 @@ bool sg_dma_ok(const GemmProblem &q)
     return aligned && shape && fits;
 }
 
-template <class Cfg, bool MASK>
+// NO_TA: only A stored M x K is instantiated (the caller has checked).
+template <class Cfg, bool MASK, bool NO_TA>
 void launch_sg_dma_ops(const SgemmArgs &a, dim3 grid, bool tA, bool tB, hipStream_t stream)
 {
     const dim3 block(Cfg::NT);
-    if (!tA && !tB)
+    if (!tA && !tB) {
         hipLaunchKernelGGL((sgemm_dma_kernel<Cfg, false, false, MASK>), grid, block, 0, stream, a);
-    else if (!tA)
+    } else if (!tA) {
         hipLaunchKernelGGL((sgemm_dma_kernel<Cfg, false, true, MASK>), grid, block, 0, stream, a);
-    else if (!tB)
-        hipLaunchKernelGGL((sgemm_dma_kernel<Cfg, true, false, MASK>), grid, block, 0, stream, a);
-    else
-        hipLaunchKernelGGL((sgemm_dma_kernel<Cfg, true, true, MASK>), grid, block, 0, stream, a);
+    } else if constexpr (!NO_TA) {
+        if (!tB)
+            hipLaunchKernelGGL((sgemm_dma_kernel<Cfg, true, false, MASK>), grid, block, 0, stream, a);
+        else
+            hipLaunchKernelGGL((sgemm_dma_kernel<Cfg, true, true, MASK>), grid, block, 0, stream, a);
+    }
 }
 
 // WHOLE_ONLY: the caller has checked that the problem is made of whole tiles,
-// so only the unmasked kernels are instantiated.
-template <class Cfg, bool WHOLE_ONLY = false>
+// so only the unmasked kernels are instantiated.  NO_TA: likewise for A
+// stored M x K.
+template <class Cfg, bool WHOLE_ONLY = false, bool NO_TA = false>
 hipError_t launch_sg_dma(const GemmProblem &q, hipStream_t stream)
 {
+    if (NO_TA && q.transA) return hipErrorInvalidValue;
     SgemmArgs a;
     a.M = q.M; a.N = q.N; a.K = q.K;
     a.alpha = q.alpha; a.beta = q.beta;
@@ -869,11 +901,11 @@ hipError_t launch_sg_dma(const GemmProblem &q, hipStream_t stream)
     const bool whole = q.M % Cfg::BM == 0 && q.N % Cfg::BN == 0 && q.K % Cfg::BK == 0;
     if constexpr (WHOLE_ONLY) {
         if (!whole) return hipErrorInvalidValue;
-        launch_sg_dma_ops<Cfg, false>(a, grid, q.transA, q.transB, stream);
+        launch_sg_dma_ops<Cfg, false, NO_TA>(a, grid, q.transA, q.transB, stream);
     } else if (whole) {
-        launch_sg_dma_ops<Cfg, false>(a, grid, q.transA, q.transB, stream);
+        launch_sg_dma_ops<Cfg, false, NO_TA>(a, grid, q.transA, q.transB, stream);
     } else {
-        launch_sg_dma_ops<Cfg, true>(a, grid, q.transA, q.transB, stream);
+        launch_sg_dma_ops<Cfg, true, NO_TA>(a, grid, q.transA, q.transB, stream);
     }
     return hipGetLastError();
 }
@@ -1141,7 +1173,10 @@ hipError_t launch_sgemm(const GemmProblem &q, hipStream_t stream)
     const long long t256 = (long long)((q.M + 255) / 256) * ((q.N + 255) / 256) * q.batch;
     const long long t128 = (long long)((q.M + 127) / 128) * ((q.N + 127) / 128) * q.batch;
     const long long t64 = (long long)((q.M + 63) / 64) * ((q.N + 63) / 64) * q.batch;
-    if (t128 < 256 && 8 * t64 >= 5 * 256 && sg_dma_ok<SgDma64>(q)) return launch_sg_dma<SgDma64>(q, stream);
+    if (t128 < 256 && 8 * t64 >= 5 * 256) {
+        if (!q.transA && sg_dma_ok<SgDma64D>(q)) return launch_sg_dma<SgDma64D, false, true>(q, stream);
+        if (sg_dma_ok<SgDma64>(q)) return launch_sg_dma<SgDma64>(q, stream);
+    }
     if (t128 < 256) {
         // fewer 128x128 tiles than CUs: split K inside smaller workgroup tiles
         if (t64 >= 256) return launch_small<SgSmall64>(q, stream);

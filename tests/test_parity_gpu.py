@@ -444,11 +444,14 @@ def test_transposed_fast_paths(kind, tA, tB):
 def test_sgemm_64_tiles_direct_to_lds(tA, tB):
     # fewer than 256 tiles of 128x128 but at least 256 whole 64x64 tiles: the
     # 64x64 direct-to-LDS kernel, whose four K groups take one eight-k step of
-    # each slice and run the slices in pairs.  K = 64, 96, 128, 160 give two to
-    # five slices (both pair endings); 120 and 136 add tails of three steps and
-    # of one, split over the groups; 416 is a longer even run.
+    # each slice and run the slices in pairs, with a two-slice ring (A stored
+    # K x M, or K below four slices) or a four-slice one.  K = 64 .. 224 give two
+    # to seven slices (every ring ending in both buffer parities); 120 and 136
+    # add tails of three steps and of one, split over the groups; 416 is a
+    # longer run.
     for M, N, K in [(1024, 1024, 64), (1024, 1024, 96), (1024, 1024, 128), (1024, 1024, 160),
-                    (1024, 1024, 120), (1024, 1024, 136), (1024, 2048, 416)]:
+                    (1024, 1024, 192), (1024, 1024, 224), (1024, 1024, 120), (1024, 1024, 136),
+                    (1024, 2048, 416)]:
         a_cols, b_cols = (M if tA else K), (K if tB else N)
         run_and_check("f32", M, N, K, 1.5, -0.5, lda=a_cols + 4, ldb=b_cols + 12, ldc=N + 3, sample=128,
                       transA=tA, transB=tB)
