@@ -837,12 +837,15 @@ using SgDma128 = SgDmaCfg<128, 128, 2, 4>;
 // more registers and loses on ragged grids, which keep SgDma128).
 using SgDma128K = SgDmaCfg<128, 128, 2, 2, 2>;
 using SgDma64 = SgDmaCfg<64, 64, 2, 1, 4>;
-// The same with a four-slice ring (64 KB of LDS, still two work-groups per
-// CU): each slice holds only about 0.2 us of MFMA work, so two slots prefetch
-// less than a load's latency.  Measured 20-30% faster at long K with A stored
-// M x K (1024^2 x 4096: 88 -> 68 us), but 8-14% slower with A stored K x M, so
-// it is built for A stored M x K only.
+// With a four-slice ring (64 KB of LDS, still two work-groups per CU): each
+// slice holds only about 0.2 us of MFMA work, so two slots prefetch less than
+// a load's latency.  The wave tile pairs the blocks of the MN-contiguous
+// operand: 32x64 when B is stored K x N (NN; NT too), 64x32 when only A is
+// stored K x M (TT).  Measured 20-30% faster at long K (1024^2 x 4096: NN
+// 88 -> 68 us, TT 84 -> 66 us); with both operands MN-contiguous (TN) neither
+// layout gained consistently, so TN keeps the two-slot ring.
 using SgDma64D = SgDmaCfg<64, 64, 2, 1, 4, 4>;
+using SgDma64DT = SgDmaCfg<64, 64, 1, 2, 4, 4>;
 
 // The direct-to-LDS kernel applies: 4-byte aligned operands, at least a ring
 // of whole slices of k, an MN-contiguous operand (A stored K x M, B stored K x N)
@@ -865,30 +868,31 @@ bool sg_dma_ok(const GemmProblem &q)
     return aligned && shape && fits;
 }
 
-// NO_TA: only A stored M x K is instantiated (the caller has checked).
-template <class Cfg, bool MASK, bool NO_TA>
+// Storage combinations as bits: 1 << (2*transA + transB).
+constexpr int OP_NN = 1, OP_NT = 2, OP_TN = 4, OP_TT = 8, OP_ALL = 15;
+
+// OPS: the storage combinations instantiated (the caller has checked).
+template <class Cfg, bool MASK, int OPS>
 void launch_sg_dma_ops(const SgemmArgs &a, dim3 grid, bool tA, bool tB, hipStream_t stream)
 {
     const dim3 block(Cfg::NT);
-    if (!tA && !tB) {
-        hipLaunchKernelGGL((sgemm_dma_kernel<Cfg, false, false, MASK>), grid, block, 0, stream, a);
-    } else if (!tA) {
-        hipLaunchKernelGGL((sgemm_dma_kernel<Cfg, false, true, MASK>), grid, block, 0, stream, a);
-    } else if constexpr (!NO_TA) {
-        if (!tB)
-            hipLaunchKernelGGL((sgemm_dma_kernel<Cfg, true, false, MASK>), grid, block, 0, stream, a);
-        else
-            hipLaunchKernelGGL((sgemm_dma_kernel<Cfg, true, true, MASK>), grid, block, 0, stream, a);
-    }
+    if constexpr ((OPS & OP_NN) != 0)
+        if (!tA && !tB) hipLaunchKernelGGL((sgemm_dma_kernel<Cfg, false, false, MASK>), grid, block, 0, stream, a);
+    if constexpr ((OPS & OP_NT) != 0)
+        if (!tA && tB) hipLaunchKernelGGL((sgemm_dma_kernel<Cfg, false, true, MASK>), grid, block, 0, stream, a);
+    if constexpr ((OPS & OP_TN) != 0)
+        if (tA && !tB) hipLaunchKernelGGL((sgemm_dma_kernel<Cfg, true, false, MASK>), grid, block, 0, stream, a);
+    if constexpr ((OPS & OP_TT) != 0)
+        if (tA && tB) hipLaunchKernelGGL((sgemm_dma_kernel<Cfg, true, true, MASK>), grid, block, 0, stream, a);
 }
 
 // WHOLE_ONLY: the caller has checked that the problem is made of whole tiles,
-// so only the unmasked kernels are instantiated.  NO_TA: likewise for A
-// stored M x K.
-template <class Cfg, bool WHOLE_ONLY = false, bool NO_TA = false>
+// so only the unmasked kernels are instantiated.  OPS: likewise for the
+// storage combinations.
+template <class Cfg, bool WHOLE_ONLY = false, int OPS = OP_ALL>
 hipError_t launch_sg_dma(const GemmProblem &q, hipStream_t stream)
 {
-    if (NO_TA && q.transA) return hipErrorInvalidValue;
+    if ((OPS & (1 << (2 * q.transA + q.transB))) == 0) return hipErrorInvalidValue;
     SgemmArgs a;
     a.M = q.M; a.N = q.N; a.K = q.K;
     a.alpha = q.alpha; a.beta = q.beta;
@@ -901,11 +905,11 @@ hipError_t launch_sg_dma(const GemmProblem &q, hipStream_t stream)
     const bool whole = q.M % Cfg::BM == 0 && q.N % Cfg::BN == 0 && q.K % Cfg::BK == 0;
     if constexpr (WHOLE_ONLY) {
         if (!whole) return hipErrorInvalidValue;
-        launch_sg_dma_ops<Cfg, false, NO_TA>(a, grid, q.transA, q.transB, stream);
+        launch_sg_dma_ops<Cfg, false, OPS>(a, grid, q.transA, q.transB, stream);
     } else if (whole) {
-        launch_sg_dma_ops<Cfg, false, NO_TA>(a, grid, q.transA, q.transB, stream);
+        launch_sg_dma_ops<Cfg, false, OPS>(a, grid, q.transA, q.transB, stream);
     } else {
-        launch_sg_dma_ops<Cfg, true, NO_TA>(a, grid, q.transA, q.transB, stream);
+        launch_sg_dma_ops<Cfg, true, OPS>(a, grid, q.transA, q.transB, stream);
     }
     return hipGetLastError();
 }
@@ -1174,7 +1178,8 @@ hipError_t launch_sgemm(const GemmProblem &q, hipStream_t stream)
     const long long t128 = (long long)((q.M + 127) / 128) * ((q.N + 127) / 128) * q.batch;
     const long long t64 = (long long)((q.M + 63) / 64) * ((q.N + 63) / 64) * q.batch;
     if (t128 < 256 && 8 * t64 >= 5 * 256) {
-        if (!q.transA && sg_dma_ok<SgDma64D>(q)) return launch_sg_dma<SgDma64D, false, true>(q, stream);
+        if (!q.transA && sg_dma_ok<SgDma64D>(q)) return launch_sg_dma<SgDma64D, false, OP_NN | OP_NT>(q, stream);
+        if (q.transA && q.transB && sg_dma_ok<SgDma64DT>(q)) return launch_sg_dma<SgDma64DT, false, OP_TT>(q, stream);
         if (sg_dma_ok<SgDma64>(q)) return launch_sg_dma<SgDma64>(q, stream);
     }
     if (t128 < 256) {
@@ -1185,7 +1190,7 @@ hipError_t launch_sgemm(const GemmProblem &q, hipStream_t stream)
     const long long r256 = (t256 + 255) / 256;
     if (20 * 1024 * r256 <= 21 * t128 && sg_dma_ok<SgDma256>(q)) return launch_sg_dma<SgDma256>(q, stream);
     if (q.M % 128 == 0 && q.N % 128 == 0 && q.K % 32 == 0 && sg_dma_ok<SgDma128K>(q))
-        return launch_sg_dma<SgDma128K, true>(q, stream);
+        return launch_sg_dma<SgDma128K, true, OP_ALL>(q, stream);
     if (sg_dma_ok<SgDma128>(q)) return launch_sg_dma<SgDma128>(q, stream);
     return launch_cfg<SgBig>(q, stream);
 }
