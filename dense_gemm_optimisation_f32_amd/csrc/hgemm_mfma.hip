@@ -39,7 +39,9 @@
 //   * hgemm_mfma_kernel -- everything else: 128x128 (64x64 for small grids)
 //     tiles of four waves in a 2 x 2 grid, read into registers with 16-byte
 //     loads (row starts 4-byte aligned: CDNA's multi-dword global loads need
-//     only dword alignment) or element loads, and written to a double-buffered
+//     only dword alignment), with a 16-byte and a dword load joined by a
+//     funnel shift (rows starting at an odd half), or, at the matrix's edge,
+//     with element loads, and written to a double-buffered
 //     LDS with one barrier per K step.  MASK = false for whole tiles, true
 //     otherwise (out-of-range elements load as zero, stores are masked).
 #include "gemm_internal.h"

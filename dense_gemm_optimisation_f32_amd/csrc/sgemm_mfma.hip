@@ -10,16 +10,16 @@
 //
 // Three kernels; launch_sgemm picks one per problem:
 //   * sgemm_dma_kernel -- the main kernel (any leading dimension).  Each
-//     K slice of A and B goes from global memory straight into a two-slot LDS
-//     ring (direct-to-LDS loads: the gfx950 form of the article's section 2.3
-//     double buffering, with no register staging), in 256x256, 128x128 or
+//     K slice of A and B goes from global memory straight into a ring of two
+//     or four LDS slots (direct-to-LDS loads: the gfx950 form of the article's
+//     section 2.3 double buffering, with no register staging), in 256x256, 128x128 or
 //     64x64 tiles; the 64x64 tiles and whole 128x128 tiles split each slice's
 //     eight-k steps over K groups of waves and sum their partial tiles in a
 //     fixed order.  Ragged M, N and K are handled by clamped slice loads, a K
 //     tail read from global memory and masked stores;
 //   * sgemm_mfma_kernel -- problems the direct-to-LDS kernel cannot take (K
-//     below two slices, or an MN-contiguous operand whose M or N is not a
-//     multiple of four) when there are enough tiles:
+//     below the ring's slices, or an MN-contiguous operand whose M or N is
+//     below eight and not a multiple of four) when there are enough tiles:
 //     128x128 tiles read with 16-byte loads into registers and written to a
 //     double-buffered LDS (one barrier per step), zero outside the matrix;
 //   * sgemm_small_kernel -- grids of fewer than 256 tiles of 128x128 whose
