@@ -37,6 +37,7 @@ METRIC = "TFLOPS (2MNK/t) + % of dtype peak: SGEMM 4096x4096x1024, HGEMM 4096^3"
 # MI355X peaks: 256 CUs x 2.4 GHz; fp32 matrix/vector 256 flop/clk/CU, fp16 dense MFMA 4096 flop/clk/CU.
 PEAK_F32_TFLOPS = 157.3
 PEAK_F16_TFLOPS = 2516.6
+PEAK_BF16_TFLOPS = 2516.6   # bf16 dense MFMA runs at the fp16 rate
 PEAK_HBM_GBS = 8000.0
 _CSRC = "dense_gemm_optimisation_f32_amd/csrc/"
 # the files whose code makes up each kernel (its source and the headers it includes)
@@ -484,6 +485,14 @@ def run_extra(dg, si, np, torch, dev, stream):
     med, _, gr = time_calls(lambda s: dg.gemm_f16_f32acc(2048, 2048, 2048, 1.0, A, 2048, B, 2048, 0.0, C, 2048, s),
                             torch, stream)
     out["hgemm_2048^3"] = rates(med, gr, 2.0 * 2048 ** 3, PEAK_F16_TFLOPS)
+
+    # bfloat16 inputs (the same kernels with the bf16 matrix-core op)
+    for n in (2048, 4096):
+        A = torch.empty(n * n, dtype=torch.bfloat16, device=dev).uniform_(-1, 1)
+        B = torch.empty(n * n, dtype=torch.bfloat16, device=dev).uniform_(-1, 1)
+        C = torch.empty(n * n, dtype=torch.float32, device=dev)
+        med, _, gr = time_calls(lambda s: dg.gemm_bf16_f32acc(n, n, n, 1.0, A, n, B, n, 0.0, C, n, s), torch, stream)
+        out[f"bf16gemm_{n}^3"] = rates(med, gr, 2.0 * n ** 3, PEAK_BF16_TFLOPS)
 
     # ragged shapes (M, N not multiples of the tile, K not of the slice): the masked
     # direct-to-LDS kernels

@@ -18,12 +18,16 @@ import ctypes
 import os
 
 __all__ = ["gemm_f32", "gemm_f16_f32acc", "gemm_batched_f16_f32acc",
-           "gemm_f32_ex", "gemm_f16_f32acc_ex", "gemm_batched_f16_f32acc_ex", "status_string",
+           "gemm_f32_ex", "gemm_f16_f32acc_ex", "gemm_batched_f16_f32acc_ex",
+           "gemm_bf16_f32acc", "gemm_batched_bf16_f32acc", "gemm_bf16_f32acc_ex", "gemm_batched_bf16_f32acc_ex",
+           "status_string",
            "GemmError", "GemmLibraryMissing", "LIB_PATH", "load_library", "EXPORTS"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmi355gemm.so")
 EXPORTS = ("gemm_f32", "gemm_f16_f32acc", "gemm_batched_f16_f32acc",
-           "gemm_f32_ex", "gemm_f16_f32acc_ex", "gemm_batched_f16_f32acc_ex", "gemm_status_string")
+           "gemm_f32_ex", "gemm_f16_f32acc_ex", "gemm_batched_f16_f32acc_ex",
+           "gemm_bf16_f32acc", "gemm_batched_bf16_f32acc", "gemm_bf16_f32acc_ex", "gemm_batched_bf16_f32acc_ex",
+           "gemm_status_string")
 
 _lib = None
 
@@ -62,6 +66,13 @@ def load_library(path: str = LIB_PATH):
     lib.gemm_f16_f32acc_ex.restype = i
     lib.gemm_batched_f16_f32acc_ex.argtypes = [i, i] + lib.gemm_batched_f16_f32acc.argtypes
     lib.gemm_batched_f16_f32acc_ex.restype = i
+    for name, base in (("gemm_bf16_f32acc", lib.gemm_f16_f32acc),
+                       ("gemm_batched_bf16_f32acc", lib.gemm_batched_f16_f32acc),
+                       ("gemm_bf16_f32acc_ex", lib.gemm_f16_f32acc_ex),
+                       ("gemm_batched_bf16_f32acc_ex", lib.gemm_batched_f16_f32acc_ex)):
+        fn = getattr(lib, name)
+        fn.argtypes = base.argtypes
+        fn.restype = i
     lib.gemm_status_string.argtypes = [i]
     lib.gemm_status_string.restype = ctypes.c_char_p
     if path == LIB_PATH:
@@ -192,3 +203,53 @@ def gemm_batched_f16_f32acc_ex(transA, transB, M, N, K, alpha, A, lda, strideA, 
                                         _stream(stream))
     if rc != 0:
         raise GemmError(rc, "gemm_batched_f16_f32acc_ex")
+
+
+def gemm_bf16_f32acc(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=None) -> None:
+    """C <- alpha*A*B + beta*C with bf16 A, B and fp32 accumulation and C."""
+    lib = load_library()
+    na, nb, nc = _needs(M, N, K, alpha, lda, ldb, ldc)
+    rc = lib.gemm_bf16_f32acc(M, N, K, alpha, _ptr(A, "A", "torch.bfloat16", na), lda,
+                              _ptr(B, "B", "torch.bfloat16", nb), ldb, beta,
+                              _ptr(C, "C", "torch.float32", nc), ldc, _stream(stream))
+    if rc != 0:
+        raise GemmError(rc, "gemm_bf16_f32acc")
+
+
+def gemm_batched_bf16_f32acc(M, N, K, alpha, A, lda, strideA, B, ldb, strideB, beta, C, ldc, strideC,
+                             batch_count, stream=None) -> None:
+    """Strided-batched form of gemm_bf16_f32acc."""
+    lib = load_library()
+    na, nb, nc = _needs(M, N, K, alpha, lda, ldb, ldc, batch_count, strideA, strideB, strideC)
+    rc = lib.gemm_batched_bf16_f32acc(M, N, K, alpha, _ptr(A, "A", "torch.bfloat16", na), lda, strideA,
+                                      _ptr(B, "B", "torch.bfloat16", nb), ldb, strideB, beta,
+                                      _ptr(C, "C", "torch.float32", nc), ldc, strideC, batch_count,
+                                      _stream(stream))
+    if rc != 0:
+        raise GemmError(rc, "gemm_batched_bf16_f32acc")
+
+
+def gemm_bf16_f32acc_ex(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=None) -> None:
+    """gemm_bf16_f32acc with op(A)/op(B) (see gemm_f32_ex)."""
+    lib = load_library()
+    tA, tB = int(transA), int(transB)   # values other than 0/1 are refused by the library
+    na, nb, nc = _needs(M, N, K, alpha, lda, ldb, ldc, transA=tA, transB=tB)
+    rc = lib.gemm_bf16_f32acc_ex(tA, tB, M, N, K, alpha, _ptr(A, "A", "torch.bfloat16", na), lda,
+                                 _ptr(B, "B", "torch.bfloat16", nb), ldb, beta,
+                                 _ptr(C, "C", "torch.float32", nc), ldc, _stream(stream))
+    if rc != 0:
+        raise GemmError(rc, "gemm_bf16_f32acc_ex")
+
+
+def gemm_batched_bf16_f32acc_ex(transA, transB, M, N, K, alpha, A, lda, strideA, B, ldb, strideB, beta, C, ldc,
+                                strideC, batch_count, stream=None) -> None:
+    """gemm_batched_bf16_f32acc with op(A)/op(B) (see gemm_f32_ex)."""
+    lib = load_library()
+    tA, tB = int(transA), int(transB)   # values other than 0/1 are refused by the library
+    na, nb, nc = _needs(M, N, K, alpha, lda, ldb, ldc, batch_count, strideA, strideB, strideC, tA, tB)
+    rc = lib.gemm_batched_bf16_f32acc_ex(tA, tB, M, N, K, alpha, _ptr(A, "A", "torch.bfloat16", na), lda,
+                                         strideA, _ptr(B, "B", "torch.bfloat16", nb), ldb, strideB, beta,
+                                         _ptr(C, "C", "torch.float32", nc), ldc, strideC, batch_count,
+                                         _stream(stream))
+    if rc != 0:
+        raise GemmError(rc, "gemm_batched_bf16_f32acc_ex")

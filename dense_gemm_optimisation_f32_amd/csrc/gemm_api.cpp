@@ -124,6 +124,23 @@ int gemm_batched_f16_f32acc_ex(int transA, int transB, int M, int N, int K, floa
                sizeof(uint16_t), stream, mi355gemm::launch_hgemm);
 }
 
+int gemm_bf16_f32acc_ex(int transA, int transB, int M, int N, int K, float alpha, const uint16_t *A, int lda,
+                        const uint16_t *B, int ldb, float beta, float *C, int ldc, hipStream_t stream)
+{
+    return run(make(transA, transB, M, N, K, alpha, A, lda, 0, B, ldb, 0, beta, C, ldc, 0, 1), sizeof(uint16_t),
+               stream, mi355gemm::launch_bgemm);
+}
+
+int gemm_batched_bf16_f32acc_ex(int transA, int transB, int M, int N, int K, float alpha, const uint16_t *A,
+                                int lda, long long strideA, const uint16_t *B, int ldb, long long strideB,
+                                float beta, float *C, int ldc, long long strideC, int batch_count,
+                                hipStream_t stream)
+{
+    return run(make(transA, transB, M, N, K, alpha, A, lda, strideA, B, ldb, strideB, beta, C, ldc, strideC,
+                    batch_count),
+               sizeof(uint16_t), stream, mi355gemm::launch_bgemm);
+}
+
 int gemm_f32(int M, int N, int K, float alpha, const float *A, int lda, const float *B, int ldb, float beta,
              float *C, int ldc, hipStream_t stream)
 {
@@ -142,6 +159,20 @@ int gemm_batched_f16_f32acc(int M, int N, int K, float alpha, const uint16_t *A,
 {
     return gemm_batched_f16_f32acc_ex(0, 0, M, N, K, alpha, A, lda, strideA, B, ldb, strideB, beta, C, ldc, strideC,
                                       batch_count, stream);
+}
+
+int gemm_bf16_f32acc(int M, int N, int K, float alpha, const uint16_t *A, int lda, const uint16_t *B, int ldb,
+                     float beta, float *C, int ldc, hipStream_t stream)
+{
+    return gemm_bf16_f32acc_ex(0, 0, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream);
+}
+
+int gemm_batched_bf16_f32acc(int M, int N, int K, float alpha, const uint16_t *A, int lda, long long strideA,
+                             const uint16_t *B, int ldb, long long strideB, float beta, float *C, int ldc,
+                             long long strideC, int batch_count, hipStream_t stream)
+{
+    return gemm_batched_bf16_f32acc_ex(0, 0, M, N, K, alpha, A, lda, strideA, B, ldb, strideB, beta, C, ldc,
+                                       strideC, batch_count, stream);
 }
 
 const char *gemm_status_string(int status)

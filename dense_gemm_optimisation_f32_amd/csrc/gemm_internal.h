@@ -25,6 +25,8 @@ struct GemmProblem {
 hipError_t launch_sgemm(const GemmProblem &p, hipStream_t stream);
 // fp16-input, fp32-accumulate GEMM on fp16 MFMA (same preconditions).
 hipError_t launch_hgemm(const GemmProblem &p, hipStream_t stream);
+// bf16-input, fp32-accumulate GEMM on bf16 MFMA (same kernels and preconditions).
+hipError_t launch_bgemm(const GemmProblem &p, hipStream_t stream);
 // C <- beta*C (or 0 when beta == 0) for the K == 0 / alpha == 0 cases.
 hipError_t launch_scale_c(const GemmProblem &p, hipStream_t stream);
 

@@ -1,5 +1,8 @@
-// hgemm_mfma.hip -- fp16-input, fp32-accumulate row-major GEMM (single and
-// strided-batched) on the CDNA4 fp16 matrix cores.
+// hgemm_mfma.hip -- 16-bit-input, fp32-accumulate row-major GEMM (single and
+// strided-batched) on the CDNA4 matrix cores: IEEE binary16 inputs (fp16 MFMA)
+// and, through the same kernels, bfloat16 inputs (bf16 MFMA), the two input
+// formats of the MindNotes 'GEMM' page's mixed-precision interface (section
+// "Batched execution and mixed precision").
 //
 // The tiling follows the wave-level hierarchy of the dandandamowang.xyz
 // 'GEMM optimisation (2): Tensor Core wmma API' page (sections 4-7: one warp
@@ -29,7 +32,8 @@
 //     form a compact block of C;
 //   * epilogue C = alpha*acc + beta*C (C not read when beta == 0).
 //
-// Two kernels; launch_hgemm picks one per problem:
+// Two kernels; launch_hgemm (binary16) and launch_bgemm (bfloat16) pick one
+// per problem:
 //   * hgemm_dma_kernel -- operands whose rows start 4-byte aligned.  K slices
 //     go from global memory straight into an LDS ring (direct-to-LDS loads, the
 //     gfx950 form of the page's asynchronous double buffering): 256x256 tiles
@@ -56,6 +60,22 @@ namespace {
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef short short4v __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// One 32x32x16 matrix-core op on eight 16-bit values of B and of A per lane:
+// IEEE binary16 (BF = false) or bfloat16 (BF = true).  The kernels only move
+// 16-bit payloads (half8 is their carrier type); the format matters here alone.
+// Products of either format are exact in fp32, and the sum is accumulated in
+// fp32 in both.
+template <bool BF>
+__device__ __forceinline__ f32x16 mfma16(half8 b, half8 a, f32x16 c)
+{
+    if constexpr (BF)
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, b), __builtin_bit_cast(bf16x8, a),
+                                                       c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(b, a, c, 0, 0, 0);
+}
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 // 16 bytes in global memory at dword (not 16-byte) alignment: multi-dword
 // global loads need only dword alignment on CDNA
@@ -149,7 +169,7 @@ __device__ __forceinline__ u32x4 load8(const uint16_t *X, long long ld, long lon
 }
 
 // TA: A stored K x M; TB: B stored N x K.
-template <class Cfg, bool MASK, bool VEC, bool TA, bool TB>
+template <class Cfg, bool BF, bool MASK, bool VEC, bool TA, bool TB>
 __global__ __launch_bounds__(256) void hgemm_mfma_kernel(HgemmArgs p)
 {
     constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, NT = Cfg::NT;
@@ -253,7 +273,7 @@ __global__ __launch_bounds__(256) void hgemm_mfma_kernel(HgemmArgs p)
         for (int i = 0; i < Cfg::FM; ++i)
 #pragma unroll
             for (int jj = 0; jj < Cfg::FN; ++jj)
-                acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b[jj], a[i], acc[i][jj], 0, 0, 0);
+                acc[i][jj] = mfma16<BF>(b[jj], a[i], acc[i][jj]);
     };
 
     constexpr int NS = BK / 16;   // k substeps per K step
@@ -458,7 +478,7 @@ __device__ __forceinline__ unsigned frag_offset(int first, int lane, int s)
 // columns, the K % BK tail is read straight from global memory after the last
 // slice, and stores outside C are skipped); a 16-byte chunk of an
 // MN-contiguous operand may straddle M or N (see the slice count below).
-template <class Cfg, bool TA, bool TB, bool MASK>
+template <class Cfg, bool BF, bool TA, bool TB, bool MASK>
 __global__ __launch_bounds__(Cfg::NT) void hgemm_dma_kernel(HgemmArgs p)
 {
     constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, S = Cfg::STAGES;
@@ -564,7 +584,7 @@ __global__ __launch_bounds__(Cfg::NT) void hgemm_dma_kernel(HgemmArgs p)
         for (int i = 0; i < Cfg::FM; ++i)
 #pragma unroll
             for (int jj = 0; jj < Cfg::FN; ++jj)
-                acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b[jj], a[i], acc[i][jj], 0, 0, 0);
+                acc[i][jj] = mfma16<BF>(b[jj], a[i], acc[i][jj]);
     };
     auto lds_barrier = [&]() {
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
@@ -715,19 +735,19 @@ __global__ __launch_bounds__(Cfg::NT) void hgemm_dma_kernel(HgemmArgs p)
 using Hg128 = HgCfg<128, 128>;
 using Hg64 = HgCfg<64, 64>;   // for grids that 128x128 tiles would leave under-filled
 
-template <class Cfg, bool TA, bool TB>
+template <class Cfg, bool BF, bool TA, bool TB>
 void launch_cfg_kernel(const HgemmArgs &a, bool whole, bool vec, dim3 grid, hipStream_t stream)
 {
     const dim3 block(Cfg::NT);
     if (whole)
-        hipLaunchKernelGGL((hgemm_mfma_kernel<Cfg, false, true, TA, TB>), grid, block, 0, stream, a);
+        hipLaunchKernelGGL((hgemm_mfma_kernel<Cfg, BF, false, true, TA, TB>), grid, block, 0, stream, a);
     else if (vec)
-        hipLaunchKernelGGL((hgemm_mfma_kernel<Cfg, true, true, TA, TB>), grid, block, 0, stream, a);
+        hipLaunchKernelGGL((hgemm_mfma_kernel<Cfg, BF, true, true, TA, TB>), grid, block, 0, stream, a);
     else
-        hipLaunchKernelGGL((hgemm_mfma_kernel<Cfg, true, false, TA, TB>), grid, block, 0, stream, a);
+        hipLaunchKernelGGL((hgemm_mfma_kernel<Cfg, BF, true, false, TA, TB>), grid, block, 0, stream, a);
 }
 
-template <class Cfg>
+template <class Cfg, bool BF>
 hipError_t launch_cfg(const GemmProblem &q, hipStream_t stream)
 {
     HgemmArgs a;
@@ -747,13 +767,13 @@ hipError_t launch_cfg(const GemmProblem &q, hipStream_t stream)
     const bool whole = vec && q.M % Cfg::BM == 0 && q.N % Cfg::BN == 0 && q.K % Cfg::BK == 0;
     const dim3 grid(a.tiles_m * a.tiles_n, 1, q.batch);
     if (!q.transA && !q.transB)
-        launch_cfg_kernel<Cfg, false, false>(a, whole, vec, grid, stream);
+        launch_cfg_kernel<Cfg, BF, false, false>(a, whole, vec, grid, stream);
     else if (!q.transA)
-        launch_cfg_kernel<Cfg, false, true>(a, whole, vec, grid, stream);
+        launch_cfg_kernel<Cfg, BF, false, true>(a, whole, vec, grid, stream);
     else if (!q.transB)
-        launch_cfg_kernel<Cfg, true, false>(a, whole, vec, grid, stream);
+        launch_cfg_kernel<Cfg, BF, true, false>(a, whole, vec, grid, stream);
     else
-        launch_cfg_kernel<Cfg, true, true>(a, whole, vec, grid, stream);
+        launch_cfg_kernel<Cfg, BF, true, true>(a, whole, vec, grid, stream);
     return hipGetLastError();
 }
 
@@ -788,21 +808,21 @@ bool dma_ok(const GemmProblem &q)
     return aligned && shape && fits;
 }
 
-template <class Cfg, bool MASK>
+template <class Cfg, bool BF, bool MASK>
 void launch_dma_ops(const HgemmArgs &a, dim3 grid, bool tA, bool tB, hipStream_t stream)
 {
     const dim3 block(Cfg::NT);
     if (!tA && !tB)
-        hipLaunchKernelGGL((hgemm_dma_kernel<Cfg, false, false, MASK>), grid, block, 0, stream, a);
+        hipLaunchKernelGGL((hgemm_dma_kernel<Cfg, BF, false, false, MASK>), grid, block, 0, stream, a);
     else if (!tA)
-        hipLaunchKernelGGL((hgemm_dma_kernel<Cfg, false, true, MASK>), grid, block, 0, stream, a);
+        hipLaunchKernelGGL((hgemm_dma_kernel<Cfg, BF, false, true, MASK>), grid, block, 0, stream, a);
     else if (!tB)
-        hipLaunchKernelGGL((hgemm_dma_kernel<Cfg, true, false, MASK>), grid, block, 0, stream, a);
+        hipLaunchKernelGGL((hgemm_dma_kernel<Cfg, BF, true, false, MASK>), grid, block, 0, stream, a);
     else
-        hipLaunchKernelGGL((hgemm_dma_kernel<Cfg, true, true, MASK>), grid, block, 0, stream, a);
+        hipLaunchKernelGGL((hgemm_dma_kernel<Cfg, BF, true, true, MASK>), grid, block, 0, stream, a);
 }
 
-template <class Cfg>
+template <class Cfg, bool BF>
 hipError_t launch_dma(const GemmProblem &q, hipStream_t stream)
 {
     HgemmArgs a;
@@ -816,13 +836,14 @@ hipError_t launch_dma(const GemmProblem &q, hipStream_t stream)
     const dim3 grid(a.tiles_m * a.tiles_n, 1, q.batch);
     const bool whole = q.M % Cfg::BM == 0 && q.N % Cfg::BN == 0 && q.K % Cfg::BK == 0;
     if (whole)
-        launch_dma_ops<Cfg, false>(a, grid, q.transA, q.transB, stream);
+        launch_dma_ops<Cfg, BF, false>(a, grid, q.transA, q.transB, stream);
     else
-        launch_dma_ops<Cfg, true>(a, grid, q.transA, q.transB, stream);
+        launch_dma_ops<Cfg, BF, true>(a, grid, q.transA, q.transB, stream);
     return hipGetLastError();
 }
 
-hipError_t launch_hgemm(const GemmProblem &q, hipStream_t stream)
+template <bool BF>
+hipError_t launch_gemm16(const GemmProblem &q, hipStream_t stream)
 {
     // Direct-to-LDS 256x256 tiles when they give at least one tile per CU,
     // else 128x128 ones; 128x128 register-staged tiles (with bounds checks
@@ -837,13 +858,23 @@ hipError_t launch_hgemm(const GemmProblem &q, hipStream_t stream)
     const bool ok256 = dma_ok<HgDma256>(q), ok128 = dma_ok<HgDma128>(q);
     if (ok256 && ok128) {
         const long long r256 = (t256 + 255) / 256, r128 = (t128 + 255) / 256;
-        if (5 * r256 <= 2 * r128) return launch_dma<HgDma256>(q, stream);
-        return launch_dma<HgDma128>(q, stream);
+        if (5 * r256 <= 2 * r128) return launch_dma<HgDma256, BF>(q, stream);
+        return launch_dma<HgDma128, BF>(q, stream);
     }
-    if (ok256 && t256 >= 256) return launch_dma<HgDma256>(q, stream);
-    if (ok128) return launch_dma<HgDma128>(q, stream);
-    if (t128 < 256) return launch_cfg<Hg64>(q, stream);
-    return launch_cfg<Hg128>(q, stream);
+    if (ok256 && t256 >= 256) return launch_dma<HgDma256, BF>(q, stream);
+    if (ok128) return launch_dma<HgDma128, BF>(q, stream);
+    if (t128 < 256) return launch_cfg<Hg64, BF>(q, stream);
+    return launch_cfg<Hg128, BF>(q, stream);
+}
+
+hipError_t launch_hgemm(const GemmProblem &q, hipStream_t stream)
+{
+    return launch_gemm16<false>(q, stream);
+}
+
+hipError_t launch_bgemm(const GemmProblem &q, hipStream_t stream)
+{
+    return launch_gemm16<true>(q, stream);
 }
 
 }  // namespace mi355gemm

@@ -76,18 +76,35 @@ def _as_f32(x) -> np.ndarray:
     return a
 
 
+def widen_bf16(bits) -> np.ndarray:
+    """bfloat16 bit patterns (uint16) as the float32 values they denote.
+
+    A bfloat16 is the upper half of an IEEE binary32 (sign, the same 8-bit
+    exponent, 7 fraction bits), so the value is exactly the binary32 whose upper
+    16 bits are the pattern and whose lower 16 bits are zero.  The MindNotes
+    'GEMM' page names bf16 beside fp16 as an input format of its mixed-precision
+    interface (section "Batched execution and mixed precision").
+    """
+    b = np.ascontiguousarray(np.asarray(bits).reshape(-1))
+    if b.dtype != np.uint16:
+        raise TypeError(f"bfloat16 operands are uint16 bit patterns, got {b.dtype}")
+    return (b.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
 def gemm_ref(M: int, N: int, K: int, alpha: float, A, lda: int, B, ldb: int,
              beta: float, C, ldc: int, rows=None, threads: int | None = None,
-             lib_path: str = LIB, transA: bool = False, transB: bool = False):
+             lib_path: str = LIB, transA: bool = False, transB: bool = False, bf16: bool = False):
     """(ref, bound) as float64 arrays of shape (len(rows) or M, N).
 
     ``A``, ``B``, ``C`` are flat row-major buffers (see ``seeded_inputs.matrix``);
     ``C`` may be None when ``beta == 0``.  ``rows`` selects output rows.
     ``transA`` / ``transB``: A is stored K x M / B is stored N x K (op = transpose).
+    ``bf16``: A and B are bfloat16 bit patterns, widened exactly (``widen_bf16``).
     """
     lib = _load(lib_path)
-    a = _as_f32(A) if M * K > 0 else np.zeros(1, np.float32)
-    b = _as_f32(B) if K * N > 0 else np.zeros(1, np.float32)
+    conv = widen_bf16 if bf16 else _as_f32
+    a = conv(A) if M * K > 0 else np.zeros(1, np.float32)
+    b = conv(B) if K * N > 0 else np.zeros(1, np.float32)
     c = _as_f32(C) if C is not None else None
     if rows is None:
         rows_arr = None
@@ -110,7 +127,7 @@ def gemm_ref(M: int, N: int, K: int, alpha: float, A, lda: int, B, ldb: int,
 
 def gemm_ref_batched(M, N, K, alpha, A, lda, strideA, B, ldb, strideB, beta, C, ldc,
                      strideC, batch, rows=None, threads=None, lib_path: str = LIB,
-                     transA: bool = False, transB: bool = False):
+                     transA: bool = False, transB: bool = False, bf16: bool = False):
     """Strided-batched form: member b uses A + b*strideA, B + b*strideB, C + b*strideC.
 
     (MindNotes 'GEMM' page, section "Batched execution and mixed precision":
@@ -128,7 +145,7 @@ def gemm_ref_batched(M, N, K, alpha, A, lda, strideA, B, ldb, strideB, beta, C, 
         bi = b[i * strideB: i * strideB + (br - 1) * ldb + bc] if K * N else b
         ci = None if c is None else c[i * strideC: i * strideC + (M - 1) * ldc + N]
         r, bd = gemm_ref(M, N, K, alpha, ai, lda, bi, ldb, beta, ci, ldc, rows, threads, lib_path,
-                         transA, transB)
+                         transA, transB, bf16)
         refs.append(r)
         bounds.append(bd)
     return np.stack(refs), np.stack(bounds)

@@ -19,6 +19,8 @@ Value recipes (each entry of the logical matrix, filled row-major):
 
 fp16 operands are the fp32 draw rounded to binary16 with round-to-nearest-even
 (numpy's ``astype(float16)``), so both sides see the same rounded values.
+bf16 operands (``dtype="bf16"``) are the fp32 draw rounded to bfloat16 with
+round-to-nearest-even, held as uint16 bit patterns (numpy has no bfloat16).
 
 Seeds: matrix A of batch b uses ``seed + 0 + 3*b``, B uses ``seed + 1 + 3*b`` and
 C uses ``seed + 2 + 3*b``.  Padding elements of a leading dimension larger than
@@ -60,22 +62,41 @@ def draw(seed: int, n: int, kind: str = "pm1") -> np.ndarray:
     raise ValueError(f"unknown value recipe {kind!r}")
 
 
+BF16 = "bf16"
+_BF16_NAN = np.uint16(0x7FC0)
+
+
+def to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 values rounded to the nearest bfloat16 (ties to even), as uint16
+    bit patterns (the upper half of the rounded binary32).  NaN maps to 0x7FC0."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    b = x.view(np.uint32).astype(np.uint64)
+    r = ((b + np.uint64(0x7FFF) + ((b >> np.uint64(16)) & np.uint64(1))) >> np.uint64(16)).astype(np.uint16)
+    r[np.isnan(x)] = _BF16_NAN
+    return r
+
+
 def matrix(seed: int, rows: int, cols: int, ld: int | None = None, kind: str = "pm1",
            dtype=np.float32) -> np.ndarray:
     """A row-major ``rows x cols`` matrix in a flat buffer of ``rows*ld`` elements.
 
     Element (r, c) sits at index ``r*ld + c``; the ``ld - cols`` pad elements at
-    the end of each row are NaN.  ``dtype`` is float32 or float16 (the float16
-    values are the float32 draw rounded to nearest even).
+    the end of each row are NaN.  ``dtype`` is float32, float16 or ``"bf16"``
+    (the float16 and bfloat16 values are the float32 draw rounded to nearest
+    even; bfloat16 ones are returned as uint16 bit patterns).
     """
     ld = cols if ld is None else ld
     if ld < cols:
         raise ValueError("leading dimension smaller than the row width")
     vals = draw(seed, rows * cols, kind).reshape(rows, cols)
+    if isinstance(dtype, str) and dtype == BF16:
+        buf = np.full((rows, ld), _BF16_NAN, dtype=np.uint16)
+        buf[:, :cols] = to_bf16_bits(vals)
+        return buf.reshape(-1)
     if dtype == np.float16:
         vals = vals.astype(np.float16)
     elif dtype != np.float32:
-        raise ValueError("dtype must be float32 or float16")
+        raise ValueError("dtype must be float32, float16 or 'bf16'")
     buf = np.full((rows, ld), np.nan, dtype=vals.dtype)
     buf[:, :cols] = vals
     return buf.reshape(-1)
@@ -87,7 +108,8 @@ def gemm_problem(M: int, N: int, K: int, *, lda: int | None = None, ldb: int | N
                  with_c: bool = True, transA: bool = False, transB: bool = False) -> dict:
     """Operands of one GEMM C = alpha*op(A)*op(B) + beta*C (row-major, see :func:`matrix`).
 
-    Returns a dict with flat buffers ``A`` and ``B`` in ``in_dtype`` and ``C``
+    Returns a dict with flat buffers ``A`` and ``B`` in ``in_dtype`` (float32,
+    float16, or ``"bf16"`` for bfloat16 bit patterns) and ``C``
     (M x N, ldc, float32), plus the shape, leading dimensions and flags.  A is
     stored M x K, or K x M when ``transA``; B is stored K x N, or N x K when
     ``transB`` (the draw fills the stored matrix row by row either way).

@@ -58,11 +58,19 @@ def f16(lib, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc):
     return lib.gemm_f16_f32acc(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, None)
 
 
+def bf16(lib, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc):
+    return lib.gemm_bf16_f32acc(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, None)
+
+
 def bat(lib, M, N, K, alpha, A, lda, sA, B, ldb, sB, beta, C, ldc, sC, nb):
     return lib.gemm_batched_f16_f32acc(M, N, K, alpha, A, lda, sA, B, ldb, sB, beta, C, ldc, sC, nb, None)
 
 
-@pytest.mark.parametrize("fn", [f32, f16])
+def batbf(lib, M, N, K, alpha, A, lda, sA, B, ldb, sB, beta, C, ldc, sC, nb):
+    return lib.gemm_batched_bf16_f32acc(M, N, K, alpha, A, lda, sA, B, ldb, sB, beta, C, ldc, sC, nb, None)
+
+
+@pytest.mark.parametrize("fn", [f32, f16, bf16])
 def test_argument_errors(lib, fn):
     # negative sizes
     assert fn(lib, -1, 4, 4, 1.0, FAKE, 4, FAKE, 4, 0.0, FAKE, 4) == ESIZE
@@ -88,7 +96,8 @@ def test_f32_alignment_is_four_bytes(lib):
     assert f32(lib, 4, 5, 6, 1.0, FAKE, 6, FAKE + 2, 5, 0.0, FAKE, 5) == EALIGN
 
 
-def test_batched_argument_errors(lib):
+@pytest.mark.parametrize("bat", [bat, batbf])
+def test_batched_argument_errors(lib, bat):
     M, N, K = 4, 5, 6
     assert bat(lib, M, N, K, 1.0, FAKE, K, M * K, FAKE, N, K * N, 0.0, FAKE, N, M * N, -1) == ESIZE
     assert bat(lib, M, N, K, 1.0, FAKE, K, -1, FAKE, N, K * N, 0.0, FAKE, N, M * N, 2) == ELD
@@ -104,10 +113,11 @@ def test_batched_argument_errors(lib):
 
 def test_empty_problems_are_noops(lib):
     # No HIP call happens for these, so they succeed without a GPU.
-    for fn in (f32, f16):
+    for fn in (f32, f16, bf16):
         assert fn(lib, 0, 5, 6, 1.0, None, 6, None, 5, 0.0, None, 5) == OK
         assert fn(lib, 4, 0, 6, 1.0, None, 6, None, 1, 0.0, None, 1) == OK
     assert bat(lib, 4, 5, 6, 1.0, None, 6, 0, None, 5, 0, 0.0, None, 5, 0, 0) == OK
+    assert batbf(lib, 4, 5, 6, 1.0, None, 6, 0, None, 5, 0, 0.0, None, 5, 0, 0) == OK
 
 
 def test_binding_refuses_cpu_tensors():
@@ -131,7 +141,11 @@ def f16x(lib, tA, tB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc):
     return lib.gemm_f16_f32acc_ex(tA, tB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, None)
 
 
-@pytest.mark.parametrize("fn", [f32x, f16x])
+def bf16x(lib, tA, tB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc):
+    return lib.gemm_bf16_f32acc_ex(tA, tB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, None)
+
+
+@pytest.mark.parametrize("fn", [f32x, f16x, bf16x])
 def test_transposed_leading_dimensions(lib, fn):
     M, N, K = 4, 5, 6
     # flags other than 0 / 1, checked first
@@ -151,9 +165,10 @@ def test_transposed_leading_dimensions(lib, fn):
     assert fn(lib, 1, 0, M, N, K, 1.0, None, M, FAKE, N, 0.0, FAKE, N) == ENULL
 
 
-def test_batched_transposed_errors(lib):
+@pytest.mark.parametrize("name", ["gemm_batched_f16_f32acc_ex", "gemm_batched_bf16_f32acc_ex"])
+def test_batched_transposed_errors(lib, name):
     M, N, K = 4, 5, 6
-    bx = lib.gemm_batched_f16_f32acc_ex
+    bx = getattr(lib, name)
     assert bx(3, 0, M, N, K, 1.0, FAKE, K, M * K, FAKE, N, K * N, 0.0, FAKE, N, M * N, 2, None) == EOP
     assert bx(1, 0, M, N, K, 1.0, FAKE, M - 1, M * K, FAKE, N, K * N, 0.0, FAKE, N, M * N, 2, None) == ELD
     assert bx(0, 1, M, N, K, 1.0, FAKE, K, M * K, FAKE, N, K * N, 0.0, FAKE, N, M * N, 0, None) == ELD
@@ -177,3 +192,15 @@ def test_grid_too_large_is_refused(lib):
     big = 2**31 - 1
     assert f32(lib, big, big, 1, 1.0, FAKE, 1, FAKE, big, 0.0, FAKE, big) == ESIZE
     assert f16(lib, big, big, 1, 1.0, FAKE, 1, FAKE, big, 0.0, FAKE, big) == ESIZE
+    assert bf16(lib, big, big, 1, 1.0, FAKE, 1, FAKE, big, 0.0, FAKE, big) == ESIZE
+
+
+def test_binding_checks_bf16_dtype():
+    torch = pytest.importorskip("torch")
+    h = torch.zeros(16, dtype=torch.float16)
+    # the binding refuses a CPU tensor, and checks the dtype of device tensors
+    with pytest.raises(ValueError):
+        dg.gemm_bf16_f32acc(4, 4, 4, 1.0, h, 4, h, 4, 0.0, h, 4, stream=0)
+    with pytest.raises(dg.GemmError) as e:
+        dg.gemm_batched_bf16_f32acc_ex(0, 2, 4, 4, 4, 1.0, FAKE, 4, 16, FAKE, 4, 16, 0.0, FAKE, 4, 16, 2, stream=0)
+    assert e.value.status == EOP

@@ -253,6 +253,67 @@ def test_pin(pin):
     pin(oracle.LIB)
 
 
+def test_bf16_widening_fixed_values():
+    """A bfloat16 pattern is the upper half of a binary32 (1 sign, 8 exponent, 7
+    fraction bits); the values of a few patterns worked out by hand."""
+    cases = {0x3F80: 1.0, 0xBF80: -1.0, 0x4000: 2.0, 0x3E80: 0.25, 0xC0A0: -5.0,
+             0x4049: 3.140625, 0x3F81: 1.0 + 2.0**-7, 0x0000: 0.0, 0x0001: 2.0**-133,
+             0x7F7F: (2.0 - 2.0**-7) * 2.0**127}
+    got = oracle.widen_bf16(np.array(list(cases), dtype=np.uint16))
+    for (bits, want), g in zip(cases.items(), got):
+        assert float(g) == want, hex(bits)
+    special = oracle.widen_bf16(np.array([0x8000, 0x7F80, 0xFF80, 0x7FC0], dtype=np.uint16))
+    assert special[0] == 0.0 and np.signbit(special[0])
+    assert special[1] == np.inf and special[2] == -np.inf and np.isnan(special[3])
+    with pytest.raises(TypeError):
+        oracle.widen_bf16(np.zeros(4, np.float16))
+
+
+def test_bf16_inputs_are_round_to_nearest_even():
+    """The bf16 input recipe: the fp32 draw rounded to nearest, ties to even, checked
+    against torch's float32 -> bfloat16 conversion and two hand-made ties."""
+    torch = pytest.importorskip("torch")
+    x = si.draw(11, 50000)
+    want = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(si.to_bf16_bits(x), want)
+    ties = np.array([1.0 + 2.0**-8, 1.0 + 3 * 2.0**-8, -(1.0 + 2.0**-8)], dtype=np.float32)
+    assert si.to_bf16_bits(ties).tolist() == [0x3F80, 0x3F82, 0xBF80]
+    buf = si.matrix(3, 4, 5, 7, "pm1", "bf16")   # pads are NaN patterns
+    assert buf.dtype == np.uint16 and np.isnan(oracle.widen_bf16(buf).reshape(4, 7)[:, 5:]).all()
+
+
+def test_bf16_problem_is_the_problem_of_the_values_it_denotes():
+    """On bf16 operands the oracle computes exactly what it computes on the float32
+    values the patterns denote (widened here by torch, not by the oracle), in all four
+    storage combinations; and on small-integer bf16 entries it equals exact rational
+    arithmetic."""
+    torch = pytest.importorskip("torch")
+
+    def torch_widen(bits):
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).float().numpy()
+
+    for t, (tA, tB) in enumerate(itertools.product((False, True), repeat=2)):
+        M, N, K = 7, 5, 19
+        p = si.gemm_problem(M, N, K, in_dtype="bf16", seed=500 + t, transA=tA, transB=tB,
+                            lda=(M if tA else K) + 2, ldb=(K if tB else N) + 1)
+        r16, b16 = oracle.gemm_ref(M, N, K, 1.5, p["A"], p["lda"], p["B"], p["ldb"], -0.5, p["C"],
+                                   p["ldc"], transA=tA, transB=tB, bf16=True)
+        r32, b32 = oracle.gemm_ref(M, N, K, 1.5, torch_widen(p["A"]), p["lda"], torch_widen(p["B"]),
+                                   p["ldb"], -0.5, p["C"], p["ldc"], transA=tA, transB=tB)
+        assert np.array_equal(r16, r32) and np.array_equal(b16, b32)
+    for t, (M, N, K) in enumerate([(3, 4, 5), (6, 2, 9), (5, 5, 16)]):
+        p = si.gemm_problem(M, N, K, in_dtype="bf16", kind="int4", seed=600 + t)
+        ref, bound = oracle.gemm_ref(M, N, K, 1.5, p["A"], K, p["B"], N, -0.5, p["C"], N, bf16=True)
+        # the int4 draws are exact in bf16, so the float32 draws are the values the patterns denote
+        A = si.matrix(600 + t, M, K, K, "int4").reshape(M, K).astype(np.float64)
+        B = si.matrix(601 + t, K, N, N, "int4").reshape(K, N).astype(np.float64)
+        C = si.matrix(602 + t, M, N, N, "int4").reshape(M, N).astype(np.float64)
+        er, eb = _exact(A, B, C, 1.5, -0.5)
+        for i in range(M):
+            for j in range(N):
+                assert Fraction(ref[i, j]) == er[i][j] and Fraction(bound[i, j]) == eb[i][j]
+
+
 def test_rejects_bad_arguments():
     p = si.gemm_problem(4, 4, 4)
     with pytest.raises(ValueError):

@@ -41,19 +41,24 @@ def note(msg: str):
 
 
 def to_dev(buf):
-    return torch.from_numpy(np.ascontiguousarray(buf)).to("cuda")
+    buf = np.ascontiguousarray(buf)
+    if buf.dtype == np.uint16:   # bfloat16 bit patterns
+        return torch.from_numpy(buf.view(np.int16)).view(torch.bfloat16).to("cuda")
+    return torch.from_numpy(buf).to("cuda")
+
+
+IN_DTYPE = {"f32": np.float32, "f16": np.float16, "bf16": "bf16"}
 
 
 def call(kind, p, alpha, beta, dA, dB, dC, stream=None):
     M, N, K = p["M"], p["N"], p["K"]
     tA, tB = int(p.get("transA", False)), int(p.get("transB", False))
     if tA or tB:   # the op(A)/op(B) entry points
-        fn = dg.gemm_f32_ex if kind == "f32" else dg.gemm_f16_f32acc_ex
+        fn = {"f32": dg.gemm_f32_ex, "f16": dg.gemm_f16_f32acc_ex, "bf16": dg.gemm_bf16_f32acc_ex}[kind]
         fn(tA, tB, M, N, K, alpha, dA, p["lda"], dB, p["ldb"], beta, dC, p["ldc"], stream)
-    elif kind == "f32":
-        dg.gemm_f32(M, N, K, alpha, dA, p["lda"], dB, p["ldb"], beta, dC, p["ldc"], stream)
     else:
-        dg.gemm_f16_f32acc(M, N, K, alpha, dA, p["lda"], dB, p["ldb"], beta, dC, p["ldc"], stream)
+        fn = {"f32": dg.gemm_f32, "f16": dg.gemm_f16_f32acc, "bf16": dg.gemm_bf16_f32acc}[kind]
+        fn(M, N, K, alpha, dA, p["lda"], dB, p["ldb"], beta, dC, p["ldc"], stream)
 
 
 def rows_of(dC, M, N, ldc, rows=None):
@@ -76,7 +81,7 @@ def to_dev_offset(buf, offset):
 
 def run_and_check(kind, M, N, K, alpha, beta, *, kind_vals="pm1", lda=None, ldb=None, ldc=None,
                   sample=None, exact=False, seed=42, c_nan=False, transA=False, transB=False, offset=0):
-    in_dtype = np.float32 if kind == "f32" else np.float16
+    in_dtype = IN_DTYPE[kind]
     note(f"{kind} M={M} N={N} K={K} alpha={alpha} beta={beta} vals={kind_vals} lda={lda} ldb={ldb} "
          f"ldc={ldc} sample={sample} seed={seed} transA={int(transA)} transB={int(transB)} offset={offset}")
     p = si.gemm_problem(M, N, K, lda=lda, ldb=ldb, ldc=ldc, in_dtype=in_dtype, kind=kind_vals, seed=seed,
@@ -91,7 +96,8 @@ def run_and_check(kind, M, N, K, alpha, beta, *, kind_vals="pm1", lda=None, ldb=
     rows = si.sample_rows(seed, M, sample) if sample else None
     got = rows_of(dC, M, N, p["ldc"], rows)
     ref, bound = oracle.gemm_ref(M, N, K, alpha, p["A"], p["lda"], p["B"], p["ldb"], beta,
-                                 None if beta == 0 else p["C"], p["ldc"], rows=rows, transA=transA, transB=transB)
+                                 None if beta == 0 else p["C"], p["ldc"], rows=rows, transA=transA, transB=transB,
+                                 bf16=kind == "bf16")
     if exact:
         want = ref.astype(np.float32)
         bad = np.argwhere(got != want)
@@ -139,39 +145,44 @@ def test_cfg4_hgemm(n):
 
 
 def batched_check(M, N, K, nb, alpha, beta, *, kind_vals="pm1", sample=None, exact=False, seed=42,
-                  pad=0, share_a=False, transA=False, transB=False):
-    note(f"batched M={M} N={N} K={K} batch={nb} alpha={alpha} beta={beta} vals={kind_vals} "
+                  pad=0, share_a=False, transA=False, transB=False, fmt="f16"):
+    note(f"batched {fmt} M={M} N={N} K={K} batch={nb} alpha={alpha} beta={beta} vals={kind_vals} "
          f"sample={sample} pad={pad} share_a={share_a} transA={int(transA)} transB={int(transB)}")
+    bf = fmt == "bf16"
+    in_np = np.uint16 if bf else np.float16
     a_rows, a_cols = (K, M) if transA else (M, K)
     b_rows, b_cols = (N, K) if transB else (K, N)
     lda, ldb, ldc = a_cols + pad, b_cols + pad, N + pad
-    probs = [si.gemm_problem(M, N, K, lda=lda, ldb=ldb, ldc=ldc, in_dtype=np.float16, kind=kind_vals,
+    probs = [si.gemm_problem(M, N, K, lda=lda, ldb=ldb, ldc=ldc, in_dtype=IN_DTYPE[fmt], kind=kind_vals,
                              seed=seed, batch=b, transA=transA, transB=transB) for b in range(nb)]
     sA = 0 if share_a else a_rows * lda + 8 * pad
     sB, sC = b_rows * ldb + 8 * pad, M * ldc + 8 * pad
 
     def pack(key, stride, n_el, dtype):
-        buf = np.full(stride * (nb - 1) + n_el if stride else n_el, np.nan, dtype=dtype)
+        fill = 0x7FC0 if dtype == np.uint16 else np.nan   # NaN between members
+        buf = np.full(stride * (nb - 1) + n_el if stride else n_el, fill, dtype=dtype)
         for b in range(nb if stride else 1):
             buf[b * stride: b * stride + n_el] = probs[b][key]
         return buf
 
-    A = pack("A", sA, a_rows * lda, np.float16)
-    B = pack("B", sB, b_rows * ldb, np.float16)
+    A = pack("A", sA, a_rows * lda, in_np)
+    B = pack("B", sB, b_rows * ldb, in_np)
     C = pack("C", sC, M * ldc, np.float32)
     dA, dB, dC = to_dev(A), to_dev(B), to_dev(C)
     if transA or transB:
-        dg.gemm_batched_f16_f32acc_ex(int(transA), int(transB), M, N, K, alpha, dA, lda, sA, dB, ldb, sB, beta,
-                                      dC, ldc, sC, nb)
+        fn = dg.gemm_batched_bf16_f32acc_ex if bf else dg.gemm_batched_f16_f32acc_ex
+        fn(int(transA), int(transB), M, N, K, alpha, dA, lda, sA, dB, ldb, sB, beta, dC, ldc, sC, nb)
     else:
-        dg.gemm_batched_f16_f32acc(M, N, K, alpha, dA, lda, sA, dB, ldb, sB, beta, dC, ldc, sC, nb)
+        fn = dg.gemm_batched_bf16_f32acc if bf else dg.gemm_batched_f16_f32acc
+        fn(M, N, K, alpha, dA, lda, sA, dB, ldb, sB, beta, dC, ldc, sC, nb)
     torch.cuda.synchronize()
     rows = si.sample_rows(seed, M, sample) if sample else None
     worst = 0.0
     for b in range(nb):
         got = rows_of(dC[b * sC:], M, N, ldc, rows)
         ref, bound = oracle.gemm_ref(M, N, K, alpha, A[b * sA:], lda, B[b * sB:], ldb, beta,
-                                     C[b * sC: b * sC + M * ldc], ldc, rows=rows, transA=transA, transB=transB)
+                                     C[b * sC: b * sC + M * ldc], ldc, rows=rows, transA=transA, transB=transB,
+                                     bf16=bf)
         if exact:
             assert np.array_equal(got, ref.astype(np.float32)), f"member {b} not bit-exact"
         e = oracle.normalized_error(got, ref, bound)
@@ -721,6 +732,61 @@ def test_random_sweep_direct_to_lds(case):
 
 
 # ------------------------------------------------------------------ graph capture
+# ------------------------------------------------------------------ bfloat16 inputs
+# The bf16 entry points run the HGEMM kernels with the bf16 matrix-core op, so
+# these cases cover each of those kernels once more with bfloat16 inputs.
+
+@pytest.mark.parametrize("n", [2048, 4096])
+def test_bf16_square(n):
+    # 128x128 (2048) and 256x256 (4096) direct-to-LDS tiles
+    run_and_check("bf16", n, n, n, 1.0, 0.0, sample=None if n <= 2048 else 256, c_nan=True, seed=n)
+    run_and_check("bf16", n, n, n, 1.0, 0.0, kind_vals="int4", exact=True, sample=128, seed=7)
+
+
+@pytest.mark.parametrize("tA,tB", [(False, False)] + OPS)
+def test_bf16_ragged_and_transposed(tA, tB):
+    run_and_check("bf16", 1000, 1200, 776, 1.5, -0.5, transA=tA, transB=tB)              # masked tiles
+    run_and_check("bf16", 2050, 2046, 320, 1.5, -0.5, transA=tA, transB=tB, sample=64)   # straddling chunks
+    run_and_check("bf16", 300, 260, 700, 1.0, 1.0, transA=tA, transB=tB)
+    run_and_check("bf16", 256, 256, 128, 1.0, 0.0, kind_vals="int4", exact=True, transA=tA, transB=tB)
+
+
+def test_bf16_register_kernels():
+    # odd leading dimensions, a 2-byte aligned pointer and K below the ring: the
+    # register-staged kernel
+    run_and_check("bf16", 500, 400, 300, 1.5, -0.5, lda=301, ldb=401)
+    run_and_check("bf16", 384, 256, 260, 1.0, 0.0, offset=1)
+    run_and_check("bf16", 1024, 1024, 64, 1.0, 0.0, kind_vals="int4", exact=True)
+
+
+def test_bf16_batched():
+    batched_check(1024, 1024, 1024, 16, 1.0, 1.0, sample=64, fmt="bf16")
+    batched_check(33, 65, 17, 4, 1.0, 0.0, kind_vals="int4", exact=True, pad=1, fmt="bf16")
+    batched_check(200, 136, 72, 3, 1.0, 1.0, pad=3, share_a=True, transA=True, transB=True, fmt="bf16")
+
+
+def test_bf16_and_fp16_agree_on_values_both_hold():
+    # entries that are exact in both formats (small integers, and multiples of
+    # 2**-7 below 1) give the same products, and the two paths add them in the
+    # same order: identical bits
+    M, N, K = 2048, 2048, 1024
+    for kind_vals, seed in (("int4", 21), ("pm1", 22)):
+        ph = si.gemm_problem(M, N, K, in_dtype=np.float16, kind=kind_vals, seed=seed)
+        if kind_vals == "pm1":   # round to multiples of 2**-7, exact in both formats
+            ph["A"] = (np.round(ph["A"].astype(np.float32) * 128) / 128).astype(np.float16)
+            ph["B"] = (np.round(ph["B"].astype(np.float32) * 128) / 128).astype(np.float16)
+        a_bf = si.to_bf16_bits(ph["A"].astype(np.float32))
+        b_bf = si.to_bf16_bits(ph["B"].astype(np.float32))
+        out = []
+        for fn, a, b in ((dg.gemm_f16_f32acc, ph["A"], ph["B"]), (dg.gemm_bf16_f32acc, a_bf, b_bf)):
+            dC = torch.zeros(M * N, dtype=torch.float32, device="cuda")
+            fn(M, N, K, 1.0, to_dev(a), K, to_dev(b), N, 0.0, dC, N)
+            torch.cuda.synchronize()
+            out.append(dC.cpu())
+        note(f"bf16 vs fp16 {kind_vals}: equal={torch.equal(out[0], out[1])}")
+        assert torch.equal(out[0], out[1])
+
+
 def test_graph_capture_replays_match_eager():
     # the library enqueues plain kernel launches on the caller's stream (no memset,
     # no allocation), so a captured sequence replays exactly; every replay is
