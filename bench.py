@@ -277,7 +277,8 @@ def write_trace(stats_csv: str, trace_csv: str, bench_log: str) -> int:
         out.append(f"| `{short(name)}` | {len(tail)} | {sum(tail) / len(tail) / 1e3:.1f} | "
                    f"{bench_line['per_kernel'][kind]['avg_ms'] * 1e3:.1f} |")
     out += ["", "The bench averages include the gap between an event and its kernel; rocprofv3 times "
-                "the kernel alone. Both kernels are the NN (no transpose) instantiations."]
+                "the kernel alone. Both kernels are the NN (no transpose) instantiations; the first flag of "
+                "the HGEMM kernel selects the input format (false: fp16)."]
     path = os.path.join(ROOT, "profiles", "kernel_trace_sgemm4096x4096x1024_hgemm4096cube.md")
     with open(path, "w") as f:
         f.write("\n".join(out) + "\n")
