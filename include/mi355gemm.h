@@ -127,12 +127,13 @@ int gemm_batched_f16_f32acc_ex(int transA, int transB, int M, int N, int K, floa
 /*
  * bfloat16 inputs.  The MindNotes page's mixed-precision interface (section
  * "Batched execution and mixed precision") takes either fp16 or bf16 inputs
- * with fp32 accumulation.  These entry points are the bf16 forms of the four
- * above: A and B hold bfloat16 values (the upper 16 bits of an IEEE binary32,
- * as uint16_t bit patterns), products are formed exactly and accumulated in
- * fp32; alpha, beta and C are fp32.  Arguments, layout, ownership, status
- * codes and the accuracy statement are as for gemm_f16_f32acc and
- * gemm_batched_f16_f32acc (and their _ex forms).
+ * with fp32 accumulation.  These four entry points are the bf16 forms of
+ * gemm_f16_f32acc, gemm_batched_f16_f32acc, gemm_f16_f32acc_ex and
+ * gemm_batched_f16_f32acc_ex, in that order: A and B hold bfloat16 values (the
+ * upper 16 bits of an IEEE binary32, as uint16_t bit patterns), products are
+ * formed exactly and accumulated in fp32; alpha, beta and C are fp32.
+ * Arguments, layout, ownership, status codes and the accuracy statement are
+ * as for the fp16 forms.
  */
 int gemm_bf16_f32acc(int M, int N, int K, float alpha,
                      const uint16_t *A, int lda, const uint16_t *B, int ldb,
