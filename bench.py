@@ -253,11 +253,11 @@ def write_trace(stats_csv: str, trace_csv: str, bench_log: str) -> int:
             (int(r["Start_Timestamp"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
     line = next(l for l in open(bench_log) if l.startswith('{"metric"'))
     bench_line = json.loads(line)
-    cmd = (f"cd /tmp && rocprofv3 --kernel-trace --stats --output-format csv -d $R/gpurun_out/prof -o run -- "
+    cmd = (f"cd /tmp && rocprofv3 --kernel-trace --stats --output-format csv -d $OUT/prof -o run -- "
            f"python3 $R/bench.py --no-cpu --no-extra --steps {TRACE_STEPS} --warmup {TRACE_WARMUP} "
-           f"> $R/gpurun_out/prof.log\n"
-           f"python3 $R/bench.py --write-trace $R/gpurun_out/prof/run_kernel_stats.csv "
-           f"$R/gpurun_out/prof/run_kernel_trace.csv $R/gpurun_out/prof.log   # R = repository root")
+           f"> $OUT/prof.log\n"
+           f"python3 $R/bench.py --write-trace $OUT/prof/run_kernel_stats.csv "
+           f"$OUT/prof/run_kernel_trace.csv $OUT/prof.log   # R = repository root, OUT = an output directory")
     out = ["# rocprofv3 kernel trace: bench step (SGEMM 4096x4096x1024 fp32 + HGEMM 4096^3 fp16->fp32)", "",
            "Commands (run on one MI355X):", "", "```", cmd, "```", "",
            "All launches (warm-up included):", "",
@@ -317,11 +317,11 @@ def write_counters(csv_paths) -> int:
     kinds = [k for k in ("sgemm", "hgemm") if k in mean]
     counters = sorted({c for k in kinds for c in mean[k]})
     cmds = "\n".join(
-        f"cd /tmp && rocprofv3 --pmc {p} --output-format csv -d $R/gpurun_out/counters{i} -o c -- "
+        f"cd /tmp && rocprofv3 --pmc {p} --output-format csv -d $OUT/counters{i} -o c -- "
         f"python3 $R/bench.py --no-cpu --no-extra --steps 3 --warmup 1" for i, p in enumerate(COUNTER_PASSES, 1))
     cmds += ("\npython3 $R/bench.py --write-counters " +
-             " ".join(f"$R/gpurun_out/counters{i}/c_counter_collection.csv" for i in range(1, len(COUNTER_PASSES) + 1)) +
-             "   # R = repository root")
+             " ".join(f"$OUT/counters{i}/c_counter_collection.csv" for i in range(1, len(COUNTER_PASSES) + 1)) +
+             "   # R = repository root, OUT = an output directory")
     lines = ["# rocprofv3 counters per launch: bench step kernels (SGEMM 4096x4096x1024 fp32, "
              "HGEMM 4096^3 fp16->fp32)", "",
              "Commands (one MI355X; each pass is a run of its own):", "", "```", cmds, "```", "",
@@ -397,12 +397,12 @@ def write_traffic(fetch_csv: str, write_csv: str) -> int:
                       "hbm_bytes_per_launch": total, "algorithmic_bytes": alg[kind]}
         rows.append(f"| {kind} | {workloads[kind]} | {f * scale_f / 1e6:.1f} | {w * scale_w / 1e6:.1f} | "
                     f"{total / 1e6:.1f} | {alg[kind] / 1e6:.1f} | {total / alg[kind]:.2f} |")
-    cmd = ("cd /tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d $R/gpurun_out/traffic_fetch -o t -- "
+    cmd = ("cd /tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d $OUT/traffic_fetch -o t -- "
            "python3 $R/bench.py --no-cpu --no-extra --steps 3 --warmup 1 --copy-calibration\n"
-           "cd /tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv -d $R/gpurun_out/traffic_write -o t -- "
+           "cd /tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv -d $OUT/traffic_write -o t -- "
            "python3 $R/bench.py --no-cpu --no-extra --steps 3 --warmup 1 --copy-calibration\n"
-           "python3 $R/bench.py --write-traffic $R/gpurun_out/traffic_fetch/t_counter_collection.csv "
-           "$R/gpurun_out/traffic_write/t_counter_collection.csv   # R = repository root")
+           "python3 $R/bench.py --write-traffic $OUT/traffic_fetch/t_counter_collection.csv "
+           "$OUT/traffic_write/t_counter_collection.csv   # R = repository root, OUT = an output directory")
     text = ("# HBM traffic per launch: bench step kernels (rocprofv3 FETCH_SIZE / WRITE_SIZE)\n\n"
             f"Commands (one MI355X):\n\n```\n{cmd}\n```\n\n"
             f"Calibration: a plain elementwise copy of {COPY_BYTES >> 20} MiB reads and writes {COPY_BYTES} bytes; "
