@@ -257,22 +257,27 @@ def test_aligned_lds_with_ragged_tails(kind):
     run_and_check(kind, 513, 515, 517, 1.5, -0.5, lda=520, ldb=520, ldc=520, kind_vals="int4", exact=True)
 
 
-@pytest.mark.parametrize("kind", ["f32", "f16"])
+@pytest.mark.parametrize("kind", ["f32", "f16", "bf16"])
 def test_beta_zero_does_not_read_c(kind):
     run_and_check(kind, 130, 70, 40, 1.0, 0.0, c_nan=True)
 
 
-@pytest.mark.parametrize("kind", ["f32", "f16"])
+def nan_like(buf):
+    """A buffer of the same shape and element type holding NaN (0x7FC0 for bf16 patterns)."""
+    return np.full_like(buf, 0x7FC0) if buf.dtype == np.uint16 else np.full_like(buf, np.nan)
+
+
+@pytest.mark.parametrize("kind", ["f32", "f16", "bf16"])
 def test_quick_returns(kind):
     note(f"{kind} quick returns")
     M, N = 37, 45
     for K, alpha, beta in [(0, 1.0, -0.5), (16, 0.0, 1.5), (0, 1.0, 0.0), (16, 0.0, 0.0)]:
-        p = si.gemm_problem(M, N, max(K, 1), in_dtype=np.float32 if kind == "f32" else np.float16)
+        p = si.gemm_problem(M, N, max(K, 1), in_dtype=IN_DTYPE[kind])
         p["K"] = K
         C0 = p["C"].copy()
         dC = to_dev(C0 if beta != 0 else np.full_like(C0, np.nan))
-        dA = to_dev(np.full_like(p["A"], np.nan))   # A and B must not be read
-        dB = to_dev(np.full_like(p["B"], np.nan))
+        dA = to_dev(nan_like(p["A"]))   # A and B must not be read
+        dB = to_dev(nan_like(p["B"]))
         call(kind, dict(p, lda=max(K, 1)), alpha, beta, dA, dB, dC)
         torch.cuda.synchronize()
         got = dC.cpu().numpy()
@@ -286,27 +291,25 @@ def test_quick_returns(kind):
     assert np.array_equal(dC.cpu().numpy(), np.arange(12, dtype=np.float32))
 
 
-@pytest.mark.parametrize("kind", ["f32", "f16"])
+@pytest.mark.parametrize("kind", ["f32", "f16", "bf16"])
 def test_misaligned_pointers(kind):
     note(f"{kind} operands offset by one element from a 16-byte boundary")
     M, N, K = 190, 210, 150
-    in_dtype = np.float32 if kind == "f32" else np.float16
-    p = si.gemm_problem(M, N, K, in_dtype=in_dtype, seed=21)
-    dA = to_dev(np.concatenate([np.zeros(1, in_dtype), p["A"]]))[1:]
-    dB = to_dev(np.concatenate([np.zeros(1, in_dtype), p["B"]]))[1:]
+    p = si.gemm_problem(M, N, K, in_dtype=IN_DTYPE[kind], seed=21)
+    dA = to_dev(np.concatenate([np.zeros(1, p["A"].dtype), p["A"]]))[1:]
+    dB = to_dev(np.concatenate([np.zeros(1, p["B"].dtype), p["B"]]))[1:]
     dC = to_dev(np.concatenate([np.zeros(1, np.float32), p["C"]]))[1:]
     call(kind, p, 1.5, -0.5, dA, dB, dC)
     torch.cuda.synchronize()
-    ref, bound = oracle.gemm_ref(M, N, K, 1.5, p["A"], K, p["B"], N, -0.5, p["C"], N)
+    ref, bound = oracle.gemm_ref(M, N, K, 1.5, p["A"], K, p["B"], N, -0.5, p["C"], N, bf16=kind == "bf16")
     assert oracle.normalized_error(rows_of(dC, M, N, N), ref, bound) <= TOL
 
 
 @pytest.mark.parametrize("kind,M,N,K", [("f32", 1001, 777, 513), ("f16", 4096, 4096, 4096),
-                                        ("f32", 4096, 4096, 1024)])
+                                        ("f32", 4096, 4096, 1024), ("bf16", 2048, 2048, 2048)])
 def test_deterministic(kind, M, N, K):
     note(f"{kind} determinism M={M} N={N} K={K}")
-    in_dtype = np.float32 if kind == "f32" else np.float16
-    p = si.gemm_problem(M, N, K, in_dtype=in_dtype, seed=33)
+    p = si.gemm_problem(M, N, K, in_dtype=IN_DTYPE[kind], seed=33)
     dA, dB = to_dev(p["A"]), to_dev(p["B"])
     outs = []
     for _ in range(2):
