@@ -576,15 +576,14 @@ def test_transposed_batched(tA, tB):
     batched_check(200, 136, 72, 3, 1.0, 1.0, pad=3, share_a=True, transA=tA, transB=tB)
 
 
-@pytest.mark.parametrize("kind", ["f32", "f16"])
+@pytest.mark.parametrize("kind", ["f32", "f16", "bf16"])
 @pytest.mark.parametrize("tA,tB", OPS)
 def test_transposed_matches_untransposed(kind, tA, tB):
     # the same logical product through the plain and the op() entry points gives
     # the same bits (all four combinations use one k order)
     M, N, K = (4096, 4096, 512)
     note(f"{kind} op() vs plain M={M} N={N} K={K} transA={int(tA)} transB={int(tB)}")
-    in_dtype = np.float32 if kind == "f32" else np.float16
-    p = si.gemm_problem(M, N, K, in_dtype=in_dtype, seed=61)
+    p = si.gemm_problem(M, N, K, in_dtype=IN_DTYPE[kind], seed=61)
     A2 = si.logical_transpose(p["A"], M, K) if tA else p["A"]
     B2 = si.logical_transpose(p["B"], K, N) if tB else p["B"]
     q = dict(p, transA=tA, transB=tB, lda=(M if tA else K), ldb=(K if tB else N))
