@@ -37,7 +37,7 @@
 //   * hgemm_dma_kernel -- operands whose rows start 4-byte aligned.  K slices
 //     go from global memory straight into an LDS ring (direct-to-LDS loads, the
 //     gfx950 form of the page's asynchronous double buffering): 256x256 tiles
-//     with two slots of 64 k, or 128x128 tiles with four.  Ragged M, N and K
+//     with two slots of 64 k, or 128x128 or 64x128 tiles with four.  Ragged M, N and K
 //     are handled by clamped slice loads, a K tail read from global memory and
 //     masked stores;
 //   * hgemm_mfma_kernel -- everything else: 128x128 (64x64 for small grids)
@@ -784,6 +784,19 @@ using HgDma256 = HgDmaCfg<256, 256, 2, 2, 4, 64>;
 // 128x128 tile, 8 waves (2 x 4) of 64x32, BK = 64, four slots of 32 KB: for
 // grids that 256x256 tiles would leave under-filled.
 using HgDma128 = HgDmaCfg<128, 128, 4, 2, 4, 64>;
+// 64x128 tile, 8 waves (2 x 4) of 32x32, four slots of 24 KB: for grids that
+// 128x128 tiles leave at most half filled.  Its A slice is 64 wide, so it takes
+// only A stored M x K (B either way).
+using HgDma64x128 = HgDmaCfg<64, 128, 4, 2, 4, 64>;
+
+// Storage combinations a tile can take: an MN-contiguous slice needs rows of
+// at least 16 chunks, i.e. BM >= 128 for A stored K x M and BN >= 128 for B
+// stored K x N.
+template <class Cfg>
+constexpr bool dma_orientation_ok(bool tA, bool tB)
+{
+    return (!tA || Cfg::BM >= 128) && (tB || Cfg::BN >= 128);
+}
 
 // The direct-to-LDS kernel applies: 4-byte aligned operand rows, at least
 // STAGES whole slices of k, an MN-contiguous operand (A stored K x M, B stored
@@ -805,21 +818,26 @@ bool dma_ok(const GemmProblem &q)
     // per-lane offsets within one slice are 32-bit: rows of the slice times ld
     const long long rows_a = q.transA ? Cfg::BK : Cfg::BM, rows_b = q.transB ? Cfg::BN : Cfg::BK;
     const bool fits = rows_a * q.lda * 2 < (1LL << 31) && rows_b * q.ldb * 2 < (1LL << 31);
-    return aligned && shape && fits;
+    return aligned && shape && fits && dma_orientation_ok<Cfg>(q.transA, q.transB);
 }
 
 template <class Cfg, bool BF, bool MASK>
 void launch_dma_ops(const HgemmArgs &a, dim3 grid, bool tA, bool tB, hipStream_t stream)
 {
     const dim3 block(Cfg::NT);
-    if (!tA && !tB)
-        hipLaunchKernelGGL((hgemm_dma_kernel<Cfg, BF, false, false, MASK>), grid, block, 0, stream, a);
-    else if (!tA)
-        hipLaunchKernelGGL((hgemm_dma_kernel<Cfg, BF, false, true, MASK>), grid, block, 0, stream, a);
-    else if (!tB)
-        hipLaunchKernelGGL((hgemm_dma_kernel<Cfg, BF, true, false, MASK>), grid, block, 0, stream, a);
-    else
-        hipLaunchKernelGGL((hgemm_dma_kernel<Cfg, BF, true, true, MASK>), grid, block, 0, stream, a);
+    if (!tA && !tB) {
+        if constexpr (dma_orientation_ok<Cfg>(false, false))
+            hipLaunchKernelGGL((hgemm_dma_kernel<Cfg, BF, false, false, MASK>), grid, block, 0, stream, a);
+    } else if (!tA) {
+        if constexpr (dma_orientation_ok<Cfg>(false, true))
+            hipLaunchKernelGGL((hgemm_dma_kernel<Cfg, BF, false, true, MASK>), grid, block, 0, stream, a);
+    } else if (!tB) {
+        if constexpr (dma_orientation_ok<Cfg>(true, false))
+            hipLaunchKernelGGL((hgemm_dma_kernel<Cfg, BF, true, false, MASK>), grid, block, 0, stream, a);
+    } else {
+        if constexpr (dma_orientation_ok<Cfg>(true, true))
+            hipLaunchKernelGGL((hgemm_dma_kernel<Cfg, BF, true, true, MASK>), grid, block, 0, stream, a);
+    }
 }
 
 template <class Cfg, bool BF>
@@ -846,8 +864,9 @@ template <bool BF>
 hipError_t launch_gemm16(const GemmProblem &q, hipStream_t stream)
 {
     // Direct-to-LDS 256x256 tiles when they give at least one tile per CU,
-    // else 128x128 ones; 128x128 register-staged tiles (with bounds checks
-    // where needed) for operands the direct-to-LDS kernel cannot take.
+    // else 128x128 ones (64x128 where those fill few CUs, below); 128x128
+    // register-staged tiles (with bounds checks where needed) for operands the
+    // direct-to-LDS kernel cannot take.
     //
     // Both direct-to-LDS tiles run one workgroup per CU, so a grid runs in
     // rounds of 256 workgroups.  A 128x128 tile does a quarter of a 256x256
@@ -856,6 +875,12 @@ hipError_t launch_gemm16(const GemmProblem &q, hipStream_t stream)
     const long long t256 = (long long)((q.M + 255) / 256) * ((q.N + 255) / 256) * q.batch;
     const long long t128 = (long long)((q.M + 127) / 128) * ((q.N + 127) / 128) * q.batch;
     const bool ok256 = dma_ok<HgDma256>(q), ok128 = dma_ok<HgDma128>(q);
+    // 64x128 tiles on grids of 128x128 tiles that fill at most a quarter of the
+    // CUs, or at most half with K >= 4096 (measured: 512x4096x4096 29.8 -> 26.0
+    // us, 1000x1000x2000 16.5 -> 12.9 us; 1024x2048x2048, half filled with
+    // K = 2048, 17.0 -> 17.8 us, so it keeps 128x128 tiles)
+    if (ok128 && (4 * t128 <= 256 || (2 * t128 <= 256 && q.K >= 4096)) && dma_ok<HgDma64x128>(q))
+        return launch_dma<HgDma64x128, BF>(q, stream);
     if (ok256 && ok128) {
         const long long r256 = (t256 + 255) / 256, r128 = (t128 + 255) / 256;
         if (5 * r256 <= 2 * r128) return launch_dma<HgDma256, BF>(q, stream);

@@ -19,7 +19,13 @@ import pytest
 
 # (kind, BM, BN, BK): the direct-to-LDS tile configurations
 CONFIGS = [("f32", 256, 256, 32), ("f32", 128, 128, 32), ("f32", 64, 64, 32),
-           ("f16", 256, 256, 64), ("f16", 128, 128, 64)]
+           ("f16", 256, 256, 64), ("f16", 128, 128, 64), ("f16", 64, 128, 64)]
+
+
+def takes(kind, BM, BN, tA, tB):
+    """Storage combinations a tile is launched for: an fp16 MN-contiguous slice
+    needs 128-wide rows (A stored K x M needs BM >= 128, B stored K x N BN >= 128)."""
+    return kind != "f16" or ((not tA or BM >= 128) and (tB or BN >= 128))
 
 
 def max_slice_index(kind, M, N, K, lda, ldb, tA, tB, BM, BN, BK, stop_before_last_row=True):
@@ -65,13 +71,15 @@ def shapes():
 def test_slice_loads_stay_inside_minimal_operands(kind, BM, BN, BK):
     checked = 0
     for (M, N, K), (tA, tB) in itertools.product(shapes(), [(0, 0), (0, 1), (1, 0), (1, 1)]):
+        if not takes(kind, BM, BN, tA, tB):
+            continue
         for pad in (0, 2, 6) if kind == "f16" else (0, 1, 3):
             lda, ldb = (M if tA else K) + pad, (K if tB else N) + pad
             hi_a, hi_b = max_slice_index(kind, M, N, K, lda, ldb, tA, tB, BM, BN, BK)
             size_a, size_b = minimal_sizes(M, N, K, lda, ldb, tA, tB)
             assert hi_a < size_a and hi_b < size_b, (kind, BM, M, N, K, tA, tB, pad)
             checked += 1
-    assert checked > 1000
+    assert checked > 500
 
 
 def test_last_row_rule_is_needed():

@@ -734,6 +734,21 @@ def test_random_sweep_direct_to_lds(case):
 
 
 # ------------------------------------------------------------------ graph capture
+def test_hgemm_64x128_tiles():
+    # grids that 128x128 tiles would fill to a quarter (or to half with K >= 4096)
+    # run 64x128 tiles when A is stored M x K; A stored K x M keeps 128x128
+    for tB in (False, True):
+        run_and_check("f16", 512, 4096, 4096, 1.0, 0.0, transB=tB, sample=64, c_nan=True)
+        run_and_check("f16", 1000, 1000, 2000, 1.5, -0.5, transB=tB)              # ragged edges and K tail
+        run_and_check("f16", 1002, 998, 600, 1.0, 1.0, transB=tB)                 # chunks straddling N (NN)
+        run_and_check("f16", 256, 2048, 1024, 1.0, 0.0, kind_vals="int4", exact=True, transB=tB)
+        run_and_check("bf16", 640, 768, 512, 1.5, -0.5, transB=tB)
+    run_and_check("f16", 1000, 1000, 2000, 1.5, -0.5, transA=True)                # stays on 128x128
+    run_and_check("f16", 512, 4096, 4096, 1.0, 0.0, transA=True, transB=True, sample=64)
+    batched_check(256, 512, 1024, 4, 1.0, 1.0, sample=32)
+    batched_check(100, 300, 520, 3, 1.5, -0.5, pad=2, transB=True)
+
+
 # ------------------------------------------------------------------ bfloat16 inputs
 # The bf16 entry points run the HGEMM kernels with the bf16 matrix-core op, so
 # these cases cover each of those kernels once more with bfloat16 inputs.
