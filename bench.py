@@ -487,6 +487,17 @@ def run_extra(dg, si, np, torch, dev, stream):
                             torch, stream)
     out["hgemm_2048^3"] = rates(med, gr, 2.0 * 2048 ** 3, PEAK_F16_TFLOPS)
 
+    # one GPU's share of the step when 8 GPUs split C by rows (512 of the 4096 rows)
+    for kind, (M, N, K) in (("sgemm", (512, 4096, 1024)), ("hgemm", (512, 4096, 4096))):
+        dt = torch.float32 if kind == "sgemm" else torch.float16
+        A = torch.empty(M * K, dtype=dt, device=dev).uniform_(-1, 1)
+        B = torch.empty(K * N, dtype=dt, device=dev).uniform_(-1, 1)
+        C = torch.empty(M * N, dtype=torch.float32, device=dev)
+        fn = dg.gemm_f32 if kind == "sgemm" else dg.gemm_f16_f32acc
+        med, _, gr = time_calls(lambda s: fn(M, N, K, 1.0, A, K, B, N, 0.0, C, N, s), torch, stream)
+        peak = PEAK_F32_TFLOPS if kind == "sgemm" else PEAK_F16_TFLOPS
+        out[f"{kind}_row_share_1of8_{M}x{N}x{K}"] = rates(med, gr, 2.0 * M * N * K, peak)
+
     # bfloat16 inputs (the same kernels with the bf16 matrix-core op)
     for n in (2048, 4096):
         A = torch.empty(n * n, dtype=torch.bfloat16, device=dev).uniform_(-1, 1)
