@@ -843,6 +843,9 @@ void launch_dma_ops(const HgemmArgs &a, dim3 grid, bool tA, bool tB, hipStream_t
 template <class Cfg, bool BF>
 hipError_t launch_dma(const GemmProblem &q, hipStream_t stream)
 {
+    // a storage combination the tile cannot take launches nothing below: refuse
+    // it here so that the caller sees an error instead of an unwritten C
+    if (!dma_orientation_ok<Cfg>(q.transA, q.transB)) return hipErrorInvalidValue;
     HgemmArgs a;
     a.M = q.M; a.N = q.N; a.K = q.K;
     a.alpha = q.alpha; a.beta = q.beta;

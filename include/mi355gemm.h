@@ -34,7 +34,10 @@
  *   - M == 0, N == 0 or batch_count == 0: nothing is done.
  *
  * Errors: every entry point returns an int status.  Arguments are checked
- * before any HIP call; on an error nothing is enqueued.
+ * before any HIP call; on an error nothing is enqueued.  Codes 0 to -4 are the
+ * BLAS-style set (size, leading dimension or stride, NULL pointer, launch
+ * refused); -5 and -6 report the two conditions that set has no code for (an
+ * element-misaligned pointer, a transpose flag other than 0 or 1).
  */
 #ifndef MI355GEMM_H
 #define MI355GEMM_H
@@ -55,8 +58,8 @@ enum {
                                 transB: ldb < max(1,K)), ldc < max(1,N), negative stride, or
                                 strideC smaller than one C member when batch_count > 1 */
     GEMM_ERR_NULL = -3,      /* NULL pointer for an operand that the call would read or write */
-    GEMM_ERR_ALIGN = -4,     /* pointer not aligned to its element size */
-    GEMM_ERR_LAUNCH = -5,    /* the HIP runtime refused a kernel launch (hipGetLastError) */
+    GEMM_ERR_LAUNCH = -4,    /* the HIP runtime refused a kernel launch (hipGetLastError) */
+    GEMM_ERR_ALIGN = -5,     /* pointer not aligned to its element size */
     GEMM_ERR_OP = -6         /* transA or transB is neither 0 nor 1 */
 };
 

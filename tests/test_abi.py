@@ -15,7 +15,7 @@ import dense_gemm_optimisation_f32_amd as dg
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "mi355gemm.h")
 
-OK, ESIZE, ELD, ENULL, EALIGN, ELAUNCH, EOP = 0, -1, -2, -3, -4, -5, -6
+OK, ESIZE, ELD, ENULL, ELAUNCH, EALIGN, EOP = 0, -1, -2, -3, -4, -5, -6
 FAKE = 0x10000          # a non-NULL, 16-byte aligned address that is never dereferenced
 
 
