@@ -9,25 +9,44 @@ the step's throughput, (2*4096*4096*1024 + 2*4096^3) / step time, in TFLOPS;
 the per-kernel TFLOPS and fraction of the MI355X peak for its dtype are
 reported beside it, with the roofline of the dominant (longest) kernel taken
 from HIP events recorded on the stream the kernels run on.  The CPU oracle is
-timed on a bounded sample of the same workload as a baseline.  The other
-benchmark configurations (SGEMM 512^3, the 1001x777x513 and 1024x1024x512
-SGEMMs, HGEMM 2048^3 and 16 batched 1024^3 HGEMMs with beta = 1), two ragged
+timed on the same workload as a baseline, and on every other benchmark
+configuration under "cpu_per_config".
+
+Clock: the shader clock takes some tens of milliseconds of load to leave its
+idle state.  Before the warm-up steps the step runs back to back for
+--settle-ms (untimed) while the clock is sampled; "clock" reports the samples
+(idle, under that load, and right after the timed steps) and where they were
+read.
+
+The other benchmark configurations (SGEMM 512^3; the 1001x777x513 and
+1024x1024x512 SGEMMs with alpha = 1.5, beta = -0.5 and with alpha = 1,
+beta = 0; the M = N sweep at K = 1024 from 128 to 16384; HGEMM 2048^3 and
+4096^3; 16 batched 1024^3 HGEMMs with beta = 1, warm and cold), one GPU's
+share of each step shape under an 8-way row split, bf16 inputs, two ragged
 shapes and the transposed storage combinations are timed after the main run
 and reported under "extra" (not part of the value).
 
-Warm-up: under this load the clocks take about 40 ms (about 100 steps) to
-settle; the default 200 untimed steps cover that, and 50 steps are timed.
+    python bench.py --profile NAME [--steps K] [--warmup W] [--copy-calibration]
+
+runs only configuration NAME ("step" or a key of "extra") K times after W
+untimed calls and prints one short line: the command rocprofv3 wraps to collect
+a configuration's counters.  --write-counters / --write-traffic /
+--write-trace turn such runs' CSV files into the summaries under profiles/.
 
 Prints exactly one JSON line.
 """
 from __future__ import annotations
 
 import argparse
+import glob
 import hashlib
 import json
 import os
+import re
 import statistics
+import subprocess
 import sys
+import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -39,6 +58,7 @@ PEAK_F32_TFLOPS = 157.3
 PEAK_F16_TFLOPS = 2516.6
 PEAK_BF16_TFLOPS = 2516.6   # bf16 dense MFMA runs at the fp16 rate
 PEAK_HBM_GBS = 8000.0
+PEAKS = {"f32": PEAK_F32_TFLOPS, "f16": PEAK_F16_TFLOPS, "bf16": PEAK_BF16_TFLOPS}
 _CSRC = "dense_gemm_optimisation_f32_amd/csrc/"
 # the files whose code makes up each kernel (its source and the headers it includes)
 KERNEL_SOURCES = {
@@ -47,12 +67,13 @@ KERNEL_SOURCES = {
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.md")
 COPY_BYTES = 256 << 20   # size of the calibration copy (read and written)
+STEP_WORKLOADS = {"sgemm": "SGEMM fp32 row-major 4096x4096x1024 alpha=1 beta=0",
+                  "hgemm": "HGEMM fp16->fp32 row-major 4096x4096x4096 alpha=1 beta=0"}
 
 
 def source_digest(kind: str) -> str:
     """Digest of a kernel's code: its files with comments and whitespace removed,
     so that a counter record stays valid across comment-only edits."""
-    import re
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES[kind]:
         with open(os.path.join(ROOT, rel)) as f:
@@ -70,11 +91,11 @@ def _traffic_records():
     return json.loads(text[start:text.index("```", start)])
 
 
-def measured_traffic(kind: str, workload: str):
+def measured_traffic(key: str, kind: str, workload: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary, or None
     when it is missing or was taken on a different version of the kernel source."""
     try:
-        rec = _traffic_records()[kind]
+        rec = _traffic_records()[key]
     except (OSError, KeyError, ValueError):
         return None
     if rec.get("source_sha") != source_digest(kind) or rec.get("workload") != workload:
@@ -82,353 +103,196 @@ def measured_traffic(kind: str, workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-def main() -> int:
-    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    # the chip's clocks settle only after some tens of milliseconds of this load
-    # (about 100 steps); the warm-up covers that so the timed steps are steady
-    ap.add_argument("--warmup", type=int, default=200)
-    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
-    ap.add_argument("--no-extra", action="store_true", help="skip the other configurations")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU-oracle time budget")
-    ap.add_argument("--copy-calibration", action="store_true",
-                    help="first run a plain 256 MiB device copy three times (counter calibration)")
-    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
-                    help="turn two rocprofv3 counter_collection.csv files (FETCH_SIZE, WRITE_SIZE) of a "
-                         "--copy-calibration run into profiles/hbm_traffic.md; uses no GPU")
-    ap.add_argument("--write-trace", nargs=3, metavar=("STATS_CSV", "TRACE_CSV", "BENCH_LOG"),
-                    help="turn a rocprofv3 --kernel-trace --stats run of this script into "
-                         "profiles/kernel_trace_sgemm4096x4096x1024_hgemm4096cube.md; uses no GPU")
-    ap.add_argument("--write-counters", nargs="+", metavar="CSV",
-                    help="turn rocprofv3 counter_collection.csv files of the step's kernels into "
-                         "profiles/counters_sgemm4096x4096x1024_hgemm4096cube.md; uses no GPU")
-    args = ap.parse_args()
-    if args.write_traffic:
-        return write_traffic(*args.write_traffic)
-    if args.write_counters:
-        return write_counters(args.write_counters)
-    if args.write_trace:
-        return write_trace(*args.write_trace)
+# ---------------------------------------------------------------- configurations
+def extra_configs():
+    """The benchmark configurations timed besides the step, in order.  Each is one
+    library call: kind (f32, f16, bf16), shape, alpha/beta, batch, storage flags."""
+    out = []
 
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on exactly one GPU: this library has no multi-GPU path "
-              "(--gpus must be 1).", file=sys.stderr)
-        return 2
+    def add(name, kind, M, N, K, alpha=1.0, beta=0.0, batch=1, tA=0, tB=0, cold=False):
+        out.append(dict(name=name, kind=kind, M=M, N=N, K=K, alpha=alpha, beta=beta, batch=batch,
+                        tA=tA, tB=tB, cold=cold))
 
-    import numpy as np
-    import torch
-
-    import dense_gemm_optimisation_f32_amd as dg
-    import seeded_inputs as si
-
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        return 2
-    dg.load_library()    # raises if the HIP library is not built: there is no fallback
-    dev = torch.device("cuda:0")
-    stream = torch.cuda.current_stream(dev)
-
-    def upload(buf):
-        return torch.from_numpy(np.ascontiguousarray(buf)).to(dev)
-
-    # ---- inputs (resident in HBM before timing)
-    Ms, Ns, Ks = 4096, 4096, 1024
-    ps = si.gemm_problem(Ms, Ns, Ks, seed=42, with_c=False)
-    sA, sB = upload(ps["A"]), upload(ps["B"])
-    sC = torch.empty(Ms * Ns, dtype=torch.float32, device=dev)
-    Mh = Nh = Kh = 4096
-    ph = si.gemm_problem(Mh, Nh, Kh, in_dtype=np.float16, seed=42, with_c=False)
-    hA, hB = upload(ph["A"]), upload(ph["B"])
-    hC = torch.empty(Mh * Nh, dtype=torch.float32, device=dev)
-    torch.cuda.synchronize()
-
-    if args.copy_calibration:
-        # uninitialised buffers: no fill kernel joins the counted dispatches
-        src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            torch.mul(src, 1.0, out=dst)   # plain elementwise copy: reads and writes COPY_BYTES
-        torch.cuda.synchronize()
-        del src, dst
-
-    def sgemm():
-        dg.gemm_f32(Ms, Ns, Ks, 1.0, sA, Ks, sB, Ns, 0.0, sC, Ns, stream)
-
-    def hgemm():
-        dg.gemm_f16_f32acc(Mh, Nh, Kh, 1.0, hA, Kh, hB, Nh, 0.0, hC, Nh, stream)
-
-    for _ in range(args.warmup):
-        sgemm()
-        hgemm()
-    torch.cuda.synchronize()
-
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        ev[i][0].record(stream)
-        sgemm()
-        ev[i][1].record(stream)
-        hgemm()
-        ev[i][2].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-
-    t_s = [e[0].elapsed_time(e[1]) * 1e-3 for e in ev]
-    t_h = [e[1].elapsed_time(e[2]) * 1e-3 for e in ev]
-    flop_s = 2.0 * Ms * Ns * Ks
-    flop_h = 2.0 * Mh * Nh * Kh
-    step_s = wall / args.steps
-    value = (flop_s + flop_h) / step_s / 1e12
-
-    def kernel_record(name, ts, flop, peak, workload, bytes_alg):
-        avg = statistics.fmean(ts)
-        return {
-            "workload": workload,
-            "avg_ms": avg * 1e3, "median_ms": statistics.median(ts) * 1e3, "min_ms": min(ts) * 1e3,
-            "tflops": flop / avg / 1e12, "peak_tflops": peak, "frac_of_peak": flop / avg / 1e12 / peak,
-            "algorithmic_flop": flop, "algorithmic_bytes": bytes_alg,
-        }
-
-    w_s = "SGEMM fp32 row-major 4096x4096x1024 alpha=1 beta=0"
-    w_h = "HGEMM fp16->fp32 row-major 4096x4096x4096 alpha=1 beta=0"
-    bytes_s = 4 * (Ms * Ks + Ks * Ns + Ms * Ns)
-    bytes_h = 2 * (Mh * Kh + Kh * Nh) + 4 * Mh * Nh
-    per_kernel = {
-        "sgemm": kernel_record("sgemm", t_s, flop_s, PEAK_F32_TFLOPS, w_s, bytes_s),
-        "hgemm": kernel_record("hgemm", t_h, flop_h, PEAK_F16_TFLOPS, w_h, bytes_h),
-    }
-    dom = max(per_kernel, key=lambda k: per_kernel[k]["avg_ms"])
-    dk = per_kernel[dom]
-    roofline = {
-        "kernel": dom, "bound": "mfma", "achieved": dk["tflops"], "peak": dk["peak_tflops"],
-        "unit": "TFLOP/s", "frac": dk["frac_of_peak"], "traffic": measured_traffic(dom, dk["workload"]),
-        "algorithmic_flop_per_launch": dk["algorithmic_flop"],
-    }
-    other = "hgemm" if dom == "sgemm" else "sgemm"
-    ok = per_kernel[other]
-    roofline_other = {
-        "kernel": other, "bound": "mfma", "achieved": ok["tflops"], "peak": ok["peak_tflops"],
-        "unit": "TFLOP/s", "frac": ok["frac_of_peak"], "traffic": measured_traffic(other, ok["workload"]),
-    }
-
-    extra = {} if args.no_extra else run_extra(dg, si, np, torch, dev, stream)
-
-    cpu = None if args.no_cpu else cpu_baseline(si, np, ps, ph, args.cpu_seconds)
-
-    line = {
-        "metric": METRIC, "value": value, "unit": "TFLOPS", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": step_s * 1e3, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "f32+f16(f32acc)", "data": "synthetic",
-        "config": {"workload": "one SGEMM 4096x4096x1024 (fp32) + one HGEMM 4096^3 (fp16 in, fp32 "
-                               "accumulate/out) per step, row-major, alpha=1 beta=0, seeded uniform[-1,1)",
-                   "parallelism": "single GPU"},
-        "per_kernel": per_kernel,
-        "roofline": roofline,
-        "roofline_other": roofline_other,
-        "cpu_baseline": cpu,
-        "extra": extra,
-    }
-    print(json.dumps(line), flush=True)
-    return 0
+    # configuration 1
+    add("sgemm_512^3", "f32", 512, 512, 512)
+    # configuration 2: the non-multiple and the regular shape, with the alpha/beta
+    # epilogue and at alpha = 1, beta = 0
+    for M, N, K in ((1001, 777, 513), (1024, 1024, 512)):
+        add(f"sgemm_{M}x{N}x{K}_a1.5_b-0.5", "f32", M, N, K, 1.5, -0.5)
+        add(f"sgemm_{M}x{N}x{K}", "f32", M, N, K)
+    # configuration 3: the M = N sweep at K = 1024 (4096 is the step's SGEMM, here alone)
+    for n in (128, 256, 512, 1024, 2048, 4096, 8192, 16384):
+        add(f"sgemm_{n}x{n}x1024", "f32", n, n, 1024)
+    # configuration 4 (4096^3 is the step's HGEMM, here alone)
+    for n in (2048, 4096):
+        add(f"hgemm_{n}^3", "f16", n, n, n)
+    # configuration 5: warm (the same buffers every call) and cold (operand sets
+    # larger than the last-level cache used in turn)
+    add("batched_hgemm_16x1024^3_b1", "f16", 1024, 1024, 1024, 1.0, 1.0, batch=16)
+    add("batched_hgemm_16x1024^3_b1_cold", "f16", 1024, 1024, 1024, 1.0, 1.0, batch=16, cold=True)
+    # one GPU's share of each step shape when 8 GPUs split C by rows
+    add("sgemm_row_share_1of8_512x4096x1024", "f32", 512, 4096, 1024)
+    add("hgemm_row_share_1of8_512x4096x4096", "f16", 512, 4096, 4096)
+    # bfloat16 inputs (the same kernels with the bf16 matrix-core op)
+    for n in (2048, 4096):
+        add(f"bf16gemm_{n}^3", "bf16", n, n, n)
+    # ragged shapes: the masked direct-to-LDS kernels
+    add("sgemm_ragged_4000x4000x1000", "f32", 4000, 4000, 1000)
+    add("hgemm_ragged_4000x4000x4000", "f16", 4000, 4000, 4000)
+    # op(A)op(B): the step shapes with A stored K x M and/or B stored N x K
+    for tA, tB in ((0, 1), (1, 0), (1, 1)):
+        tag = ("T" if tA else "N") + ("T" if tB else "N")
+        add(f"sgemm_{tag}_4096x4096x1024", "f32", 4096, 4096, 1024, tA=tA, tB=tB)
+        add(f"hgemm_{tag}_4096x4096x4096", "f16", 4096, 4096, 4096, tA=tA, tB=tB)
+    return out
 
 
-TRACE_STEPS, TRACE_WARMUP = 50, 200
+def config_bytes(c):
+    """Algorithmic bytes of one call: A and B read once, C written once and read when beta != 0."""
+    ein = 4 if c["kind"] == "f32" else 2
+    per = ein * (c["M"] * c["K"] + c["K"] * c["N"]) + 4 * c["M"] * c["N"] * (2 if c["beta"] != 0 else 1)
+    return per * c["batch"]
 
 
-def write_trace(stats_csv: str, trace_csv: str, bench_log: str) -> int:
-    """Kernel-trace summary of a profiled run of this script: rocprofv3's statistics over
-    all launches, the same over the timed launches only (the last TRACE_STEPS of each
-    kernel), and the bench line's own HIP-event averages for comparison."""
-    import csv
+def config_flop(c):
+    return 2.0 * c["M"] * c["N"] * c["K"] * c["batch"]
 
-    def short(n):
-        return n.replace("mi355gemm::(anonymous namespace)::", "").split("(")[0]
 
-    stats = list(csv.DictReader(open(stats_csv)))
-    per = {}
-    for r in csv.DictReader(open(trace_csv)):
-        per.setdefault(r["Kernel_Name"], []).append(
-            (int(r["Start_Timestamp"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
-    line = next(l for l in open(bench_log) if l.startswith('{"metric"'))
-    bench_line = json.loads(line)
-    cmd = (f"cd /tmp && rocprofv3 --kernel-trace --stats --output-format csv -d $OUT/prof -o run -- "
-           f"python3 $R/bench.py --no-cpu --no-extra --steps {TRACE_STEPS} --warmup {TRACE_WARMUP} "
-           f"> $OUT/prof.log\n"
-           f"python3 $R/bench.py --write-trace $OUT/prof/run_kernel_stats.csv "
-           f"$OUT/prof/run_kernel_trace.csv $OUT/prof.log   # R = repository root, OUT = an output directory")
-    out = ["# rocprofv3 kernel trace: bench step (SGEMM 4096x4096x1024 fp32 + HGEMM 4096^3 fp16->fp32)", "",
-           "Commands (run on one MI355X):", "", "```", cmd, "```", "",
-           "All launches (warm-up included):", "",
-           "| kernel | calls | average (us) | min (us) | max (us) | share |", "|---|---|---|---|---|---|"]
-    for r in stats:
-        out.append(f"| `{short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
-                   f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.1f}% |")
-    out += ["", f"Timed launches only (the last {TRACE_STEPS} of each kernel), beside the bench line's "
-                "HIP-event averages over the same steps:", "",
-            "| kernel | launches | rocprofv3 average (us) | bench average (us) |", "|---|---|---|---|"]
-    for name, v in per.items():
-        kind = "sgemm" if "sgemm" in name else "hgemm" if "hgemm" in name else None
-        if kind is None:
+class ConfigRunner:
+    """Seeded operands of one configuration resident on the device, and a closure
+    that enqueues the library call on a given stream."""
+
+    def __init__(self, c, dg, si, np, torch, dev, sets=1):
+        self.c = c
+        M, N, K, nb = c["M"], c["N"], c["K"], c["batch"]
+        in_dtype = {"f32": np.float32, "f16": np.float16, "bf16": "bf16"}[c["kind"]]
+        a_rows, a_cols = (K, M) if c["tA"] else (M, K)
+        b_rows, b_cols = (N, K) if c["tB"] else (K, N)
+        self.lda, self.ldb, self.ldc = a_cols, b_cols, N
+
+        def up(buf):
+            buf = np.ascontiguousarray(buf)
+            if buf.dtype == np.uint16:
+                return torch.from_numpy(buf.view(np.int16)).view(torch.bfloat16).to(dev)
+            return torch.from_numpy(buf).to(dev)
+
+        self.sets = []
+        for s in range(sets):
+            probs = [si.gemm_problem(M, N, K, in_dtype=in_dtype, seed=42 + 1000 * s, batch=b,
+                                     with_c=c["beta"] != 0, transA=bool(c["tA"]), transB=bool(c["tB"]))
+                     for b in range(nb)]
+            A = up(np.concatenate([p["A"] for p in probs]))
+            B = up(np.concatenate([p["B"] for p in probs]))
+            if c["beta"] != 0:
+                C = up(np.concatenate([p["C"] for p in probs]))
+            else:
+                C = torch.empty(nb * M * N, dtype=torch.float32, device=dev)
+            self.sets.append((A, B, C))
+            del probs
+        self.turn = 0
+        self.dg = dg
+
+    def __call__(self, stream):
+        c, dg = self.c, self.dg
+        A, B, C = self.sets[self.turn % len(self.sets)]
+        self.turn += 1
+        M, N, K, nb = c["M"], c["N"], c["K"], c["batch"]
+        if nb > 1:
+            fn = dg.gemm_batched_bf16_f32acc_ex if c["kind"] == "bf16" else dg.gemm_batched_f16_f32acc_ex
+            fn(c["tA"], c["tB"], M, N, K, c["alpha"], A, self.lda, M * K, B, self.ldb, K * N, c["beta"], C,
+               self.ldc, M * N, nb, stream)
+            return
+        fn = {"f32": dg.gemm_f32_ex, "f16": dg.gemm_f16_f32acc_ex, "bf16": dg.gemm_bf16_f32acc_ex}[c["kind"]]
+        fn(c["tA"], c["tB"], M, N, K, c["alpha"], A, self.lda, B, self.ldb, c["beta"], C, self.ldc, stream)
+
+
+# ---------------------------------------------------------------- clock
+def _sysfs_sclk():
+    """Current shader clock (MHz) of each GPU the sysfs DPM tables show: the level
+    marked '*' in pp_dpm_sclk."""
+    vals = []
+    for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+        try:
+            for line in open(path):
+                if "*" in line:
+                    m = re.search(r"(\d+)\s*[Mm][Hh]z", line)
+                    if m:
+                        vals.append(int(m.group(1)))
+        except OSError:
             continue
-        v.sort()
-        tail = [d for _, d in v[-TRACE_STEPS:]]
-        out.append(f"| `{short(name)}` | {len(tail)} | {sum(tail) / len(tail) / 1e3:.1f} | "
-                   f"{bench_line['per_kernel'][kind]['avg_ms'] * 1e3:.1f} |")
-    out += ["", "The bench averages include the gap between an event and its kernel; rocprofv3 times "
-                "the kernel alone. Both kernels are the NN (no transpose) instantiations; the first flag of "
-                "the HGEMM kernel selects the input format (false: fp16)."]
-    path = os.path.join(ROOT, "profiles", "kernel_trace_sgemm4096x4096x1024_hgemm4096cube.md")
-    with open(path, "w") as f:
-        f.write("\n".join(out) + "\n")
-    print(path)
-    return 0
+    return vals
 
 
-COUNTER_PASSES = (
-    "SQ_INSTS_MFMA SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE "
-    "SQ_INSTS_VALU SQ_INSTS_VMEM_RD SQ_INSTS_VMEM_WR GRBM_GUI_ACTIVE",
-    "SQ_WAVES SQ_WAVE_CYCLES SQ_BUSY_CYCLES SQ_WAIT_INST_ANY SQ_WAIT_ANY SQ_WAIT_INST_LDS "
-    "SQ_ACTIVE_INST_LDS SQ_LDS_ADDR_CONFLICT GRBM_GUI_ACTIVE",
-    "TCC_HIT_sum TCC_MISS_sum TCC_EA0_RDREQ_DRAM_sum TCC_EA0_WRREQ_DRAM_sum",
-)
+def _smi_sclk():
+    """Shader clock (MHz) as rocm-smi reports it (the current sclk level)."""
+    try:
+        out = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=20).stdout
+    except (OSError, subprocess.SubprocessError):
+        return []
+    vals = []
+    for line in out.splitlines():
+        if "sclk" in line.lower():
+            m = re.search(r"\((\d+)\s*[Mm][Hh]z\)", line)
+            if m:
+                vals.append(int(m.group(1)))
+    return vals
 
 
-def write_counters(csv_paths) -> int:
-    """Per-launch means of rocprofv3 counters for the step's two kernels, with the
-    derived figures the kernel design relies on (cycles per MFMA instruction, LDS bank
-    conflicts), written as a markdown summary under profiles/."""
-    import csv
-
-    vals = {}          # kind -> counter -> list of per-dispatch values
-    durs = {}          # kind -> list of dispatch durations (ns)
-    names = {}
-    for path in csv_paths:
-        for r in csv.DictReader(open(path)):
-            name = r["Kernel_Name"]
-            kind = "sgemm" if "sgemm" in name else "hgemm" if "hgemm" in name else None
-            if kind is None:
-                continue
-            names[kind] = name
-            vals.setdefault(kind, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
-            durs.setdefault(kind, []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
-    mean = {k: {c: sum(v) / len(v) for c, v in d.items()} for k, d in vals.items()}
-    kinds = [k for k in ("sgemm", "hgemm") if k in mean]
-    counters = sorted({c for k in kinds for c in mean[k]})
-    cmds = "\n".join(
-        f"cd /tmp && rocprofv3 --pmc {p} --output-format csv -d $OUT/counters{i} -o c -- "
-        f"python3 $R/bench.py --no-cpu --no-extra --steps 3 --warmup 1" for i, p in enumerate(COUNTER_PASSES, 1))
-    cmds += ("\npython3 $R/bench.py --write-counters " +
-             " ".join(f"$OUT/counters{i}/c_counter_collection.csv" for i in range(1, len(COUNTER_PASSES) + 1)) +
-             "   # R = repository root, OUT = an output directory")
-    lines = ["# rocprofv3 counters per launch: bench step kernels (SGEMM 4096x4096x1024 fp32, "
-             "HGEMM 4096^3 fp16->fp32)", "",
-             "Commands (one MI355X; each pass is a run of its own):", "", "```", cmds, "```", "",
-             "Mean over the dispatches of each kernel in the runs (the counters are summed over the "
-             "whole device; SQ_LDS_* and SQ_*_CYCLES count in units of four cycles).", "",
-             "| counter | " + " | ".join(kinds) + " |", "|---|" + "---|" * len(kinds)]
-    for c in counters:
-        lines.append(f"| {c} | " + " | ".join(f"{mean[k].get(c, float('nan')):.4g}" for k in kinds) + " |")
-    lines += ["", "Derived:", ""]
-    for k in kinds:
-        m = mean[k]
-        d = sum(durs[k]) / len(durs[k]) / 1e3
-        short = names[k].replace("mi355gemm::(anonymous namespace)::", "").split("(")[0]
-        parts = [f"- {k} (`{short}`, "
-                 f"{d:.1f} us per profiled launch):"]
-        if m.get("SQ_INSTS_MFMA"):
-            parts.append(f"{m['SQ_VALU_MFMA_BUSY_CYCLES'] / m['SQ_INSTS_MFMA']:.1f} matrix-core cycles "
-                         f"per MFMA instruction, {m['SQ_INSTS_MFMA']:.4g} MFMA instructions;")
-        if m.get("SQ_LDS_IDX_ACTIVE"):
-            parts.append(f"LDS bank conflicts {100 * m.get('SQ_LDS_BANK_CONFLICT', 0) / m['SQ_LDS_IDX_ACTIVE']:.2f}% "
-                         f"of LDS-active cycles;")
-        if m.get("TCC_HIT_sum") is not None and m.get("TCC_MISS_sum"):
-            parts.append(f"L2 hit rate {100 * m['TCC_HIT_sum'] / (m['TCC_HIT_sum'] + m['TCC_MISS_sum']):.1f}%;")
-        if m.get("SQ_INSTS_MFMA") and m.get("SQ_INSTS_VALU") is not None:
-            parts.append(f"{m['SQ_INSTS_VALU'] / m['SQ_INSTS_MFMA']:.2f} VALU instructions (MFMA included) "
-                         f"per MFMA.")
-        lines.append(" ".join(parts))
-    path = os.path.join(ROOT, "profiles", "counters_sgemm4096x4096x1024_hgemm4096cube.md")
-    with open(path, "w") as f:
-        f.write("\n".join(lines) + "\n")
-    print(path)
-    return 0
+def read_sclk():
+    """(MHz values, source) of the shader clock, from sysfs when readable, else rocm-smi."""
+    v = _sysfs_sclk()
+    if v:
+        return v, "sysfs pp_dpm_sclk"
+    v = _smi_sclk()
+    return v, ("rocm-smi --showclocks" if v else "unavailable")
 
 
-def write_traffic(fetch_csv: str, write_csv: str) -> int:
-    """Per-launch HBM traffic of the step's kernels from FETCH_SIZE / WRITE_SIZE counter
-    runs, each scaled by the ratio of known bytes to counted bytes for the calibration copy."""
-    import csv
+class ClockSampler:
+    """Samples the shader clock in a background thread until stopped."""
 
-    def per_kernel(path, counter):
-        vals = {}
-        for r in csv.DictReader(open(path)):
-            if r["Counter_Name"] != counter:
-                continue
-            name, value = r["Kernel_Name"], float(r["Counter_Value"]) * 1024.0
-            kind = "sgemm" if "sgemm" in name else "hgemm" if "hgemm" in name else "copy"
-            if kind == "copy" and value < COPY_BYTES / 8:
-                continue   # other small kernels of the run (tensor fills), not the calibration copy
-            vals.setdefault(kind, {}).setdefault(name, []).append(value)
-        return vals
+    def __init__(self, period_s=0.02):
+        self.period = period_s
+        self.samples = []
+        self.source = None
+        self._stop = threading.Event()
+        self._t = threading.Thread(target=self._run, daemon=True)
 
-    fetch, write = per_kernel(fetch_csv, "FETCH_SIZE"), per_kernel(write_csv, "WRITE_SIZE")
+    def _run(self):
+        while not self._stop.is_set():
+            v, src = read_sclk()
+            if v:
+                self.samples.append(v[0])
+                self.source = src
+            self._stop.wait(self.period)
 
-    def mean(d, kind):
-        (name, v), = d[kind].items()
-        return name, sum(v) / len(v)
+    def __enter__(self):
+        self._t.start()
+        return self
 
-    copy_name, copy_f = mean(fetch, "copy")
-    _, copy_w = mean(write, "copy")
-    scale_f, scale_w = COPY_BYTES / copy_f, COPY_BYTES / copy_w
-    workloads = {"sgemm": "SGEMM fp32 row-major 4096x4096x1024 alpha=1 beta=0",
-                 "hgemm": "HGEMM fp16->fp32 row-major 4096x4096x4096 alpha=1 beta=0"}
-    alg = {"sgemm": 4 * (4096 * 1024 * 2 + 4096 * 4096), "hgemm": 2 * (4096 * 4096 * 2) + 4 * 4096 * 4096}
-    recs = {"copy_calibration": {"kernel": copy_name, "bytes": COPY_BYTES, "fetch_counted": copy_f,
-                                 "write_counted": copy_w, "fetch_scale": scale_f, "write_scale": scale_w}}
-    rows = []
-    for kind in ("sgemm", "hgemm"):
-        name, f = mean(fetch, kind)
-        _, w = mean(write, kind)
-        total = f * scale_f + w * scale_w
-        recs[kind] = {"kernel": name, "workload": workloads[kind], "source_sha": source_digest(kind),
-                      "fetch_bytes_per_launch": f * scale_f, "write_bytes_per_launch": w * scale_w,
-                      "hbm_bytes_per_launch": total, "algorithmic_bytes": alg[kind]}
-        rows.append(f"| {kind} | {workloads[kind]} | {f * scale_f / 1e6:.1f} | {w * scale_w / 1e6:.1f} | "
-                    f"{total / 1e6:.1f} | {alg[kind] / 1e6:.1f} | {total / alg[kind]:.2f} |")
-    cmd = ("cd /tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d $OUT/traffic_fetch -o t -- "
-           "python3 $R/bench.py --no-cpu --no-extra --steps 3 --warmup 1 --copy-calibration\n"
-           "cd /tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv -d $OUT/traffic_write -o t -- "
-           "python3 $R/bench.py --no-cpu --no-extra --steps 3 --warmup 1 --copy-calibration\n"
-           "python3 $R/bench.py --write-traffic $OUT/traffic_fetch/t_counter_collection.csv "
-           "$OUT/traffic_write/t_counter_collection.csv   # R = repository root, OUT = an output directory")
-    text = ("# HBM traffic per launch: bench step kernels (rocprofv3 FETCH_SIZE / WRITE_SIZE)\n\n"
-            f"Commands (one MI355X):\n\n```\n{cmd}\n```\n\n"
-            f"Calibration: a plain elementwise copy of {COPY_BYTES >> 20} MiB reads and writes {COPY_BYTES} bytes; "
-            f"the counters read {copy_f:.0f} B fetched and {copy_w:.0f} B written, so fetch counts are scaled by "
-            f"{scale_f:.4f} and write counts by {scale_w:.4f}.\n\n"
-            "| kernel | workload | fetched (MB) | written (MB) | total (MB) | algorithmic (MB) | ratio |\n"
-            "|---|---|---|---|---|---|---|\n" + "\n".join(rows) + "\n\n"
-            "Machine-readable copy (bench.py reads it; a record whose source_sha no longer matches the kernel "
-            "source is ignored):\n\n```json\n" + json.dumps(recs, indent=1) + "\n```\n")
-    with open(TRAFFIC_FILE, "w") as f:
-        f.write(text)
-    print(text)
-    return 0
+    def __exit__(self, *exc):
+        self._stop.set()
+        self._t.join(timeout=30)
 
 
-def time_calls(fn, torch, stream, warmup=20, reps=30, graph_calls=20):
+# ---------------------------------------------------------------- timing helpers
+def time_calls(fn, torch, stream, warmup=20, reps=30, graph_calls=20, warm_s=0.1):
     """Seconds per call of fn(s), which enqueues one library call on stream s.
 
+    Warm-up: at least `warmup` calls and `warm_s` seconds of back-to-back calls, so
+    the shader clock has left its idle state (the host-side input generation before
+    each configuration leaves the GPU idle for long enough to drop it).
     Returns (median, min) over `reps` calls, each between its own pair of events on
     `stream` (so a launch gap before the kernel counts), and the median over five
     replays of one HIP graph holding `graph_calls` calls back to back, divided by
     `graph_calls` (kernel time without launch gaps: what matters for kernels of a
     few microseconds)."""
-    for _ in range(warmup):
-        fn(stream)
-    torch.cuda.synchronize()
+    t_end = time.perf_counter() + warm_s
+    n = 0
+    while n < warmup or time.perf_counter() < t_end:
+        for _ in range(10):
+            fn(stream)
+        n += 10
+        torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
     for a, b in evs:
         a.record(stream)
@@ -461,112 +325,253 @@ def rates(med, graph, flop, peak):
             "graph_ms_per_call": graph * 1e3, "graph_tflops": flop / graph / 1e12}
 
 
-def run_extra(dg, si, np, torch, dev, stream):
-    out = {}
+# ---------------------------------------------------------------- main
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--settle-ms", type=float, default=300.0,
+                    help="untimed back-to-back steps before the warm-up, while the clock is sampled")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baselines")
+    ap.add_argument("--no-extra", action="store_true", help="skip the other configurations")
+    ap.add_argument("--only", nargs="+", metavar="NAME", help="time only these extra configurations")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU-oracle time budget for the step")
+    ap.add_argument("--profile", metavar="NAME",
+                    help="run only configuration NAME ('step' or an extra key) --steps times after --warmup calls")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run a plain 256 MiB device copy three times (counter calibration)")
+    ap.add_argument("--write-traffic", nargs=3, metavar=("NAME", "FETCH_CSV", "WRITE_CSV"),
+                    help="turn two rocprofv3 counter_collection.csv files (FETCH_SIZE, WRITE_SIZE) of a "
+                         "--profile NAME --copy-calibration run into a record of profiles/hbm_traffic.md")
+    ap.add_argument("--write-trace", nargs=3, metavar=("STATS_CSV", "TRACE_CSV", "BENCH_LOG"),
+                    help="turn a rocprofv3 --kernel-trace --stats run of this script into "
+                         "profiles/kernel_trace_sgemm4096x4096x1024_hgemm4096cube.md; uses no GPU")
+    ap.add_argument("--write-counters", nargs="+", metavar=("NAME", "CSV"),
+                    help="turn rocprofv3 counter_collection.csv files of a --profile NAME run into "
+                         "profiles/counters_NAME.md; uses no GPU")
+    args = ap.parse_args()
+    if args.write_traffic:
+        return write_traffic(*args.write_traffic)
+    if args.write_counters:
+        return write_counters(args.write_counters[0], args.write_counters[1:])
+    if args.write_trace:
+        return write_trace(*args.write_trace)
 
-    def up(buf):
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: this library has no multi-GPU path "
+              "(--gpus must be 1).", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import dense_gemm_optimisation_f32_amd as dg
+    import seeded_inputs as si
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    dg.load_library()    # raises if the HIP library is not built: there is no fallback
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+
+    if args.profile and args.profile != "step":
+        return profile_config(args, dg, si, np, torch, dev, stream)
+
+    def upload(buf):
         return torch.from_numpy(np.ascontiguousarray(buf)).to(dev)
 
-    def sg(M, N, K, alpha, beta, name):
-        p = si.gemm_problem(M, N, K, seed=42, with_c=beta != 0)
-        A, B = up(p["A"]), up(p["B"])
-        C = up(p["C"]) if beta != 0 else torch.empty(M * N, dtype=torch.float32, device=dev)
-        med, _, gr = time_calls(lambda s: dg.gemm_f32(M, N, K, alpha, A, K, B, N, beta, C, N, s), torch, stream)
-        out[name] = rates(med, gr, 2.0 * M * N * K, PEAK_F32_TFLOPS)
+    # ---- inputs (resident in HBM before timing)
+    Ms, Ns, Ks = 4096, 4096, 1024
+    ps = si.gemm_problem(Ms, Ns, Ks, seed=42, with_c=False)
+    sA, sB = upload(ps["A"]), upload(ps["B"])
+    sC = torch.empty(Ms * Ns, dtype=torch.float32, device=dev)
+    Mh = Nh = Kh = 4096
+    ph = si.gemm_problem(Mh, Nh, Kh, in_dtype=np.float16, seed=42, with_c=False)
+    hA, hB = upload(ph["A"]), upload(ph["B"])
+    hC = torch.empty(Mh * Nh, dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
 
-    sg(512, 512, 512, 1.0, 0.0, "sgemm_512^3")
-    sg(1001, 777, 513, 1.5, -0.5, "sgemm_1001x777x513_a1.5_b-0.5")
-    sg(1024, 1024, 512, 1.5, -0.5, "sgemm_1024x1024x512_a1.5_b-0.5")
-    for n in (1024, 2048, 8192):
-        sg(n, n, 1024, 1.0, 0.0, f"sgemm_{n}x{n}x1024")
+    if args.copy_calibration:
+        copy_calibration(torch, dev)
 
-    p = si.gemm_problem(2048, 2048, 2048, in_dtype=np.float16, seed=42, with_c=False)
-    A, B = up(p["A"]), up(p["B"])
-    C = torch.empty(2048 * 2048, dtype=torch.float32, device=dev)
-    med, _, gr = time_calls(lambda s: dg.gemm_f16_f32acc(2048, 2048, 2048, 1.0, A, 2048, B, 2048, 0.0, C, 2048, s),
-                            torch, stream)
-    out["hgemm_2048^3"] = rates(med, gr, 2.0 * 2048 ** 3, PEAK_F16_TFLOPS)
+    def sgemm():
+        dg.gemm_f32(Ms, Ns, Ks, 1.0, sA, Ks, sB, Ns, 0.0, sC, Ns, stream)
 
-    # one GPU's share of the step when 8 GPUs split C by rows (512 of the 4096 rows)
-    for kind, (M, N, K) in (("sgemm", (512, 4096, 1024)), ("hgemm", (512, 4096, 4096))):
-        dt = torch.float32 if kind == "sgemm" else torch.float16
-        A = torch.empty(M * K, dtype=dt, device=dev).uniform_(-1, 1)
-        B = torch.empty(K * N, dtype=dt, device=dev).uniform_(-1, 1)
-        C = torch.empty(M * N, dtype=torch.float32, device=dev)
-        fn = dg.gemm_f32 if kind == "sgemm" else dg.gemm_f16_f32acc
-        med, _, gr = time_calls(lambda s: fn(M, N, K, 1.0, A, K, B, N, 0.0, C, N, s), torch, stream)
-        peak = PEAK_F32_TFLOPS if kind == "sgemm" else PEAK_F16_TFLOPS
-        out[f"{kind}_row_share_1of8_{M}x{N}x{K}"] = rates(med, gr, 2.0 * M * N * K, peak)
+    def hgemm():
+        dg.gemm_f16_f32acc(Mh, Nh, Kh, 1.0, hA, Kh, hB, Nh, 0.0, hC, Nh, stream)
 
-    # bfloat16 inputs (the same kernels with the bf16 matrix-core op)
-    for n in (2048, 4096):
-        A = torch.empty(n * n, dtype=torch.bfloat16, device=dev).uniform_(-1, 1)
-        B = torch.empty(n * n, dtype=torch.bfloat16, device=dev).uniform_(-1, 1)
-        C = torch.empty(n * n, dtype=torch.float32, device=dev)
-        med, _, gr = time_calls(lambda s: dg.gemm_bf16_f32acc(n, n, n, 1.0, A, n, B, n, 0.0, C, n, s), torch, stream)
-        out[f"bf16gemm_{n}^3"] = rates(med, gr, 2.0 * n ** 3, PEAK_BF16_TFLOPS)
+    if args.profile == "step":
+        for _ in range(args.warmup):
+            sgemm()
+            hgemm()
+        torch.cuda.synchronize()
+        for _ in range(args.steps):
+            sgemm()
+            hgemm()
+        torch.cuda.synchronize()
+        print(f"profiled step: {args.steps} steps after {args.warmup}", flush=True)
+        return 0
 
-    # ragged shapes (M, N not multiples of the tile, K not of the slice): the masked
-    # direct-to-LDS kernels
-    for kind, (M, N, K) in (("sgemm", (4000, 4000, 1000)), ("hgemm", (4000, 4000, 4000))):
-        dt = torch.float32 if kind == "sgemm" else torch.float16
-        A = torch.empty(M * K, dtype=dt, device=dev).uniform_(-1, 1)
-        B = torch.empty(K * N, dtype=dt, device=dev).uniform_(-1, 1)
-        C = torch.empty(M * N, dtype=torch.float32, device=dev)
-        fn = dg.gemm_f32 if kind == "sgemm" else dg.gemm_f16_f32acc
-        med, _, gr = time_calls(lambda s: fn(M, N, K, 1.0, A, K, B, N, 0.0, C, N, s), torch, stream)
-        peak = PEAK_F32_TFLOPS if kind == "sgemm" else PEAK_F16_TFLOPS
-        out[f"{kind}_ragged_{M}x{N}x{K}"] = rates(med, gr, 2.0 * M * N * K, peak)
+    # ---- clock: idle, then under back-to-back steps (untimed), then the warm-up
+    idle_mhz, clock_src = read_sclk()
+    settle_steps = 0
+    with ClockSampler() as sampler:
+        t_end = time.perf_counter() + args.settle_ms * 1e-3
+        while time.perf_counter() < t_end:
+            for _ in range(20):
+                sgemm()
+                hgemm()
+            settle_steps += 20
+            torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        sgemm()
+        hgemm()
+    torch.cuda.synchronize()
 
-    # op(A)op(B): the bench shapes with A stored K x M and/or B stored N x K
-    for tA, tB in ((0, 1), (1, 0), (1, 1)):
-        tag = ("T" if tA else "N") + ("T" if tB else "N")
-        for kind, (M, N, K) in (("sgemm", (4096, 4096, 1024)), ("hgemm", (4096, 4096, 4096))):
-            dt = torch.float32 if kind == "sgemm" else torch.float16
-            A = torch.empty(M * K, dtype=dt, device=dev).uniform_(-1, 1)
-            B = torch.empty(K * N, dtype=dt, device=dev).uniform_(-1, 1)
-            C = torch.empty(M * N, dtype=torch.float32, device=dev)
-            lda, ldb = (M if tA else K), (K if tB else N)
-            fn = dg.gemm_f32_ex if kind == "sgemm" else dg.gemm_f16_f32acc_ex
-            med, _, gr = time_calls(lambda s: fn(tA, tB, M, N, K, 1.0, A, lda, B, ldb, 0.0, C, N, s), torch, stream)
-            peak = PEAK_F32_TFLOPS if kind == "sgemm" else PEAK_F16_TFLOPS
-            out[f"{kind}_{tag}_{M}x{N}x{K}"] = rates(med, gr, 2.0 * M * N * K, peak)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        sgemm()
+        ev[i][1].record(stream)
+        hgemm()
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    after_mhz, _ = read_sclk()
 
-    # 16 x 1024^3 batched, beta = 1 (C is read and written: HBM-bound, ridge below the fp16 peak)
-    nb, n = 16, 1024
-    A = torch.empty(nb * n * n, dtype=torch.float16, device=dev).uniform_(-1, 1)
-    B = torch.empty(nb * n * n, dtype=torch.float16, device=dev).uniform_(-1, 1)
-    C = torch.empty(nb * n * n, dtype=torch.float32, device=dev).uniform_(-1, 1)
-    med, _, gr = time_calls(lambda s: dg.gemm_batched_f16_f32acc(n, n, n, 1.0, A, n, n * n, B, n, n * n, 1.0, C, n,
-                                                                 n * n, nb, s), torch, stream)
-    fl = 2.0 * nb * n ** 3
-    bytes_alg = nb * n * n * (2 + 2 + 4 + 4)
-    out["batched_hgemm_16x1024^3_b1"] = dict(rates(med, gr, fl, PEAK_F16_TFLOPS),
-                                             hbm_roofline_tflops=min(PEAK_F16_TFLOPS, fl / bytes_alg * PEAK_HBM_GBS / 1e3),
-                                             warm_buffers=True)
-    # cold: three operand sets (384 MB, more than the 256 MB last-level cache) used in turn,
-    # so each call finds its inputs in HBM
-    sets = [(torch.empty(nb * n * n, dtype=torch.float16, device=dev).uniform_(-1, 1),
-             torch.empty(nb * n * n, dtype=torch.float16, device=dev).uniform_(-1, 1),
-             torch.empty(nb * n * n, dtype=torch.float32, device=dev).uniform_(-1, 1)) for _ in range(3)]
-    turn = [0]
+    t_s = [e[0].elapsed_time(e[1]) * 1e-3 for e in ev]
+    t_h = [e[1].elapsed_time(e[2]) * 1e-3 for e in ev]
+    flop_s = 2.0 * Ms * Ns * Ks
+    flop_h = 2.0 * Mh * Nh * Kh
+    step_s = wall / args.steps
+    value = (flop_s + flop_h) / step_s / 1e12
 
-    def cold_call(s):
-        a, b, c = sets[turn[0] % 3]
-        turn[0] += 1
-        dg.gemm_batched_f16_f32acc(n, n, n, 1.0, a, n, n * n, b, n, n * n, 1.0, c, n, n * n, nb, s)
+    def kernel_record(ts, flop, peak, workload, bytes_alg):
+        avg = statistics.fmean(ts)
+        return {
+            "workload": workload,
+            "avg_ms": avg * 1e3, "median_ms": statistics.median(ts) * 1e3, "min_ms": min(ts) * 1e3,
+            "tflops": flop / avg / 1e12, "peak_tflops": peak, "frac_of_peak": flop / avg / 1e12 / peak,
+            "algorithmic_flop": flop, "algorithmic_bytes": bytes_alg,
+        }
 
-    med, _, gr = time_calls(cold_call, torch, stream, graph_calls=21)
-    hbm_roof = min(PEAK_F16_TFLOPS, fl / bytes_alg * PEAK_HBM_GBS / 1e3)
-    out["batched_hgemm_16x1024^3_b1_cold"] = dict(rates(med, gr, fl, PEAK_F16_TFLOPS), hbm_roofline_tflops=hbm_roof,
-                                                  frac_of_hbm_roofline=fl / med / 1e12 / hbm_roof,
-                                                  warm_buffers=False, operand_sets=3)
-    del sets
+    bytes_s = 4 * (Ms * Ks + Ks * Ns + Ms * Ns)
+    bytes_h = 2 * (Mh * Kh + Kh * Nh) + 4 * Mh * Nh
+    per_kernel = {
+        "sgemm": kernel_record(t_s, flop_s, PEAK_F32_TFLOPS, STEP_WORKLOADS["sgemm"], bytes_s),
+        "hgemm": kernel_record(t_h, flop_h, PEAK_F16_TFLOPS, STEP_WORKLOADS["hgemm"], bytes_h),
+    }
+    dom = max(per_kernel, key=lambda k: per_kernel[k]["avg_ms"])
+    dk = per_kernel[dom]
+    roofline = {
+        "kernel": dom, "bound": "mfma", "achieved": dk["tflops"], "peak": dk["peak_tflops"],
+        "unit": "TFLOP/s", "frac": dk["frac_of_peak"], "traffic": measured_traffic(dom, dom, dk["workload"]),
+        "algorithmic_flop_per_launch": dk["algorithmic_flop"],
+    }
+    other = "hgemm" if dom == "sgemm" else "sgemm"
+    ok = per_kernel[other]
+    roofline_other = {
+        "kernel": other, "bound": "mfma", "achieved": ok["tflops"], "peak": ok["peak_tflops"],
+        "unit": "TFLOP/s", "frac": ok["frac_of_peak"], "traffic": measured_traffic(other, other, ok["workload"]),
+    }
+    s = sampler.samples
+    clock = {"source": sampler.source or clock_src, "idle_mhz": idle_mhz[:1] or None,
+             "settle_ms": args.settle_ms, "settle_steps": settle_steps,
+             "under_step_load_mhz": {"samples": len(s), "min": min(s) if s else None,
+                                     "median": statistics.median(s) if s else None,
+                                     "max": max(s) if s else None},
+             "after_timed_steps_mhz": after_mhz[:1] or None}
+
+    extra = {}
+    if not args.no_extra:
+        extra = run_extra(dg, si, np, torch, dev, stream, args.only)
+
+    cpu = cpu_per = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(si, np, ps, ph, args.cpu_seconds)
+        if not args.only:
+            cpu_per = cpu_per_config(si, np)
+
+    line = {
+        "metric": METRIC, "value": value, "unit": "TFLOPS", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": step_s * 1e3, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32+f16(f32acc)", "data": "synthetic",
+        "config": {"workload": "one SGEMM 4096x4096x1024 (fp32) + one HGEMM 4096^3 (fp16 in, fp32 "
+                               "accumulate/out) per step, row-major, alpha=1 beta=0, seeded uniform[-1,1)",
+                   "parallelism": "single GPU"},
+        "per_kernel": per_kernel,
+        "roofline": roofline,
+        "roofline_other": roofline_other,
+        "cpu_baseline": cpu,
+        "clock": clock,
+        "extra": extra,
+        "cpu_per_config": cpu_per,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def copy_calibration(torch, dev):
+    """A plain 256 MiB elementwise copy, three times: the reference dispatch whose
+    FETCH_SIZE / WRITE_SIZE counts scale the kernels' counts to bytes."""
+    # uninitialised buffers: no fill kernel joins the counted dispatches
+    src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.mul(src, 1.0, out=dst)   # reads and writes COPY_BYTES
+    torch.cuda.synchronize()
+    del src, dst
+
+
+def profile_config(args, dg, si, np, torch, dev, stream):
+    """--profile NAME: only configuration NAME, --steps calls after --warmup calls."""
+    cfg = {c["name"]: c for c in extra_configs()}.get(args.profile)
+    if cfg is None:
+        print(f"unknown configuration {args.profile!r}; choose 'step' or one of: "
+              + ", ".join(c["name"] for c in extra_configs()), file=sys.stderr)
+        return 2
+    run = ConfigRunner(cfg, dg, si, np, torch, dev, sets=3 if cfg["cold"] else 1)
+    torch.cuda.synchronize()
+    if args.copy_calibration:
+        copy_calibration(torch, dev)
+    for _ in range(args.warmup):
+        run(stream)
+    torch.cuda.synchronize()
+    for _ in range(args.steps):
+        run(stream)
+    torch.cuda.synchronize()
+    print(f"profiled {args.profile}: {args.steps} calls after {args.warmup}", flush=True)
+    return 0
+
+
+def run_extra(dg, si, np, torch, dev, stream, only=None):
+    out = {}
+    for c in extra_configs():
+        if only and c["name"] not in only:
+            continue
+        run = ConfigRunner(c, dg, si, np, torch, dev, sets=3 if c["cold"] else 1)
+        # cold: 21 graph calls over three operand sets (each set ~67 MB of A and B
+        # plus 67 MB of C: 403 MB in all, more than the 256 MB last-level cache)
+        med, _, gr = time_calls(run, torch, stream, graph_calls=21 if c["cold"] else 20)
+        fl = config_flop(c)
+        rec = rates(med, gr, fl, PEAKS[c["kind"]])
+        if c["batch"] > 1:
+            roof = min(PEAKS[c["kind"]], fl / config_bytes(c) * PEAK_HBM_GBS / 1e3)
+            rec.update(hbm_roofline_tflops=roof, frac_of_hbm_roofline=fl / med / 1e12 / roof,
+                       graph_frac_of_hbm_roofline=fl / gr / 1e12 / roof,
+                       warm_buffers=not c["cold"], operand_sets=len(run.sets))
+        out[c["name"]] = rec
+        del run
+        torch.cuda.empty_cache()
     return out
 
 
 def cpu_baseline(si, np, ps, ph, budget_s):
-    """The oracle, as it stands, on row blocks of both workloads until the time budget is spent."""
+    """The oracle, as it stands, on row blocks of both step workloads until the time budget is spent."""
     import oracle
 
     threads = oracle.default_threads()
@@ -599,6 +604,261 @@ def cpu_baseline(si, np, ps, ph, budget_s):
                       f"HGEMM 4096^3 (fp64 triple loop), {dt:.1f} s",
             "single_thread": {"value": 2.0 * one_rows * 4096 * 1024 / dt1 / 1e12, "unit": "TFLOPS",
                               "sample": f"first {one_rows} rows of the SGEMM 4096x4096x1024, {dt1:.2f} s"}}
+
+
+# the benchmark configurations the oracle is timed on (the others repeat one of
+# these shapes with other alpha/beta, storage flags or cache state)
+CPU_CONFIGS = ("sgemm_512^3", "sgemm_1001x777x513_a1.5_b-0.5", "sgemm_1024x1024x512_a1.5_b-0.5",
+               *(f"sgemm_{n}x{n}x1024" for n in (128, 256, 512, 1024, 2048, 4096, 8192, 16384)),
+               "hgemm_2048^3", "hgemm_4096^3", "batched_hgemm_16x1024^3_b1")
+
+
+def cpu_per_config(si, np):
+    """The oracle on each benchmark configuration: the whole C up to 4096 rows (all
+    16 members of the batch), 64 seeded rows of the 8192 and 16384 sweep points."""
+    import oracle
+
+    threads = oracle.default_threads()
+    out = {}
+    for c in extra_configs():
+        if c["name"] not in CPU_CONFIGS:
+            continue   # the same arithmetic as a configuration that is timed
+        M, N, K, nb = c["M"], c["N"], c["K"], c["batch"]
+        in_dtype = np.float16 if c["kind"] == "f16" else np.float32
+        rows = si.sample_rows(42, M, 64) if M > 4096 else None
+        n_rows = M if rows is None else len(rows)
+        dt = 0.0
+        for b in range(nb):
+            p = si.gemm_problem(M, N, K, in_dtype=in_dtype, seed=42, batch=b, with_c=c["beta"] != 0)
+            t0 = time.perf_counter()
+            oracle.gemm_ref(M, N, K, c["alpha"], p["A"], p["lda"], p["B"], p["ldb"], c["beta"], p["C"], p["ldc"],
+                            rows=rows, threads=threads)
+            dt += time.perf_counter() - t0
+        out[c["name"]] = {"gflops": 2.0 * n_rows * N * K * nb / dt / 1e9, "seconds": dt, "cores": threads,
+                          "rows": "all" if rows is None else f"{n_rows} seeded rows of {M}"}
+    return out
+
+
+# ---------------------------------------------------------------- profile summaries
+TRACE_STEPS, TRACE_WARMUP = 50, 20
+
+
+def _short(n):
+    return n.replace("mi355gemm::(anonymous namespace)::", "").split("(")[0]
+
+
+def write_trace(stats_csv: str, trace_csv: str, bench_log: str) -> int:
+    """Kernel-trace summary of a profiled run of this script: rocprofv3's statistics over
+    all launches, the same over the timed launches only (the last TRACE_STEPS of each
+    kernel), and the bench line's own HIP-event averages for comparison."""
+    import csv
+
+    stats = list(csv.DictReader(open(stats_csv)))
+    per = {}
+    for r in csv.DictReader(open(trace_csv)):
+        per.setdefault(r["Kernel_Name"], []).append(
+            (int(r["Start_Timestamp"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+    line = next(l for l in open(bench_log) if l.startswith('{"metric"'))
+    bench_line = json.loads(line)
+    cmd = (f"cd /tmp && rocprofv3 --kernel-trace --stats --output-format csv -d $OUT/prof -o run -- "
+           f"python3 $R/bench.py --no-cpu --no-extra --steps {TRACE_STEPS} --warmup {TRACE_WARMUP} "
+           f"> $OUT/prof.log\n"
+           f"python3 $R/bench.py --write-trace $OUT/prof/run_kernel_stats.csv "
+           f"$OUT/prof/run_kernel_trace.csv $OUT/prof.log   # R = repository root, OUT = an output directory")
+    out = ["# rocprofv3 kernel trace: bench step (SGEMM 4096x4096x1024 fp32 + HGEMM 4096^3 fp16->fp32)", "",
+           "Commands (run on one MI355X):", "", "```", cmd, "```", "",
+           "All launches (clock-settling steps and warm-up included):", "",
+           "| kernel | calls | average (us) | min (us) | max (us) | share |", "|---|---|---|---|---|---|"]
+    for r in stats:
+        out.append(f"| `{_short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                   f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.1f}% |")
+    out += ["", f"Timed launches only (the last {TRACE_STEPS} of each kernel), beside the bench line's "
+                "HIP-event averages over the same steps:", "",
+            "| kernel | launches | rocprofv3 average (us) | bench average (us) |", "|---|---|---|---|"]
+    for name, v in per.items():
+        kind = "sgemm" if "sgemm" in name else "hgemm" if "hgemm" in name else None
+        if kind is None:
+            continue
+        v.sort()
+        tail = [d for _, d in v[-TRACE_STEPS:]]
+        out.append(f"| `{_short(name)}` | {len(tail)} | {sum(tail) / len(tail) / 1e3:.1f} | "
+                   f"{bench_line['per_kernel'][kind]['avg_ms'] * 1e3:.1f} |")
+    ck = bench_line.get("clock") or {}
+    out += ["", f"Shader clock ({ck.get('source')}): idle {ck.get('idle_mhz')} MHz, under back-to-back steps "
+                f"{ck.get('under_step_load_mhz')}, right after the timed steps {ck.get('after_timed_steps_mhz')} MHz.",
+            "", "The bench averages include the gap between an event and its kernel; rocprofv3 times "
+                "the kernel alone. Both kernels are the NN (no transpose) instantiations; the first flag of "
+                "the HGEMM kernel selects the input format (false: fp16)."]
+    path = os.path.join(ROOT, "profiles", "kernel_trace_sgemm4096x4096x1024_hgemm4096cube.md")
+    with open(path, "w") as f:
+        f.write("\n".join(out) + "\n")
+    print(path)
+    return 0
+
+
+COUNTER_PASSES = (
+    "SQ_INSTS_MFMA SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE "
+    "SQ_INSTS_VALU SQ_INSTS_VMEM_RD SQ_INSTS_VMEM_WR GRBM_GUI_ACTIVE",
+    "SQ_WAVES SQ_WAVE_CYCLES SQ_BUSY_CYCLES SQ_WAIT_INST_ANY SQ_WAIT_ANY SQ_WAIT_INST_LDS "
+    "SQ_ACTIVE_INST_LDS SQ_LDS_ADDR_CONFLICT GRBM_GUI_ACTIVE",
+    "TCC_HIT_sum TCC_MISS_sum TCC_EA0_RDREQ_DRAM_sum TCC_EA0_WRREQ_DRAM_sum",
+)
+
+
+def _slug(name: str) -> str:
+    return re.sub(r"[^A-Za-z0-9_.-]", "", name.replace("^3", "cube").replace("^", ""))
+
+
+def write_counters(name: str, csv_paths) -> int:
+    """Per-launch means of rocprofv3 counters for the library's kernels in --profile NAME
+    runs, with the derived figures the kernel design relies on (cycles per MFMA
+    instruction, VALU instructions per MFMA, LDS bank conflicts, L2 hit rate), written as
+    a markdown summary profiles/counters_NAME.md."""
+    import csv
+
+    vals, durs = {}, {}   # kernel -> counter -> values; kernel -> durations (ns)
+    for path in csv_paths:
+        for r in csv.DictReader(open(path)):
+            kname = r["Kernel_Name"]
+            if "gemm" not in kname:
+                continue
+            k = _short(kname) + ("<" + kname.split("<", 1)[1].split(">(")[0] + ">" if "<" in kname else "")
+            vals.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+            durs.setdefault(k, []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    mean = {k: {c: sum(v) / len(v) for c, v in d.items()} for k, d in vals.items()}
+    kernels = sorted(mean)
+    counters = sorted({c for k in kernels for c in mean[k]})
+    what = "step" if name == "step" else name
+    cmds = "\n".join(
+        f"cd /tmp && timeout -s KILL 120 rocprofv3 --pmc {p} --output-format csv -d $OUT/counters{i} -o c -- "
+        f"python3 $R/bench.py --profile {what} --steps 3 --warmup 1" for i, p in enumerate(COUNTER_PASSES, 1))
+    cmds += (f"\npython3 $R/bench.py --write-counters {what} " +
+             " ".join(f"$OUT/counters{i}/c_counter_collection.csv" for i in range(1, len(COUNTER_PASSES) + 1)) +
+             "   # R = repository root, OUT = an output directory")
+    title = ("bench step kernels (SGEMM 4096x4096x1024 fp32, HGEMM 4096^3 fp16->fp32)" if name == "step"
+             else f"configuration {name}")
+    lines = [f"# rocprofv3 counters per launch: {title}", "",
+             "Commands (one MI355X; each pass is a run of its own):", "", "```", cmds, "```", "",
+             "Mean over the dispatches of each kernel in the runs (the counters are summed over the "
+             "whole device; SQ_LDS_* and SQ_*_CYCLES count in units of four cycles).", ""]
+    for j, k in enumerate(kernels):
+        lines.append(f"- kernel {j}: `{k}`")
+    lines += ["", "| counter | " + " | ".join(f"kernel {j}" for j in range(len(kernels))) + " |",
+              "|---|" + "---|" * len(kernels)]
+    for c in counters:
+        lines.append(f"| {c} | " + " | ".join(f"{mean[k].get(c, float('nan')):.4g}" for k in kernels) + " |")
+    lines += ["", "Derived:", ""]
+    for j, k in enumerate(kernels):
+        m = mean[k]
+        d = sum(durs[k]) / len(durs[k]) / 1e3
+        parts = [f"- kernel {j} ({d:.1f} us per profiled launch):"]
+        if m.get("SQ_INSTS_MFMA"):
+            parts.append(f"{m['SQ_VALU_MFMA_BUSY_CYCLES'] / m['SQ_INSTS_MFMA']:.1f} matrix-core cycles "
+                         f"per MFMA instruction, {m['SQ_INSTS_MFMA']:.4g} MFMA instructions;")
+            if m.get("GRBM_GUI_ACTIVE"):
+                # busy cycles are counted per SIMD summed over the device (256 CUs x 4 SIMDs)
+                parts.append(f"matrix cores busy {100 * m['SQ_VALU_MFMA_BUSY_CYCLES'] / (1024 * m['GRBM_GUI_ACTIVE']):.1f}% "
+                             f"of the GPU-active cycles;")
+        if m.get("SQ_LDS_IDX_ACTIVE"):
+            parts.append(f"LDS bank conflicts {100 * m.get('SQ_LDS_BANK_CONFLICT', 0) / m['SQ_LDS_IDX_ACTIVE']:.2f}% "
+                         f"of LDS-active cycles;")
+        if m.get("TCC_HIT_sum") is not None and m.get("TCC_MISS_sum"):
+            parts.append(f"L2 hit rate {100 * m['TCC_HIT_sum'] / (m['TCC_HIT_sum'] + m['TCC_MISS_sum']):.1f}%;")
+        if m.get("SQ_INSTS_MFMA") and m.get("SQ_INSTS_VALU") is not None:
+            parts.append(f"{m['SQ_INSTS_VALU'] / m['SQ_INSTS_MFMA']:.2f} VALU instructions (MFMA included) "
+                         f"per MFMA.")
+        if m.get("SQ_WAVE_CYCLES") and m.get("SQ_WAIT_INST_ANY") is not None:
+            parts.append(f"waves waiting on an instruction {100 * m['SQ_WAIT_INST_ANY'] / m['SQ_WAVE_CYCLES']:.0f}% "
+                         f"of wave cycles.")
+        lines.append(" ".join(parts))
+    fname = ("counters_sgemm4096x4096x1024_hgemm4096cube.md" if name == "step" else f"counters_{_slug(name)}.md")
+    path = os.path.join(ROOT, "profiles", fname)
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(path)
+    return 0
+
+
+def write_traffic(name: str, fetch_csv: str, write_csv: str) -> int:
+    """Per-launch HBM traffic of the library's kernels in a --profile NAME --copy-calibration
+    run, from FETCH_SIZE / WRITE_SIZE counter runs, each scaled by the ratio of known
+    bytes to counted bytes for the calibration copy.  The records are merged into the
+    JSON block of profiles/hbm_traffic.md (step kernels under "sgemm" and "hgemm",
+    other configurations under their names)."""
+    import csv
+
+    def per_kernel(path, counter):
+        vals = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            kname, value = r["Kernel_Name"], float(r["Counter_Value"]) * 1024.0
+            key = ("sgemm" if "sgemm" in kname else "hgemm") if "gemm" in kname else "copy"
+            if key == "copy" and value < COPY_BYTES / 8:
+                continue   # other small kernels of the run (tensor fills), not the calibration copy
+            vals.setdefault(key, {}).setdefault(kname, []).append(value)
+        return vals
+
+    fetch, write = per_kernel(fetch_csv, "FETCH_SIZE"), per_kernel(write_csv, "WRITE_SIZE")
+
+    def mean(d, key):
+        items = d[key]
+        allv = [x for v in items.values() for x in v]
+        return " + ".join(sorted(items)), sum(allv) / len(allv)
+
+    copy_name, copy_f = mean(fetch, "copy")
+    _, copy_w = mean(write, "copy")
+    scale_f, scale_w = COPY_BYTES / copy_f, COPY_BYTES / copy_w
+    try:
+        recs = _traffic_records()
+    except (OSError, ValueError):
+        recs = {}
+    recs["copy_calibration"] = {"kernel": copy_name, "bytes": COPY_BYTES, "fetch_counted": copy_f,
+                                "write_counted": copy_w, "fetch_scale": scale_f, "write_scale": scale_w}
+    if name == "step":
+        targets = [("sgemm", "sgemm", STEP_WORKLOADS["sgemm"],
+                    4 * (4096 * 1024 * 2 + 4096 * 4096), "step"),
+                   ("hgemm", "hgemm", STEP_WORKLOADS["hgemm"], 2 * (4096 * 4096 * 2) + 4 * 4096 * 4096, "step")]
+    else:
+        c = {x["name"]: x for x in extra_configs()}[name]
+        kind = "sgemm" if c["kind"] == "f32" else "hgemm"
+        targets = [(name, kind, name, config_bytes(c), name)]
+    for key, kind, workload, alg, prof in targets:
+        kname, f = mean(fetch, kind)
+        _, w = mean(write, kind)
+        total = f * scale_f + w * scale_w
+        recs[key] = {"kernel": kname, "workload": workload, "profile": prof, "source_sha": source_digest(kind),
+                     "fetch_bytes_per_launch": f * scale_f, "write_bytes_per_launch": w * scale_w,
+                     "hbm_bytes_per_launch": total, "algorithmic_bytes": alg}
+    rows = []
+    for key, r in recs.items():
+        if key == "copy_calibration":
+            continue
+        rows.append(f"| {key} | {r['workload']} | {r['fetch_bytes_per_launch'] / 1e6:.1f} | "
+                    f"{r['write_bytes_per_launch'] / 1e6:.1f} | {r['hbm_bytes_per_launch'] / 1e6:.1f} | "
+                    f"{r['algorithmic_bytes'] / 1e6:.1f} | {r['hbm_bytes_per_launch'] / r['algorithmic_bytes']:.2f} |")
+    cmd = ("cd /tmp && timeout -s KILL 120 rocprofv3 --pmc FETCH_SIZE --output-format csv -d $OUT/traffic_fetch -o t -- "
+           "python3 $R/bench.py --profile NAME --steps 3 --warmup 1 --copy-calibration\n"
+           "cd /tmp && timeout -s KILL 120 rocprofv3 --pmc WRITE_SIZE --output-format csv -d $OUT/traffic_write -o t -- "
+           "python3 $R/bench.py --profile NAME --steps 3 --warmup 1 --copy-calibration\n"
+           "python3 $R/bench.py --write-traffic NAME $OUT/traffic_fetch/t_counter_collection.csv "
+           "$OUT/traffic_write/t_counter_collection.csv\n"
+           "# R = repository root, OUT = an output directory, NAME = step or a configuration name")
+    cal = recs["copy_calibration"]
+    text = ("# HBM traffic per launch (rocprofv3 FETCH_SIZE / WRITE_SIZE)\n\n"
+            f"Commands (one MI355X):\n\n```\n{cmd}\n```\n\n"
+            f"Calibration (latest run): a plain elementwise copy of {COPY_BYTES >> 20} MiB reads and writes "
+            f"{COPY_BYTES} bytes; the counters read {cal['fetch_counted']:.0f} B fetched and "
+            f"{cal['write_counted']:.0f} B written, so fetch counts are scaled by {cal['fetch_scale']:.4f} and "
+            f"write counts by {cal['write_scale']:.4f}.\n\n"
+            "| record | workload | fetched (MB) | written (MB) | total (MB) | algorithmic (MB) | ratio |\n"
+            "|---|---|---|---|---|---|---|\n" + "\n".join(rows) + "\n\n"
+            "Machine-readable copy (bench.py reads it; a record whose source_sha no longer matches the kernel "
+            "source is ignored):\n\n```json\n" + json.dumps(recs, indent=1) + "\n```\n")
+    with open(TRAFFIC_FILE, "w") as f:
+        f.write(text)
+    print(text)
+    return 0
 
 
 if __name__ == "__main__":
