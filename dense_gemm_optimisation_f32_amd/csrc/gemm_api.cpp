@@ -4,12 +4,64 @@
 #include <limits.h>
 #include <stdint.h>
 
+#include <map>
+#include <mutex>
+#include <utility>
+#include <vector>
+
 #include "../../include/mi355gemm.h"
 #include "gemm_internal.h"
 
 namespace {
 
 using mi355gemm::GemmProblem;
+
+// Scratch for K splits, one buffer per (device, stream): calls on one stream
+// run one after another, so they can share it, and calls on different streams
+// never do.  A buffer is allocated (and its counters cleared on the stream) the
+// first time a call on that stream needs more than it holds; the one it
+// replaces may still be in use by work queued on the stream, so it is kept
+// until the process ends.  Nothing is allocated while the stream is being
+// captured into a graph: the call then gets no scratch and runs a plan that
+// needs none.
+constexpr size_t kScratchMin = 16u << 20;
+constexpr size_t kScratchMax = 512u << 20;
+
+struct StreamScratch {
+    void *ptr = nullptr;
+    size_t bytes = 0;
+};
+std::mutex g_scratch_mutex;
+std::map<std::pair<int, hipStream_t>, StreamScratch> g_scratch;
+std::vector<void *> g_scratch_retired;
+
+void *stream_scratch(void *, size_t bytes, hipStream_t stream)
+{
+    if (bytes > kScratchMax) return nullptr;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    StreamScratch &e = g_scratch[{dev, stream}];
+    if (e.bytes >= bytes) return e.ptr;
+    hipStreamCaptureStatus status = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &status) != hipSuccess || status != hipStreamCaptureStatusNone) return nullptr;
+    size_t want = bytes < kScratchMin ? kScratchMin : bytes;
+    want = (want + (1u << 20) - 1) & ~(size_t)((1u << 20) - 1);
+    void *p = nullptr;
+    if (hipMalloc(&p, want) != hipSuccess) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    if (hipMemsetAsync(p, 0, mi355gemm::kCounterBytes, stream) != hipSuccess) {
+        (void)hipGetLastError();
+        (void)hipFree(p);
+        return nullptr;
+    }
+    if (e.ptr) g_scratch_retired.push_back(e.ptr);
+    e.ptr = p;
+    e.bytes = want;
+    return p;
+}
 
 constexpr int kMaxGridZ = 65535;  // batch members per launch
 
@@ -88,6 +140,7 @@ GemmProblem make(int tA, int tB, int M, int N, int K, float alpha, const void *A
                  const void *B, int ldb, long long sB, float beta, float *C, int ldc, long long sC, int batch)
 {
     GemmProblem p;
+    p.scratch.get = stream_scratch;
     p.transA = tA; p.transB = tB;
     p.M = M; p.N = N; p.K = K; p.batch = batch;
     p.alpha = alpha; p.beta = beta;

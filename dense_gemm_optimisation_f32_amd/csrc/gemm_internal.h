@@ -7,6 +7,19 @@
 
 namespace mi355gemm {
 
+// Scratch device memory a launcher may use for one call (the partial tiles and
+// tile counters of a K split over workgroups).  get(ctx, bytes, stream) returns
+// at least `bytes` bytes, 256-byte aligned, whose first kCounterBytes bytes are
+// zero, or nullptr when no such memory can be had (the launcher then takes a
+// plan that needs none).  Every kernel that uses the counters leaves them zero.
+// The memory is not used by another call that can overlap this one.
+constexpr size_t kCounterBytes = 256 * 1024;   // 65536 tile counters
+struct Scratch {
+    void *(*get)(void *ctx, size_t bytes, hipStream_t stream) = nullptr;
+    void *ctx = nullptr;
+    void *acquire(size_t bytes, hipStream_t stream) const { return get ? get(ctx, bytes, stream) : nullptr; }
+};
+
 // One (possibly batched) row-major GEMM after argument checking.  Offsets are
 // 64-bit; strides are in elements.
 struct GemmProblem {
@@ -19,6 +32,7 @@ struct GemmProblem {
     long long ldb, strideB;
     float *C;
     long long ldc, strideC;
+    Scratch scratch;      // where a K split may keep its partial tiles
 };
 
 // fp32 SGEMM on fp32 MFMA (K > 0, alpha != 0, M, N > 0; any transA/transB).

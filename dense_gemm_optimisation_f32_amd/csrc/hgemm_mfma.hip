@@ -51,6 +51,7 @@
 #include "gemm_internal.h"
 #include "tile_order.h"
 #include "epilogue.h"
+#include "plan16.h"
 
 #include <type_traits>
 
@@ -92,6 +93,15 @@ struct HgemmArgs {
     float *C;
     long long ldc, sC;
     int tiles_m, tiles_n;
+    // K split over workgroups (direct-to-LDS kernel only): nsplit workgroups
+    // share each tile, split s taking whole slices [s*q + min(s, r), ...) of the
+    // nk slices (q = nk / nsplit, r = nk % nsplit) and the last split the K
+    // tail; their partial tiles meet in ws_part and the last to finish (counted
+    // in ws_count) adds them in split order and runs the epilogue.  nsplit = 1:
+    // no split, ws_* unused.
+    int nsplit;
+    unsigned *ws_count;   // one counter per (member, tile), zero between launches
+    float *ws_part;       // nsplit partial tiles per (member, tile)
 };
 
 template <int BM_, int BN_>
@@ -358,9 +368,10 @@ __global__ __launch_bounds__(256) void hgemm_mfma_kernel(HgemmArgs p)
 // one wave's MFMAs cover the other's LDS latency.
 // Requires M % BM == 0, N % BN == 0, K % BK == 0, K >= STAGES*BK, 16-byte
 // aligned rows and byte offsets within a slice below 2^31.
-template <int BM_, int BN_, int STAGES_, int WM_, int WN_, int BK_>
+template <int BM_, int BN_, int STAGES_, int WM_, int WN_, int BK_, bool SPLITS_ = false>
 struct HgDmaCfg {
     static constexpr int BM = BM_, BN = BN_, BK = BK_, STAGES = STAGES_, WM = WM_, WN = WN_;
+    static constexpr bool SPLITS = SPLITS_;   // also built with a K split over workgroups
     static constexpr int NW = WM * WN, NT = 64 * NW;
     static constexpr int A_CPR = BK / 8;                        // 16-byte chunks per A row
     static constexpr int TM = BM / WM, TN = BN / WN;
@@ -478,7 +489,7 @@ __device__ __forceinline__ unsigned frag_offset(int first, int lane, int s)
 // columns, the K % BK tail is read straight from global memory after the last
 // slice, and stores outside C are skipped); a 16-byte chunk of an
 // MN-contiguous operand may straddle M or N (see the slice count below).
-template <class Cfg, bool BF, bool TA, bool TB, bool MASK>
+template <class Cfg, bool BF, bool TA, bool TB, bool MASK, bool SPLIT>
 __global__ __launch_bounds__(Cfg::NT) void hgemm_dma_kernel(HgemmArgs p)
 {
     constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, S = Cfg::STAGES;
@@ -488,16 +499,31 @@ __global__ __launch_bounds__(Cfg::NT) void hgemm_dma_kernel(HgemmArgs p)
     const unsigned lds0 = (unsigned)(uintptr_t)lds;
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    int mb, tm, tn;   // batch member, tile row, tile column
-    tile_coords(blockIdx.x, blockIdx.z, gridDim.z, p.tiles_m, p.tiles_n, &mb, &tm, &tn);
+    const int nsplit = SPLIT ? p.nsplit : 1;
+    int mb, tm, tn, sp;   // batch member, tile row, tile column, K split
+    tile_coords_split(blockIdx.x, blockIdx.z, gridDim.z, p.tiles_m, p.tiles_n, nsplit, &mb, &tm, &tn, &sp);
     const long long m0 = (long long)tm * BM, n0 = (long long)tn * BN;
     const long long lda = p.lda, ldb = p.ldb, ldc = p.ldc;
-    // first element of the tile's slice 0 in each operand, and the bytes
-    // between consecutive slices
-    const char *Ab = reinterpret_cast<const char *>(p.A + (long long)mb * p.sA + (A_KC ? m0 * lda : m0));
-    const char *Bb = reinterpret_cast<const char *>(p.B + (long long)mb * p.sB + (B_KC ? n0 * ldb : n0));
+    // An MN-contiguous operand whose M or N is not a multiple of eight has a
+    // chunk that straddles that edge.  Its halves past the edge only reach C
+    // entries that are never stored, and in any row but the matrix's last they
+    // lie in the next row.  The slices then stop before row K-1 and the K tail
+    // below takes the rest, so no slice load reads past the operand.
+    const bool straddle = MASK && ((!A_KC && p.M % 8 != 0) || (!B_KC && p.N % 8 != 0));
+    const int nk_all = (p.K - (straddle ? 1 : 0)) / BK;   // whole slices of the problem
+    // this workgroup's slices [s_begin, s_begin + nk), nk >= S (checked by the launcher)
+    const int q_split = nk_all / nsplit, r_split = nk_all % nsplit;
+    const int s_begin = sp * q_split + (sp < r_split ? sp : r_split);
+    const int nk = q_split + (sp < r_split ? 1 : 0);
+    const bool last_split = sp == nsplit - 1;
+    // first element of the workgroup's first slice in each operand, and the
+    // bytes between consecutive slices
     const long long stepA = A_KC ? BK * 2 : BK * lda * 2;
     const long long stepB = B_KC ? BK * 2 : BK * ldb * 2;
+    const char *Ab = reinterpret_cast<const char *>(p.A + (long long)mb * p.sA + (A_KC ? m0 * lda : m0)) +
+                     (long long)s_begin * stepA;
+    const char *Bb = reinterpret_cast<const char *>(p.B + (long long)mb * p.sB + (B_KC ? n0 * ldb : n0)) +
+                     (long long)s_begin * stepB;
     float *C = p.C + (long long)mb * p.sC;
 
     // Loading waves are NW-LW .. NW-1; loader index lw numbers their 1 KB
@@ -631,13 +657,6 @@ __global__ __launch_bounds__(Cfg::NT) void hgemm_dma_kernel(HgemmArgs p)
         }
     };
 
-    // An MN-contiguous operand whose M or N is not a multiple of eight has a
-    // chunk that straddles that edge.  Its halves past the edge only reach C
-    // entries that are never stored, and in any row but the matrix's last they
-    // lie in the next row.  The slices then stop before row K-1 and the K tail
-    // below takes the rest, so no slice load reads past the operand.
-    const bool straddle = MASK && ((!A_KC && p.M % 8 != 0) || (!B_KC && p.N % 8 != 0));
-    const int nk = (p.K - (straddle ? 1 : 0)) / BK;   // whole slices, >= S (checked by the launcher)
     // Prologue: slices 0..S-1 in flight; slice 0 resident; substep 0 fragments read.
 #pragma unroll
     for (int st = 0; st < S; ++st) issue_slice(st, st);
@@ -647,16 +666,14 @@ __global__ __launch_bounds__(Cfg::NT) void hgemm_dma_kernel(HgemmArgs p)
 
     // Steady state: slices up to t+S-1 issued, slice t+1 needed.
     for (int t = 0; t + S < nk; ++t) step(t, std::integral_constant<int, S - 2>{}, std::true_type{}, t >= 1);
-    // Tail: no more slices to issue; the outstanding count drains to zero.
+    // Tail: no more slices to issue; the outstanding count drains to zero
+    // (with staggered refills, the upper waves still issue their share of the
+    // last slice during the first of these steps).
     const int t0 = nk - S;
-    if constexpr (S == 4) {
-        step(t0 + 0, std::integral_constant<int, 2>{}, std::false_type{}, t0 >= 1);
-        step(t0 + 1, std::integral_constant<int, 1>{}, std::false_type{}, false);
-        step(t0 + 2, std::integral_constant<int, 0>{}, std::false_type{}, false);
-    } else {
-        static_assert(S == 2, "ring of two or four slices");
-        step(t0 + 0, std::integral_constant<int, 0>{}, std::false_type{}, false);
-    }
+    static_assert(S >= 2 && S <= 4, "ring of two to four slices");
+    step(t0, std::integral_constant<int, S - 2>{}, std::false_type{}, t0 >= 1);
+    if constexpr (S >= 3) step(t0 + 1, std::integral_constant<int, S - 3>{}, std::false_type{}, false);
+    if constexpr (S >= 4) step(t0 + 2, std::integral_constant<int, S - 4>{}, std::false_type{}, false);
     {   // last slice: everything is resident
         const int slot = (nk - 1) % S;
 #pragma unroll
@@ -670,8 +687,8 @@ __global__ __launch_bounds__(Cfg::NT) void hgemm_dma_kernel(HgemmArgs p)
         // The K % BK tail, after the whole slices (k still ascends): each lane
         // loads its eight k of each operand fragment straight from global
         // memory, zero for k >= K, rows and columns clamped as for the slices.
-        const int K = p.K, k0 = nk * BK;
-        if (k0 < K) {
+        const int K = p.K, k0 = (s_begin + nk) * BK;
+        if (last_split && k0 < K) {
             const uint16_t *Am = p.A + (long long)mb * p.sA;
             const uint16_t *Bm = p.B + (long long)mb * p.sB;
             long long ar[Cfg::FM], bc[Cfg::FN];
@@ -705,6 +722,72 @@ __global__ __launch_bounds__(Cfg::NT) void hgemm_dma_kernel(HgemmArgs p)
                 for (int jj = 0; jj < Cfg::FN; ++jj)
                     tb[jj] = B_KC ? eight(Bm + bc[jj] * ldb + kq, 1, kq) : eight(Bm + (long long)kq * ldb + bc[jj], ldb, kq);
                 mfmas(ta, tb);
+            }
+        }
+    }
+
+    if constexpr (SPLIT) {
+        // K split: publish this workgroup's partial tile, count the arrival, and
+        // let the last of the tile's nsplit workgroups add the partials in split
+        // order -- a fixed order, so the bits do not depend on which finishes
+        // last -- and run the epilogue.  No workgroup waits for another.
+        //
+        // Visibility across XCDs: the partials are written and read with
+        // device-scope accesses (relaxed atomic stores and loads at agent scope,
+        // which go through to the device's point of coherence instead of staying
+        // in one XCD's L2), each wave waits for its stores to complete before the
+        // barrier that precedes the arrival count, and the partials are read only
+        // after the count has shown the workgroup to be last.  Nothing else
+        // crosses workgroups, so no L2-wide write-back or invalidation is needed.
+        //
+        // Layout per (member, tile, split): per wave and accumulator register,
+        // the 64 lanes' values side by side, so each lane reads back exactly the
+        // entries it holds and every access is a full 256-byte row.
+        constexpr int NR = Cfg::FM * Cfg::FN * 16;   // accumulator registers per lane
+        const long long tile_id = ((long long)mb * p.tiles_m + tm) * p.tiles_n + tn;
+        const long long tiles_all = (long long)gridDim.z * p.tiles_m * p.tiles_n;
+        auto part = [&](int s) -> float * {
+            return p.ws_part + ((s * tiles_all + tile_id) * Cfg::NW + wave) * NR * 64 + lane;
+        };
+        auto reg = [&](int r) -> float { return acc[r / 16 / Cfg::FN][(r / 16) % Cfg::FN][r % 16]; };
+        auto set_reg = [&](int r, float v) { acc[r / 16 / Cfg::FN][(r / 16) % Cfg::FN][r % 16] = v; };
+        {
+            float *mine = part(sp);
+#pragma unroll
+            for (int r = 0; r < NR; ++r) __hip_atomic_store(mine + r * 64, reg(r), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        __shared__ unsigned arrived;
+        __builtin_amdgcn_s_waitcnt(0);   // this wave's partial stores are complete
+        __syncthreads();
+        if (tid == 0)
+            arrived = __hip_atomic_fetch_add(p.ws_count + tile_id, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        if (arrived != (unsigned)(nsplit - 1)) return;
+        if (tid == 0) __hip_atomic_store(p.ws_count + tile_id, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        auto load = [&](const float *q, int r) {
+            return __hip_atomic_load(q + r * 64, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        };
+        if (nsplit == 2) {
+            // p0 + p1: IEEE addition is commutative, so either workgroup gets the same sum
+            const float *other = part(1 - sp);
+            float o[NR];
+#pragma unroll
+            for (int r = 0; r < NR; ++r) o[r] = load(other, r);
+#pragma unroll
+            for (int r = 0; r < NR; ++r) set_reg(r, reg(r) + o[r]);
+        } else {
+            // ((p0 + p1) + p2) + ...: every partial, this workgroup's included,
+            // read back in split order
+            const float *first = part(0);
+#pragma unroll
+            for (int r = 0; r < NR; ++r) set_reg(r, load(first, r));
+            for (int s = 1; s < nsplit; ++s) {
+                const float *ps = part(s);
+                float o[NR];
+#pragma unroll
+                for (int r = 0; r < NR; ++r) o[r] = load(ps, r);
+#pragma unroll
+                for (int r = 0; r < NR; ++r) set_reg(r, reg(r) + o[r]);
             }
         }
     }
@@ -758,6 +841,7 @@ hipError_t launch_cfg(const GemmProblem &q, hipStream_t stream)
     a.C = q.C; a.ldc = q.ldc; a.sC = q.strideC;
     a.tiles_m = (q.M + Cfg::BM - 1) / Cfg::BM;
     a.tiles_n = (q.N + Cfg::BN - 1) / Cfg::BN;
+    a.nsplit = 1; a.ws_count = nullptr; a.ws_part = nullptr;
     // 16-byte loads need 4-byte aligned row starts (column offsets are
     // multiples of eight halves)
     const bool vec = (q.lda % 2 == 0) && (q.ldb % 2 == 0) &&
@@ -783,7 +867,7 @@ hipError_t launch_cfg(const GemmProblem &q, hipStream_t stream)
 using HgDma256 = HgDmaCfg<256, 256, 2, 2, 4, 64>;
 // 128x128 tile, 8 waves (2 x 4) of 64x32, BK = 64, four slots of 32 KB: for
 // grids that 256x256 tiles would leave under-filled.
-using HgDma128 = HgDmaCfg<128, 128, 4, 2, 4, 64>;
+using HgDma128 = HgDmaCfg<128, 128, 4, 2, 4, 64, true>;
 // 64x128 tile, 8 waves (2 x 4) of 32x32, four slots of 24 KB: for grids that
 // 128x128 tiles leave at most half filled.  Its A slice is 64 wide, so it takes
 // only A stored M x K (B either way).
@@ -798,54 +882,56 @@ constexpr bool dma_orientation_ok(bool tA, bool tB)
     return (!tA || Cfg::BM >= 128) && (tB || Cfg::BN >= 128);
 }
 
-// The direct-to-LDS kernel applies: 4-byte aligned operand rows, at least
-// STAGES whole slices of k, an MN-contiguous operand (A stored K x M, B stored
-// K x N) at least eight wide where M or N is not a multiple of eight, and
-// 32-bit slice offsets.
-template <class Cfg>
-bool dma_ok(const GemmProblem &q)
-{
-    // 16-byte chunks start a multiple of eight halves into a row, so 4-byte
-    // aligned rows keep them dword aligned, which is all the 16-byte loads need
-    const bool aligned = (q.lda % 2 == 0) && (q.ldb % 2 == 0) && (q.strideA % 2 == 0) &&
-                         (q.strideB % 2 == 0) && (reinterpret_cast<uintptr_t>(q.A) % 4 == 0) &&
-                         (reinterpret_cast<uintptr_t>(q.B) % 4 == 0);
-    // a chunk straddling M or N (see the kernel) needs M or N >= 8, so that its
-    // overflow stays in the next row, and one row of K left to the tail
-    const bool straddle = (q.transA && q.M % 8 != 0) || (!q.transB && q.N % 8 != 0);
-    const bool shape = q.K - (straddle ? 1 : 0) >= Cfg::BK * Cfg::STAGES && (!q.transA || q.M % 8 == 0 || q.M >= 8) &&
-                       (q.transB || q.N % 8 == 0 || q.N >= 8);
-    // per-lane offsets within one slice are 32-bit: rows of the slice times ld
-    const long long rows_a = q.transA ? Cfg::BK : Cfg::BM, rows_b = q.transB ? Cfg::BN : Cfg::BK;
-    const bool fits = rows_a * q.lda * 2 < (1LL << 31) && rows_b * q.ldb * 2 < (1LL << 31);
-    return aligned && shape && fits && dma_orientation_ok<Cfg>(q.transA, q.transB);
-}
-
-template <class Cfg, bool BF, bool MASK>
+template <class Cfg, bool BF, bool MASK, bool SPLIT>
 void launch_dma_ops(const HgemmArgs &a, dim3 grid, bool tA, bool tB, hipStream_t stream)
 {
     const dim3 block(Cfg::NT);
     if (!tA && !tB) {
         if constexpr (dma_orientation_ok<Cfg>(false, false))
-            hipLaunchKernelGGL((hgemm_dma_kernel<Cfg, BF, false, false, MASK>), grid, block, 0, stream, a);
+            hipLaunchKernelGGL((hgemm_dma_kernel<Cfg, BF, false, false, MASK, SPLIT>), grid, block, 0, stream, a);
     } else if (!tA) {
         if constexpr (dma_orientation_ok<Cfg>(false, true))
-            hipLaunchKernelGGL((hgemm_dma_kernel<Cfg, BF, false, true, MASK>), grid, block, 0, stream, a);
+            hipLaunchKernelGGL((hgemm_dma_kernel<Cfg, BF, false, true, MASK, SPLIT>), grid, block, 0, stream, a);
     } else if (!tB) {
         if constexpr (dma_orientation_ok<Cfg>(true, false))
-            hipLaunchKernelGGL((hgemm_dma_kernel<Cfg, BF, true, false, MASK>), grid, block, 0, stream, a);
+            hipLaunchKernelGGL((hgemm_dma_kernel<Cfg, BF, true, false, MASK, SPLIT>), grid, block, 0, stream, a);
     } else {
         if constexpr (dma_orientation_ok<Cfg>(true, true))
-            hipLaunchKernelGGL((hgemm_dma_kernel<Cfg, BF, true, true, MASK>), grid, block, 0, stream, a);
+            hipLaunchKernelGGL((hgemm_dma_kernel<Cfg, BF, true, true, MASK, SPLIT>), grid, block, 0, stream, a);
     }
 }
 
+// Bytes of scratch a K split over nsplit workgroups per tile needs: the tile
+// counters, then nsplit fp32 partial tiles per (member, tile).
+template <class Cfg>
+size_t split_bytes(const GemmProblem &q, int nsplit)
+{
+    const long long tiles = (long long)((q.M + Cfg::BM - 1) / Cfg::BM) * ((q.N + Cfg::BN - 1) / Cfg::BN) * q.batch;
+    return kCounterBytes + (size_t)nsplit * tiles * Cfg::BM * Cfg::BN * sizeof(float);
+}
+
+// A K split over nsplit workgroups per tile applies: scratch given, one
+// counter per (member, tile), and every split at least STAGES whole slices (the
+// ring is filled before the first wait, so fewer would load past the split's
+// range -- and, for the last split, past K).
+template <class Cfg>
+bool split_ok(const GemmProblem &q, int nsplit, const void *ws)
+{
+    const long long tiles = (long long)((q.M + Cfg::BM - 1) / Cfg::BM) * ((q.N + Cfg::BN - 1) / Cfg::BN) * q.batch;
+    const bool straddle = (q.transA && q.M % 8 != 0) || (!q.transB && q.N % 8 != 0);
+    const int slices = (q.K - (straddle ? 1 : 0)) / Cfg::BK;
+    return ws != nullptr && tiles <= (long long)(kCounterBytes / sizeof(unsigned)) && slices / nsplit >= Cfg::STAGES;
+}
+
+
+// ws: scratch of split_bytes<Cfg>(q, nsplit) bytes when nsplit > 1.
 template <class Cfg, bool BF>
-hipError_t launch_dma(const GemmProblem &q, hipStream_t stream)
+hipError_t launch_dma(const GemmProblem &q, hipStream_t stream, int nsplit = 1, void *ws = nullptr)
 {
     // a storage combination the tile cannot take launches nothing below: refuse
     // it here so that the caller sees an error instead of an unwritten C
     if (!dma_orientation_ok<Cfg>(q.transA, q.transB)) return hipErrorInvalidValue;
+    if (nsplit > 1 && !split_ok<Cfg>(q, nsplit, ws)) return hipErrorInvalidValue;
     HgemmArgs a;
     a.M = q.M; a.N = q.N; a.K = q.K;
     a.alpha = q.alpha; a.beta = q.beta;
@@ -854,45 +940,64 @@ hipError_t launch_dma(const GemmProblem &q, hipStream_t stream)
     a.C = q.C; a.ldc = q.ldc; a.sC = q.strideC;
     a.tiles_m = (q.M + Cfg::BM - 1) / Cfg::BM;
     a.tiles_n = (q.N + Cfg::BN - 1) / Cfg::BN;
-    const dim3 grid(a.tiles_m * a.tiles_n, 1, q.batch);
+    a.nsplit = nsplit;
+    a.ws_count = static_cast<unsigned *>(ws);
+    a.ws_part = ws ? reinterpret_cast<float *>(static_cast<char *>(ws) + kCounterBytes) : nullptr;
+    const dim3 grid(a.tiles_m * a.tiles_n * nsplit, 1, q.batch);
     const bool whole = q.M % Cfg::BM == 0 && q.N % Cfg::BN == 0 && q.K % Cfg::BK == 0;
-    if (whole)
-        launch_dma_ops<Cfg, BF, false>(a, grid, q.transA, q.transB, stream);
-    else
-        launch_dma_ops<Cfg, BF, true>(a, grid, q.transA, q.transB, stream);
+    if (nsplit > 1) {
+        if constexpr (Cfg::SPLITS) {
+            if (whole)
+                launch_dma_ops<Cfg, BF, false, true>(a, grid, q.transA, q.transB, stream);
+            else
+                launch_dma_ops<Cfg, BF, true, true>(a, grid, q.transA, q.transB, stream);
+        } else {
+            return hipErrorInvalidValue;
+        }
+    } else if (whole) {
+        launch_dma_ops<Cfg, BF, false, false>(a, grid, q.transA, q.transB, stream);
+    } else {
+        launch_dma_ops<Cfg, BF, true, false>(a, grid, q.transA, q.transB, stream);
+    }
     return hipGetLastError();
+}
+
+template <class Cfg>
+constexpr bool same_shape(const TileShape16 &t)
+{
+    return Cfg::BM == t.bm && Cfg::BN == t.bn && Cfg::BK == t.bk && Cfg::STAGES == t.stages;
+}
+static_assert(same_shape<HgDma256>(kDma256) && same_shape<HgDma128>(kDma128) && same_shape<HgDma64x128>(kDma64x128),
+              "plan16.h describes the tiles built here");
+
+Problem16 planner_view(const GemmProblem &q)
+{
+    Problem16 v;
+    v.M = q.M; v.N = q.N; v.K = q.K; v.batch = q.batch;
+    v.transA = q.transA; v.transB = q.transB;
+    v.lda = q.lda; v.ldb = q.ldb; v.strideA = q.strideA; v.strideB = q.strideB;
+    v.A = reinterpret_cast<uintptr_t>(q.A); v.B = reinterpret_cast<uintptr_t>(q.B);
+    return v;
 }
 
 template <bool BF>
 hipError_t launch_gemm16(const GemmProblem &q, hipStream_t stream)
 {
-    // Direct-to-LDS 256x256 tiles when they give at least one tile per CU,
-    // else 128x128 ones (64x128 where those fill few CUs, below); 128x128
-    // register-staged tiles (with bounds checks where needed) for operands the
-    // direct-to-LDS kernel cannot take.
-    //
-    // Both direct-to-LDS tiles run one workgroup per CU, so a grid runs in
-    // rounds of 256 workgroups.  A 128x128 tile does a quarter of a 256x256
-    // tile's work at about 0.6 of its rate (measured), i.e. takes 0.4 of its
-    // time: the 256x256 tile wins when 5 * its rounds <= 2 * the 128x128 rounds.
-    const long long t256 = (long long)((q.M + 255) / 256) * ((q.N + 255) / 256) * q.batch;
-    const long long t128 = (long long)((q.M + 127) / 128) * ((q.N + 127) / 128) * q.batch;
-    const bool ok256 = dma_ok<HgDma256>(q), ok128 = dma_ok<HgDma128>(q);
-    // 64x128 tiles on grids of 128x128 tiles that fill at most a quarter of the
-    // CUs, or at most half with K >= 4096 (measured: 512x4096x4096 29.8 -> 26.0
-    // us, 1000x1000x2000 16.5 -> 12.9 us; 1024x2048x2048, half filled with
-    // K = 2048, 17.0 -> 17.8 us, so it keeps 128x128 tiles)
-    if (ok128 && (4 * t128 <= 256 || (2 * t128 <= 256 && q.K >= 4096)) && dma_ok<HgDma64x128>(q))
-        return launch_dma<HgDma64x128, BF>(q, stream);
-    if (ok256 && ok128) {
-        const long long r256 = (t256 + 255) / 256, r128 = (t128 + 255) / 256;
-        if (5 * r256 <= 2 * r128) return launch_dma<HgDma256, BF>(q, stream);
-        return launch_dma<HgDma128, BF>(q, stream);
+    const Problem16 v = planner_view(q);
+    Plan16 plan = plan16(v, true);
+    void *ws = nullptr;
+    if (plan.nsplit > 1) {
+        ws = q.scratch.acquire(split_bytes<HgDma128>(q, plan.nsplit), stream);
+        if (ws == nullptr) plan = plan16(v, false);   // no scratch to be had: a plan that needs none
     }
-    if (ok256 && t256 >= 256) return launch_dma<HgDma256, BF>(q, stream);
-    if (ok128) return launch_dma<HgDma128, BF>(q, stream);
-    if (t128 < 256) return launch_cfg<Hg64, BF>(q, stream);
-    return launch_cfg<Hg128, BF>(q, stream);
+    switch (plan.kernel) {
+    case Kernel16::Dma256: return launch_dma<HgDma256, BF>(q, stream);
+    case Kernel16::Dma128: return launch_dma<HgDma128, BF>(q, stream, plan.nsplit, ws);
+    case Kernel16::Dma64x128: return launch_dma<HgDma64x128, BF>(q, stream);
+    case Kernel16::Reg64: return launch_cfg<Hg64, BF>(q, stream);
+    case Kernel16::Reg128: return launch_cfg<Hg128, BF>(q, stream);
+    }
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_hgemm(const GemmProblem &q, hipStream_t stream)

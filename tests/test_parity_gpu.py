@@ -825,6 +825,103 @@ def test_bf16_and_fp16_agree_on_values_both_hold():
         assert torch.equal(out[0], out[1])
 
 
+# ------------------------------------------------------------------ K split over workgroups (HGEMM)
+# Shapes whose 128x128 tiles fill at most a quarter of the CUs and whose K holds
+# at least 64 slices split each tile's K range over several workgroups; the last
+# to finish adds the partial tiles in split order.  The split each shape gets is
+# checked on the host by tests/test_plan16.py.
+
+@pytest.mark.parametrize("M,N,K,tA,tB", [
+    (512, 512, 8192, False, False),      # 8 splits of 16 slices
+    (1000, 1000, 5000, False, False),    # 2 splits, ragged tiles and a K tail
+    (300, 200, 6000, False, False),      # 5 splits of 18 or 19 slices, K tail
+    (500, 1002, 8192, False, False),     # B chunks straddling N: the slices stop before row K-1
+    (512, 768, 5000, True, True),
+    (768, 768, 4096, True, False),
+    (768, 768, 4096, False, True),
+])
+def test_split_k_parity(M, N, K, tA, tB):
+    run_and_check("f16", M, N, K, 1.5, -0.5, transA=tA, transB=tB, seed=101)
+    run_and_check("f16", M, N, K, 1.0, 1.0, kind_vals="int4", exact=True, transA=tA, transB=tB, seed=102)
+    run_and_check("f16", M, N, K, 1.0, 0.0, c_nan=True, transA=tA, transB=tB, seed=103)
+
+
+def test_split_k_bf16_and_batched():
+    run_and_check("bf16", 512, 512, 8192, 1.5, -0.5, seed=104)
+    run_and_check("bf16", 1000, 1000, 5000, 1.0, 1.0, kind_vals="int4", exact=True, seed=105)
+    batched_check(256, 384, 4096, 3, 1.5, -0.5)                               # 18 tiles x 4 splits
+    batched_check(256, 384, 4096, 3, 1.0, 1.0, kind_vals="int4", exact=True, seed=106)
+
+
+def test_split_k_deterministic():
+    # the partial tiles are added in split order whichever workgroup finishes last
+    M, N, K = 512, 512, 8192
+    p = si.gemm_problem(M, N, K, in_dtype=np.float16, seed=107)
+    dA, dB = to_dev(p["A"]), to_dev(p["B"])
+    outs = []
+    for _ in range(4):
+        dC = to_dev(p["C"])
+        dg.gemm_f16_f32acc(M, N, K, 1.5, dA, K, dB, N, -0.5, dC, N)
+        torch.cuda.synchronize()
+        outs.append(dC)
+    assert all(torch.equal(outs[0], o) for o in outs[1:])
+
+
+def test_split_k_concurrent_streams():
+    # each stream has its own scratch: split calls on four streams at once
+    note("split-K HGEMM on four streams at once")
+    shapes = [(512, 512, 8192), (1024, 1024, 8192), (300, 200, 6000), (256, 256, 8192)]
+    probs = [si.gemm_problem(M, N, K, in_dtype=np.float16, seed=110 + i) for i, (M, N, K) in enumerate(shapes)]
+    devs = [(to_dev(p["A"]), to_dev(p["B"]), to_dev(p["C"])) for p in probs]
+    streams = [torch.cuda.Stream() for _ in shapes]
+    torch.cuda.synchronize()
+    for _ in range(3):   # repeated: the counters must be left zero by every call
+        for (M, N, K), p, (dA, dB, dC), s in zip(shapes, probs, devs, streams):
+            dC.copy_(to_dev(p["C"]))
+            torch.cuda.synchronize()
+        for (M, N, K), p, (dA, dB, dC), s in zip(shapes, probs, devs, streams):
+            dg.gemm_f16_f32acc(M, N, K, 1.5, dA, K, dB, N, -0.5, dC, N, s)
+        torch.cuda.synchronize()
+        for (M, N, K), p, (_, _, dC) in zip(shapes, probs, devs):
+            ref, bound = oracle.gemm_ref(M, N, K, 1.5, p["A"], K, p["B"], N, -0.5, p["C"], N)
+            assert oracle.normalized_error(rows_of(dC, M, N, N), ref, bound) <= TOL
+
+
+def test_split_k_graph_capture():
+    # A stream that has already run a split call holds its scratch, so a graph
+    # captured on it records the split kernel and replays it bit for bit.  A
+    # stream that has not cannot allocate during capture: its graph records the
+    # unsplit kernel, whose result is equally within tolerance.
+    M, N, K = 512, 512, 8192
+    p = si.gemm_problem(M, N, K, in_dtype=np.float16, seed=120)
+    dA, dB, c0 = to_dev(p["A"]), to_dev(p["B"]), to_dev(p["C"])
+    ref, bound = oracle.gemm_ref(M, N, K, 1.5, p["A"], K, p["B"], N, -0.5, p["C"], N)
+    warm = torch.cuda.Stream()
+    eager = c0.clone()
+    with torch.cuda.stream(warm):
+        dg.gemm_f16_f32acc(M, N, K, 1.5, dA, K, dB, N, -0.5, eager, N, warm)
+    torch.cuda.synchronize()
+    for stream, same_bits in ((warm, True), (torch.cuda.Stream(), False)):
+        out = c0.clone()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            dg.gemm_f16_f32acc(M, N, K, 1.5, dA, K, dB, N, -0.5, out, N, stream)
+        first = None
+        for replay in range(3):
+            out.copy_(c0)
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert oracle.normalized_error(rows_of(out, M, N, N), ref, bound) <= TOL
+            if same_bits:
+                assert torch.equal(out, eager), f"replay {replay} differs from the eager split result"
+            first = out.clone() if first is None else first
+            assert torch.equal(out, first)
+            _ = (dA.float() * 2).sum().item()   # unrelated eager work between replays
+        del g
+
+
 # ------------------------------------------------------------------ graph capture
 def test_graph_capture_replays_match_eager():
     # the library enqueues plain kernel launches on the caller's stream (no memset,

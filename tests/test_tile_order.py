@@ -53,6 +53,30 @@ int main() {
             if (count[m] != 0 && count[m] != 16) { std::printf("xcd %d has part of member %d\n", x, m); return 1; }
         if (members != 2) { std::printf("xcd %d runs %d members\n", x, members); return 1; }
     }
+    // with a K split: a bijection onto (member, tile, split), and the splits of
+    // one tile land on one XCD when the split count divides the items per XCD
+    for (int ns = 1; ns <= 4; ++ns)
+        for (int nb = 1; nb <= 3; ++nb)
+            for (int tm_n = 1; tm_n <= 12; ++tm_n)
+                for (int tn_n = 1; tn_n <= 12; ++tn_n) {
+                    const int items = tm_n * tn_n * ns;
+                    std::vector<int> seen(nb * items, 0), xcd_of(nb * tm_n * tn_n, -1);
+                    bool same_xcd = true;
+                    for (int z = 0; z < nb; ++z)
+                        for (int w = 0; w < items; ++w) {
+                            int mb, tm, tn, sp;
+                            mi355gemm::tile_coords_split(w, z, nb, tm_n, tn_n, ns, &mb, &tm, &tn, &sp);
+                            if (mb < 0 || mb >= nb || tm < 0 || tm >= tm_n || tn < 0 || tn >= tn_n || sp < 0 ||
+                                sp >= ns) { std::printf("split range\n"); return 1; }
+                            const int tile = (mb * tm_n + tm) * tn_n + tn;
+                            if (seen[tile * ns + sp]++) { std::printf("split dup\n"); return 1; }
+                            const int x = (z * items + w) % 8;
+                            if (xcd_of[tile] < 0) xcd_of[tile] = x;
+                            else if (xcd_of[tile] != x) same_xcd = false;
+                        }
+                    if ((nb * items) % (8 * ns) == 0 && !same_xcd) {
+                        std::printf("splits of a tile on two XCDs %d %d %d %d\n", ns, nb, tm_n, tn_n); return 1; }
+                }
     std::printf("ok\n");
     return 0;
 }
