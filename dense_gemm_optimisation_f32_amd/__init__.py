@@ -20,14 +20,14 @@ import os
 __all__ = ["gemm_f32", "gemm_f16_f32acc", "gemm_batched_f16_f32acc",
            "gemm_f32_ex", "gemm_f16_f32acc_ex", "gemm_batched_f16_f32acc_ex",
            "gemm_bf16_f32acc", "gemm_batched_bf16_f32acc", "gemm_bf16_f32acc_ex", "gemm_batched_bf16_f32acc_ex",
-           "status_string",
+           "gemm_f16_f32acc_noalloc", "status_string",
            "GemmError", "GemmLibraryMissing", "LIB_PATH", "load_library", "EXPORTS"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmi355gemm.so")
 EXPORTS = ("gemm_f32", "gemm_f16_f32acc", "gemm_batched_f16_f32acc",
            "gemm_f32_ex", "gemm_f16_f32acc_ex", "gemm_batched_f16_f32acc_ex",
            "gemm_bf16_f32acc", "gemm_batched_bf16_f32acc", "gemm_bf16_f32acc_ex", "gemm_batched_bf16_f32acc_ex",
-           "gemm_status_string")
+           "gemm_f16_f32acc_noalloc", "gemm_status_string")
 
 _lib = None
 
@@ -73,6 +73,8 @@ def load_library(path: str = LIB_PATH):
         fn = getattr(lib, name)
         fn.argtypes = base.argtypes
         fn.restype = i
+    lib.gemm_f16_f32acc_noalloc.argtypes = lib.gemm_f16_f32acc.argtypes
+    lib.gemm_f16_f32acc_noalloc.restype = i
     lib.gemm_status_string.argtypes = [i]
     lib.gemm_status_string.restype = ctypes.c_char_p
     if path == LIB_PATH:
@@ -152,6 +154,18 @@ def gemm_f16_f32acc(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=None) -
                              _ptr(C, "C", "torch.float32", nc), ldc, _stream(stream))
     if rc != 0:
         raise GemmError(rc, "gemm_f16_f32acc")
+
+
+def gemm_f16_f32acc_noalloc(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=None) -> None:
+    """gemm_f16_f32acc for callers that cannot allocate: its K split keeps its partial tiles in one
+    static buffer per GPU (calls that overlap on one GPU must not be made)."""
+    lib = load_library()
+    na, nb, nc = _needs(M, N, K, alpha, lda, ldb, ldc)
+    rc = lib.gemm_f16_f32acc_noalloc(M, N, K, alpha, _ptr(A, "A", "torch.float16", na), lda,
+                                     _ptr(B, "B", "torch.float16", nb), ldb, beta,
+                                     _ptr(C, "C", "torch.float32", nc), ldc, _stream(stream))
+    if rc != 0:
+        raise GemmError(rc, "gemm_f16_f32acc_noalloc")
 
 
 def gemm_batched_f16_f32acc(M, N, K, alpha, A, lda, strideA, B, ldb, strideB, beta, C, ldc, strideC,

@@ -136,6 +136,53 @@ int run(GemmProblem p, size_t elem_in, hipStream_t stream, Launch launch)
     return GEMM_OK;
 }
 
+// ---- scratch of the entry point that allocates nothing
+//
+// One file-scope array per GPU holds the K split's tile counters and partial
+// tiles for gemm_f16_f32acc_noalloc.  Its size covers every K split the
+// planner makes (at most 128 workgroups of 128 x 128 fp32 partial tiles, see
+// plan16.h), so no call is refused today; the check stays for any plan that
+// would need more.  In host code `noalloc_scratch` names a host-side stand-in:
+// the device address comes from hipGetSymbolAddress, once per device, and only
+// that address is passed to kernels.
+constexpr size_t kNoallocScratchBytes = mi355gemm::kCounterBytes + (size_t)128 * 128 * 128 * sizeof(float);
+__device__ __align__(256) unsigned char noalloc_scratch[kNoallocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_noalloc_mutex;
+void *g_noalloc_ptr[kMaxDevices];
+
+// The device address of this GPU's array (the current device), looked up on
+// the first call on the device.  The array is zero when the library is loaded
+// and every kernel leaves its counters zero; the first call also clears them on
+// its stream unless that stream is being captured into a graph.
+void *noalloc_scratch_setup(hipStream_t stream)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_noalloc_mutex);
+    if (g_noalloc_ptr[dev]) return g_noalloc_ptr[dev];
+    void *ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(noalloc_scratch)) != hipSuccess || ptr == nullptr) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    hipStreamCaptureStatus status = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &status) == hipSuccess && status == hipStreamCaptureStatusNone) {
+        if (hipMemsetAsync(ptr, 0, mi355gemm::kCounterBytes, stream) != hipSuccess) {
+            (void)hipGetLastError();
+            return nullptr;
+        }
+    }
+    g_noalloc_ptr[dev] = ptr;
+    return ptr;
+}
+
+void *noalloc_scratch_get(void *ctx, size_t bytes, hipStream_t)
+{
+    return bytes <= kNoallocScratchBytes ? ctx : nullptr;
+}
+
 GemmProblem make(int tA, int tB, int M, int N, int K, float alpha, const void *A, int lda, long long sA,
                  const void *B, int ldb, long long sB, float beta, float *C, int ldc, long long sC, int batch)
 {
@@ -214,6 +261,21 @@ int gemm_batched_f16_f32acc(int M, int N, int K, float alpha, const uint16_t *A,
                                       batch_count, stream);
 }
 
+int gemm_f16_f32acc_noalloc(int M, int N, int K, float alpha, const uint16_t *A, int lda, const uint16_t *B,
+                            int ldb, float beta, float *C, int ldc, hipStream_t stream)
+{
+    GemmProblem p = make(0, 0, M, N, K, alpha, A, lda, 0, B, ldb, 0, beta, C, ldc, 0, 1);
+    const int rc = check(p, sizeof(uint16_t));
+    if (rc != GEMM_OK) return rc;
+    if (M == 0 || N == 0) return GEMM_OK;
+    if (mi355gemm::gemm16_scratch_bytes(p) > kNoallocScratchBytes) return GEMM_ERR_SCRATCH;
+    void *ptr = noalloc_scratch_setup(stream);
+    if (ptr == nullptr) return GEMM_ERR_LAUNCH;
+    p.scratch.get = noalloc_scratch_get;
+    p.scratch.ctx = ptr;
+    return run(p, sizeof(uint16_t), stream, mi355gemm::launch_hgemm);
+}
+
 int gemm_bf16_f32acc(int M, int N, int K, float alpha, const uint16_t *A, int lda, const uint16_t *B, int ldb,
                      float beta, float *C, int ldc, hipStream_t stream)
 {
@@ -238,6 +300,7 @@ const char *gemm_status_string(int status)
     case GEMM_ERR_ALIGN: return "pointer not aligned to its element size";
     case GEMM_ERR_LAUNCH: return "the HIP runtime refused a kernel launch";
     case GEMM_ERR_OP: return "transpose flag is neither 0 nor 1";
+    case GEMM_ERR_SCRATCH: return "the call needs more scratch than the static buffer of the no-allocation entry point holds";
     default: return "unknown status";
     }
 }

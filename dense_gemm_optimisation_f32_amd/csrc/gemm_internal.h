@@ -41,6 +41,8 @@ hipError_t launch_sgemm(const GemmProblem &p, hipStream_t stream);
 hipError_t launch_hgemm(const GemmProblem &p, hipStream_t stream);
 // bf16-input, fp32-accumulate GEMM on bf16 MFMA (same kernels and preconditions).
 hipError_t launch_bgemm(const GemmProblem &p, hipStream_t stream);
+// Scratch bytes the fp16/bf16 launchers will ask p.scratch for (0: none).
+size_t gemm16_scratch_bytes(const GemmProblem &p);
 // C <- beta*C (or 0 when beta == 0) for the K == 0 / alpha == 0 cases.
 hipError_t launch_scale_c(const GemmProblem &p, hipStream_t stream);
 

@@ -1000,6 +1000,13 @@ hipError_t launch_gemm16(const GemmProblem &q, hipStream_t stream)
     return hipErrorInvalidValue;
 }
 
+size_t gemm16_scratch_bytes(const GemmProblem &q)
+{
+    if (q.M <= 0 || q.N <= 0 || q.batch <= 0 || q.K <= 0 || q.alpha == 0.f) return 0;
+    const Plan16 plan = plan16(planner_view(q), true);
+    return plan.nsplit > 1 ? split_bytes<HgDma128>(q, plan.nsplit) : 0;
+}
+
 hipError_t launch_hgemm(const GemmProblem &q, hipStream_t stream)
 {
     return launch_gemm16<false>(q, stream);

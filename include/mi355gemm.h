@@ -60,7 +60,9 @@ enum {
     GEMM_ERR_NULL = -3,      /* NULL pointer for an operand that the call would read or write */
     GEMM_ERR_LAUNCH = -4,    /* the HIP runtime refused a kernel launch (hipGetLastError) */
     GEMM_ERR_ALIGN = -5,     /* pointer not aligned to its element size */
-    GEMM_ERR_OP = -6         /* transA or transB is neither 0 nor 1 */
+    GEMM_ERR_OP = -6,        /* transA or transB is neither 0 nor 1 */
+    GEMM_ERR_SCRATCH = -7    /* gemm_f16_f32acc_noalloc only: the call needs more scratch than
+                                the library's static buffer holds */
 };
 
 /*
@@ -157,6 +159,25 @@ int gemm_batched_bf16_f32acc_ex(int transA, int transB, int M, int N, int K, flo
                                 const uint16_t *B, int ldb, long long strideB,
                                 float beta, float *C, int ldc, long long strideC,
                                 int batch_count, hipStream_t stream);
+
+/*
+ * gemm_f16_f32acc_noalloc -- gemm_f16_f32acc for callers that cannot allocate
+ * device memory (code under graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  Same arguments, results and status codes, plus
+ * GEMM_ERR_SCRATCH.  Where gemm_f16_f32acc splits a tile's K range over several
+ * workgroups it keeps the partial tiles and counters in scratch that the
+ * library allocates per (device, stream) on first need; this form uses instead
+ * one static device buffer per GPU, 8.25 MiB (256 KiB of tile counters and 128
+ * fp32 partial tiles of 128 x 128), which covers every split the library makes,
+ * and calls no allocating routine.  That buffer is shared by every call of this
+ * entry point on the GPU and keeps the last call's contents: calls that overlap
+ * on one GPU (different streams, or graphs replayed concurrently) race and must
+ * not be made.  A call that would need more scratch returns GEMM_ERR_SCRATCH
+ * and enqueues nothing.
+ */
+int gemm_f16_f32acc_noalloc(int M, int N, int K, float alpha,
+                            const uint16_t *A, int lda, const uint16_t *B, int ldb,
+                            float beta, float *C, int ldc, hipStream_t stream);
 
 /* gemm_status_string -- a static, NUL-terminated description of a status code. */
 const char *gemm_status_string(int status);

@@ -15,7 +15,7 @@ import dense_gemm_optimisation_f32_amd as dg
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "mi355gemm.h")
 
-OK, ESIZE, ELD, ENULL, ELAUNCH, EALIGN, EOP = 0, -1, -2, -3, -4, -5, -6
+OK, ESIZE, ELD, ENULL, ELAUNCH, EALIGN, EOP, ESCRATCH = 0, -1, -2, -3, -4, -5, -6, -7
 FAKE = 0x10000          # a non-NULL, 16-byte aligned address that is never dereferenced
 
 
@@ -44,7 +44,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_status_strings(lib):
-    for code in (OK, ESIZE, ELD, ENULL, EALIGN, ELAUNCH, EOP):
+    for code in (OK, ESIZE, ELD, ENULL, EALIGN, ELAUNCH, EOP, ESCRATCH):
         s = dg.status_string(code)
         assert s and s != "unknown status"
     assert dg.status_string(12345) == "unknown status"
@@ -204,3 +204,13 @@ def test_binding_checks_bf16_dtype():
     with pytest.raises(dg.GemmError) as e:
         dg.gemm_batched_bf16_f32acc_ex(0, 2, 4, 4, 4, 1.0, FAKE, 4, 16, FAKE, 4, 16, 0.0, FAKE, 4, 16, 2, stream=0)
     assert e.value.status == EOP
+
+
+def test_noalloc_entry_point_checks_arguments_first(lib):
+    # the entry point that allocates nothing runs the same checks before any HIP call
+    fn = lib.gemm_f16_f32acc_noalloc
+    assert fn(-1, 4, 4, 1.0, FAKE, 4, FAKE, 4, 0.0, FAKE, 4, None) == ESIZE
+    assert fn(4, 4, 4, 1.0, FAKE, 3, FAKE, 4, 0.0, FAKE, 4, None) == ELD
+    assert fn(4, 4, 4, 1.0, None, 4, FAKE, 4, 0.0, FAKE, 4, None) == ENULL
+    assert fn(4, 4, 4, 1.0, FAKE + 1, 4, FAKE, 4, 0.0, FAKE, 4, None) == EALIGN
+    assert fn(0, 4, 4, 1.0, None, 4, None, 4, 0.0, None, 4, None) == OK   # empty: nothing to do
