@@ -24,7 +24,7 @@ LIB = os.path.join(PKG, "libmi355gemm.so")
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 
-COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
+COMMON = ["-O3", "-std=c++20", "-fPIC", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-I", os.path.join(ROOT, "include"), "-Wall", "-Wno-unused-command-line-argument"]
 

@@ -545,8 +545,8 @@ __global__ __launch_bounds__(Cfg::NT) void hgemm_dma_kernel(HgemmArgs p)
         if (!loader) return;
         const char *a = Ab + (long long)kt * stepA;
         const char *b = Bb + (long long)kt * stepB;
-        const unsigned la = lds0 + slot * Cfg::STAGE_BYTES + lw * Cfg::A_LOADS * 1024;
-        const unsigned lb = lds0 + slot * Cfg::STAGE_BYTES + Cfg::A_BYTES + lw * Cfg::B_LOADS * 1024;
+        const unsigned la = lds0 + slot * Cfg::A_BYTES + lw * Cfg::A_LOADS * 1024;
+        const unsigned lb = lds0 + S * Cfg::A_BYTES + slot * Cfg::B_BYTES + lw * Cfg::B_LOADS * 1024;
 #pragma unroll
         for (int i = 0; i < Cfg::A_LOADS; ++i) dma16(a, offA[i], la + 1024 * i);
 #pragma unroll
@@ -571,7 +571,7 @@ __global__ __launch_bounds__(Cfg::NT) void hgemm_dma_kernel(HgemmArgs p)
                         : frag_offset<false, BM, BK>(wm * Cfg::TM + 32 * x, lane, 0);
 #pragma unroll
     for (int x = 0; x < NFB; ++x)
-        fragB[x] = Cfg::A_BYTES + (B_KC ? frag_offset<true, BN, BK>(wn * Cfg::TN, lane, x)
+        fragB[x] = S * Cfg::A_BYTES + (B_KC ? frag_offset<true, BN, BK>(wn * Cfg::TN, lane, x)
                                         : frag_offset<false, BN, BK>(wn * Cfg::TN + 32 * x, lane, 0));
 
     f32x16 acc[Cfg::FM][Cfg::FN];
@@ -596,14 +596,17 @@ __global__ __launch_bounds__(Cfg::NT) void hgemm_dma_kernel(HgemmArgs p)
         }
     };
     half8 fa[2][Cfg::FM], fb[2][Cfg::FN];
+    // LDS ring layout: the S slots of A, then the S slots of B, so that with the
+    // slot known at compile time every fragment read is a register offset fixed
+    // for the whole loop plus an immediate below 64 KB (slot, block, substep).
     auto read_frags = [&](int slot, int s, half8 *a, half8 *b) {
-        const unsigned base = lds0 + slot * Cfg::STAGE_BYTES;
+        const unsigned base_a = lds0 + slot * Cfg::A_BYTES, base_b = lds0 + slot * Cfg::B_BYTES;
 #pragma unroll
         for (int i = 0; i < Cfg::FM; ++i)
-            a[i] = frag(std::bool_constant<A_KC>{}, std::integral_constant<int, BM>{}, base, fragA, i, s);
+            a[i] = frag(std::bool_constant<A_KC>{}, std::integral_constant<int, BM>{}, base_a, fragA, i, s);
 #pragma unroll
         for (int jj = 0; jj < Cfg::FN; ++jj)
-            b[jj] = frag(std::bool_constant<B_KC>{}, std::integral_constant<int, BN>{}, base, fragB, jj, s);
+            b[jj] = frag(std::bool_constant<B_KC>{}, std::integral_constant<int, BN>{}, base_b, fragB, jj, s);
     };
     auto mfmas = [&](const half8 *a, const half8 *b) {
 #pragma unroll
@@ -637,24 +640,34 @@ __global__ __launch_bounds__(Cfg::NT) void hgemm_dma_kernel(HgemmArgs p)
     // slices at each wait is the same for both halves.
     const bool late = Cfg::STAGGER && uwave >= Cfg::NW / 2;
     static_assert(!Cfg::STAGGER || NS >= 2, "staggered refills need two substeps per slice");
-    auto step = [&](int t, auto pending, auto refill, bool late_refill) {
-        const int slot = t % S;
+    // slot_of(t): the ring slot of slice t, t % S; where the caller knows it at
+    // compile time (the unrolled steady loop below) it passes it as a constant,
+    // so every fragment read of the step addresses LDS with a fixed offset from
+    // registers computed once, instead of adding the slot base per read.
+    auto step_in = [&](int t, auto pending, auto refill, bool late_refill, auto slot_c) {
+        constexpr int SC = decltype(slot_c)::value;   // < 0: not known at compile time
+        const int slot = SC >= 0 ? SC : t % S;
+        const int next = SC >= 0 ? (SC + 1) % S : (t + 1) % S;
+        const int prev = SC >= 0 ? (SC + S - 1) % S : (t - 1 + S) % S;
 #pragma unroll
         for (int sub = 0; sub < NS; ++sub) {
             const int cur = sub & 1, nxt = cur ^ 1;
             if (sub + 1 < NS) {
                 read_frags(slot, sub + 1, fa[nxt], fb[nxt]);
-                if (Cfg::STAGGER && sub == NS - 2 && late && late_refill) issue_slice(t - 1 + S, (t - 1 + S) % S);
+                if (Cfg::STAGGER && sub == NS - 2 && late && late_refill) issue_slice(t - 1 + S, prev);
             } else {
                 wait_vmcnt<LOADS * decltype(pending)::value>();
                 __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's slice-t reads are done
                 lds_barrier();
                 if (decltype(refill)::value && !late) issue_slice(t + S, slot);
-                read_frags((t + 1) % S, 0, fa[nxt], fb[nxt]);
+                read_frags(next, 0, fa[nxt], fb[nxt]);
             }
             mfmas(fa[cur], fb[cur]);
             interleave();
         }
+    };
+    auto step = [&](int t, auto pending, auto refill, bool late_refill) {
+        step_in(t, pending, refill, late_refill, std::integral_constant<int, -1>{});
     };
 
     // Prologue: slices 0..S-1 in flight; slice 0 resident; substep 0 fragments read.
@@ -665,7 +678,21 @@ __global__ __launch_bounds__(Cfg::NT) void hgemm_dma_kernel(HgemmArgs p)
     read_frags(0, 0, fa[0], fb[0]);
 
     // Steady state: slices up to t+S-1 issued, slice t+1 needed.
-    for (int t = 0; t + S < nk; ++t) step(t, std::integral_constant<int, S - 2>{}, std::true_type{}, t >= 1);
+    // (unrolled over the S slots, so each step's slot is a compile-time constant;
+    // not for the 64-row tile, whose four-way unrolled loop measured slower:
+    // 512x4096x4096 25.0 -> 26.2 us)
+    {
+        int t = 0;
+        constexpr bool UNROLL = Cfg::BM >= 128 && !MASK && B_KC == false;
+        for (; UNROLL && t + S - 1 + S < nk; t += S) {
+            [&]<int... I>(std::integer_sequence<int, I...>) {
+                (step_in(t + I, std::integral_constant<int, S - 2>{}, std::true_type{}, t + I >= 1,
+                         std::integral_constant<int, I>{}),
+                 ...);
+            }(std::make_integer_sequence<int, S>{});
+        }
+        for (; t + S < nk; ++t) step(t, std::integral_constant<int, S - 2>{}, std::true_type{}, t >= 1);
+    }
     // Tail: no more slices to issue; the outstanding count drains to zero
     // (with staggered refills, the upper waves still issue their share of the
     // last slice during the first of these steps).
