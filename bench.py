@@ -130,6 +130,9 @@ def extra_configs():
     # larger than the last-level cache used in turn)
     add("batched_hgemm_16x1024^3_b1", "f16", 1024, 1024, 1024, 1.0, 1.0, batch=16)
     add("batched_hgemm_16x1024^3_b1_cold", "f16", 1024, 1024, 1024, 1.0, 1.0, batch=16, cold=True)
+    # few tiles and a long K: the HGEMM splits each tile's K range over workgroups
+    add("hgemm_splitk_512x512x8192", "f16", 512, 512, 8192)
+    add("hgemm_splitk_1024x1024x8192", "f16", 1024, 1024, 8192)
     # one GPU's share of each step shape when 8 GPUs split C by rows
     add("sgemm_row_share_1of8_512x4096x1024", "f32", 512, 4096, 1024)
     add("hgemm_row_share_1of8_512x4096x4096", "f16", 512, 4096, 4096)
@@ -538,13 +541,18 @@ def profile_config(args, dg, si, np, torch, dev, stream):
     torch.cuda.synchronize()
     if args.copy_calibration:
         copy_calibration(torch, dev)
-    for _ in range(args.warmup):
+    # at least --warmup calls and 100 ms of back-to-back calls (the clock leaves its idle state)
+    n, t_end = 0, time.perf_counter() + 0.1
+    while n < args.warmup or time.perf_counter() < t_end:
         run(stream)
+        n += 1
+        if n % 10 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     for _ in range(args.steps):
         run(stream)
     torch.cuda.synchronize()
-    print(f"profiled {args.profile}: {args.steps} calls after {args.warmup}", flush=True)
+    print(f"profiled {args.profile}: {args.steps} calls after {n}", flush=True)
     return 0
 
 
@@ -739,8 +747,10 @@ def write_counters(name: str, csv_paths) -> int:
              else f"configuration {name}")
     lines = [f"# rocprofv3 counters per launch: {title}", "",
              "Commands (one MI355X; each pass is a run of its own):", "", "```", cmds, "```", "",
-             "Mean over the dispatches of each kernel in the runs (the counters are summed over the "
-             "whole device; SQ_LDS_* and SQ_*_CYCLES count in units of four cycles).", ""]
+             "Mean over the dispatches of each kernel in the runs (each run warms the clock with about 100 ms of "
+             "calls first, so most dispatches are those). Counters are summed over the whole device: "
+             "SQ_VALU_MFMA_BUSY_CYCLES over the 1024 SIMDs in cycles, SQ_WAVE_CYCLES and SQ_WAIT_* over the waves "
+             "in units of four cycles, GRBM_GUI_ACTIVE over the 8 XCDs.", ""]
     for j, k in enumerate(kernels):
         lines.append(f"- kernel {j}: `{k}`")
     lines += ["", "| counter | " + " | ".join(f"kernel {j}" for j in range(len(kernels))) + " |",
@@ -752,13 +762,22 @@ def write_counters(name: str, csv_paths) -> int:
         m = mean[k]
         d = sum(durs[k]) / len(durs[k]) / 1e3
         parts = [f"- kernel {j} ({d:.1f} us per profiled launch):"]
+        if m.get("GRBM_GUI_ACTIVE"):
+            # GRBM_GUI_ACTIVE is summed over the 8 XCDs: an eighth of it is the launch's
+            # length in shader-clock cycles, which over the launch's duration is the clock
+            # (for launches of a few tens of microseconds the count also covers the
+            # dispatch's set-up under counter collection, so the clock is given for
+            # long launches only and the busy share below is a lower bound)
+            gpu_cycles = m["GRBM_GUI_ACTIVE"] / 8
+            parts.append(f"{gpu_cycles:.4g} GPU-active cycles" +
+                         (f", i.e. a mean shader clock of {gpu_cycles / d / 1e3:.2f} GHz;" if d >= 50 else ";"))
         if m.get("SQ_INSTS_MFMA"):
             parts.append(f"{m['SQ_VALU_MFMA_BUSY_CYCLES'] / m['SQ_INSTS_MFMA']:.1f} matrix-core cycles "
                          f"per MFMA instruction, {m['SQ_INSTS_MFMA']:.4g} MFMA instructions;")
             if m.get("GRBM_GUI_ACTIVE"):
-                # busy cycles are counted per SIMD summed over the device (256 CUs x 4 SIMDs)
-                parts.append(f"matrix cores busy {100 * m['SQ_VALU_MFMA_BUSY_CYCLES'] / (1024 * m['GRBM_GUI_ACTIVE']):.1f}% "
-                             f"of the GPU-active cycles;")
+                # SQ_VALU_MFMA_BUSY_CYCLES sums the busy cycles of all 1024 SIMDs (256 CUs x 4)
+                parts.append(f"matrix cores busy {100 * m['SQ_VALU_MFMA_BUSY_CYCLES'] / 1024 / gpu_cycles:.1f}% "
+                             f"of the launch's cycles;")
         if m.get("SQ_LDS_IDX_ACTIVE"):
             parts.append(f"LDS bank conflicts {100 * m.get('SQ_LDS_BANK_CONFLICT', 0) / m['SQ_LDS_IDX_ACTIVE']:.2f}% "
                          f"of LDS-active cycles;")
@@ -823,6 +842,10 @@ def write_traffic(name: str, fetch_csv: str, write_csv: str) -> int:
         c = {x["name"]: x for x in extra_configs()}[name]
         kind = "sgemm" if c["kind"] == "f32" else "hgemm"
         targets = [(name, kind, name, config_bytes(c), name)]
+        # the step's two calls are these configurations alone (same kernel, shape and data)
+        step_of = {"sgemm_4096x4096x1024": "sgemm", "hgemm_4096^3": "hgemm"}
+        if name in step_of:
+            targets.append((step_of[name], kind, STEP_WORKLOADS[kind], config_bytes(c), name))
     for key, kind, workload, alg, prof in targets:
         kname, f = mean(fetch, kind)
         _, w = mean(write, kind)
