@@ -305,6 +305,11 @@ def time_calls(fn, torch, stream, warmup=20, reps=30, graph_calls=20, warm_s=0.1
     ts = sorted(a.elapsed_time(b) * 1e-3 for a, b in evs)
     g = torch.cuda.CUDAGraph()
     side = torch.cuda.Stream()
+    # one call on the capture stream first: a K split keeps its scratch per stream
+    # and cannot allocate it during capture, so this makes the graph record the
+    # same plan as the calls timed above
+    fn(side)
+    torch.cuda.synchronize()
     with torch.cuda.graph(g, stream=side):
         for _ in range(graph_calls):
             fn(side)
