@@ -715,6 +715,7 @@ COUNTER_PASSES = (
     "SQ_WAVES SQ_WAVE_CYCLES SQ_BUSY_CYCLES SQ_WAIT_INST_ANY SQ_WAIT_ANY SQ_WAIT_INST_LDS "
     "SQ_ACTIVE_INST_LDS SQ_LDS_ADDR_CONFLICT GRBM_GUI_ACTIVE",
     "TCC_HIT_sum TCC_MISS_sum TCC_EA0_RDREQ_DRAM_sum TCC_EA0_WRREQ_DRAM_sum",
+    "TA_BUSY_avr TA_BUSY_max TA_FLAT_READ_LDS_WAVEFRONTS_sum TD_TD_BUSY_sum TD_TC_STALL_sum GRBM_GUI_ACTIVE",
 )
 
 
@@ -791,6 +792,16 @@ def write_counters(name: str, csv_paths) -> int:
         if m.get("SQ_INSTS_MFMA") and m.get("SQ_INSTS_VALU") is not None:
             parts.append(f"{m['SQ_INSTS_VALU'] / m['SQ_INSTS_MFMA']:.2f} VALU instructions (MFMA included) "
                          f"per MFMA.")
+        if m.get("TA_BUSY_avr") is not None and m.get("GRBM_GUI_ACTIVE"):
+            # TA_TA_BUSY counts busy cycles per texture-addresser instance (one per CU);
+            # a direct-to-LDS load is one TA_FLAT_READ_LDS wavefront of 1 KB
+            gpu_cycles = m["GRBM_GUI_ACTIVE"] / 8
+            parts.append(f"texture addressers busy {100 * m['TA_BUSY_avr'] / gpu_cycles:.1f}% of the launch's "
+                         f"cycles on average ({100 * m.get('TA_BUSY_max', 0) / gpu_cycles:.1f}% at most);")
+            if m.get("TA_FLAT_READ_LDS_WAVEFRONTS_sum"):
+                lds_bytes = m["TA_FLAT_READ_LDS_WAVEFRONTS_sum"] * 1024
+                parts.append(f"{lds_bytes / 2**20:.1f} MiB loaded straight into LDS, "
+                             f"{lds_bytes / 256 / gpu_cycles:.1f} bytes per CU per cycle;")
         if m.get("SQ_WAVE_CYCLES") and m.get("SQ_WAIT_INST_ANY") is not None:
             parts.append(f"waves waiting on an instruction {100 * m['SQ_WAIT_INST_ANY'] / m['SQ_WAVE_CYCLES']:.0f}% "
                          f"of wave cycles.")
