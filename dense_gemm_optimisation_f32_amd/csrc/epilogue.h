@@ -48,4 +48,42 @@ __device__ __forceinline__ void store_row4(float *C, long long ldc, long long ro
     }
 }
 
+// The beta term split from the store, so that a kernel can read C ahead of
+// the stores that use it: four consecutive floats of C at (row, col..col+3),
+// with MASK rows >= M and columns >= N reading as zero (they are never stored).
+template <bool MASK>
+__device__ __forceinline__ f32x4_t load_row4(const float *C, long long ldc, long long row, long long col, int M, int N)
+{
+    f32x4_t c = {0.f, 0.f, 0.f, 0.f};
+    if (MASK && row >= M) return c;
+    const float *src = C + row * ldc + col;
+    if (!MASK || col + 3 < N) return *reinterpret_cast<const f32x4_g *>(src);
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        if (col + e < N) c[e] = src[e];
+    return c;
+}
+
+// C[row][col..col+3] = alpha*acc + beta*c for c read by load_row4: the same
+// fma(beta, c, alpha*acc) as store_row4, so either gives the same bits.
+template <bool MASK>
+__device__ __forceinline__ void store_row4_c(float *C, long long ldc, long long row, long long col, f32x4_t acc,
+                                             f32x4_t c, float alpha, float beta, int M, int N)
+{
+    if (MASK && row >= M) return;
+    float *dst = C + row * ldc + col;
+    f32x4_t v = alpha * acc;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = __builtin_fmaf(beta, c[e], v[e]);
+    if (!MASK || col + 3 < N) {
+        *reinterpret_cast<f32x4_g *>(dst) = v;
+        return;
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        if (col + e >= N) break;
+        dst[e] = v[e];
+    }
+}
+
 }  // namespace mi355gemm

@@ -701,6 +701,23 @@ __global__ __launch_bounds__(Cfg::NT) void hgemm_dma_kernel(HgemmArgs p)
     step(t0, std::integral_constant<int, S - 2>{}, std::false_type{}, t0 >= 1);
     if constexpr (S >= 3) step(t0 + 1, std::integral_constant<int, S - 3>{}, std::false_type{}, false);
     if constexpr (S >= 4) step(t0 + 2, std::integral_constant<int, S - 4>{}, std::false_type{}, false);
+    // With beta != 0 the epilogue reads C one block row ahead of its stores
+    // (below).  Where no global read follows the last slice (no K tail) and
+    // the workgroup is the only one on its tile (no K split), the first block
+    // row's read is issued here, so that it is in flight during the last
+    // slice's MFMAs.
+    const float alpha = p.alpha, beta = p.beta;
+    auto col_of = [&](int jj, int g) -> long long { return n0 + wn * Cfg::TN + 32 * jj + 8 * g + 4 * lk; };
+    f32x4_t cb[2][Cfg::FN * 4];
+    auto read_row = [&](int i, f32x4_t *dst) {
+        const long long row = m0 + wm * Cfg::TM + 32 * i + lr;
+#pragma unroll
+        for (int jj = 0; jj < Cfg::FN; ++jj)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) dst[jj * 4 + g] = load_row4<MASK>(C, ldc, row, col_of(jj, g), p.M, p.N);
+    };
+    const bool early_c = !MASK && !SPLIT && beta != 0.f;
+    if (early_c) read_row(0, cb[0]);
     {   // last slice: everything is resident
         const int slot = (nk - 1) % S;
 #pragma unroll
@@ -819,27 +836,46 @@ __global__ __launch_bounds__(Cfg::NT) void hgemm_dma_kernel(HgemmArgs p)
         }
     }
 
-    const float alpha = p.alpha, beta = p.beta;
-    auto epilogue = [&](auto with_c) {
+    auto quad = [&](int i, int jj, int g) -> f32x4_t {
+        return {acc[i][jj][4 * g], acc[i][jj][4 * g + 1], acc[i][jj][4 * g + 2], acc[i][jj][4 * g + 3]};
+    };
+    if (MASK || beta == 0.f) {
+        // (tiles at the edge of C keep the plain order: their masked reads need
+        // the registers that a read-ahead would take)
+        auto plain = [&](auto with_c) {
+#pragma unroll
+            for (int i = 0; i < Cfg::FM; ++i) {
+                const long long row = m0 + wm * Cfg::TM + 32 * i + lr;
+#pragma unroll
+                for (int jj = 0; jj < Cfg::FN; ++jj)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g)
+                        store_row4<MASK, decltype(with_c)::value>(C, ldc, row, col_of(jj, g), quad(i, jj, g), alpha,
+                                                                  beta, p.M, p.N);
+            }
+        };
+        if (beta != 0.f)
+            plain(std::true_type{});
+        else
+            plain(std::false_type{});
+    } else {
+        // C is read one block row ahead: the reads of block row i+1 are issued
+        // before the stores of block row i, so they are in flight while block
+        // row i is combined and stored, and each wait covers one read latency
+        // instead of one per block row behind the previous stores.
+        if (!early_c) read_row(0, cb[0]);
 #pragma unroll
         for (int i = 0; i < Cfg::FM; ++i) {
+            if (i + 1 < Cfg::FM) read_row(i + 1, cb[(i + 1) & 1]);
             const long long row = m0 + wm * Cfg::TM + 32 * i + lr;
 #pragma unroll
-            for (int jj = 0; jj < Cfg::FN; ++jj) {
+            for (int jj = 0; jj < Cfg::FN; ++jj)
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const long long col = n0 + wn * Cfg::TN + 32 * jj + 8 * g + 4 * lk;
-                    const f32x4_t v = {acc[i][jj][4 * g], acc[i][jj][4 * g + 1], acc[i][jj][4 * g + 2],
-                                       acc[i][jj][4 * g + 3]};
-                    store_row4<MASK, decltype(with_c)::value>(C, ldc, row, col, v, alpha, beta, p.M, p.N);
-                }
-            }
+                for (int g = 0; g < 4; ++g)
+                    store_row4_c<MASK>(C, ldc, row, col_of(jj, g), quad(i, jj, g), cb[i & 1][jj * 4 + g], alpha, beta,
+                                       p.M, p.N);
         }
-    };
-    if (beta != 0.f)
-        epilogue(std::true_type{});
-    else
-        epilogue(std::false_type{});
+    }
 }
 
 using Hg128 = HgCfg<128, 128>;

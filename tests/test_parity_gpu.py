@@ -770,6 +770,30 @@ def test_hgemm_64x128_matches_128x128_bits(M, N, K):
     assert torch.equal(c0, c1)
 
 
+# ------------------------------------------------------------------ beta epilogue on whole tiles
+# Whole tiles of the direct-to-LDS HGEMM kernels read C one block row ahead of
+# their stores (the first block row before the last slice); tiles at the edge of
+# C keep the plain order.  Whole-tile shapes of each tile and storage
+# combination, beta != 0, int4 values: bit-exact against the oracle, so a block
+# row read into the wrong buffer or combined with the wrong accumulators fails.
+@pytest.mark.parametrize("tA,tB", [(False, False)] + OPS)
+@pytest.mark.parametrize("M,N,K,tile", [
+    (4096, 4096, 128, "256x256"),
+    (1536, 1536, 4096, "128x128"),
+    (1024, 1024, 2048, "64x128 (128x128 when A is stored K x M)"),
+])
+def test_hgemm_beta_read_ahead(M, N, K, tile, tA, tB):
+    note(f"beta read-ahead, {tile} tile")
+    run_and_check("f16", M, N, K, 1.0, -0.5, kind_vals="int4", exact=True, sample=48, transA=tA, transB=tB,
+                  seed=83)
+    run_and_check("f16", M, N, K, 1.5, 2.0, sample=32, transA=tA, transB=tB, seed=84)
+
+
+def test_batched_beta_read_ahead_bits():
+    # the batched configuration's 256x256 tiles, beta = 1, int4 values
+    batched_check(1024, 1024, 1024, 16, 1.0, 1.0, kind_vals="int4", exact=True, sample=16, seed=85)
+
+
 # ------------------------------------------------------------------ bfloat16 inputs
 # The bf16 entry points run the HGEMM kernels with the bf16 matrix-core op, so
 # these cases cover each of those kernels once more with bfloat16 inputs.
