@@ -415,6 +415,7 @@ __device__ __forceinline__ int swz_b(int k)
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) half8 lds_half8;
+typedef __attribute__((address_space(3))) f32x4_t lds_f32x4;
 
 __device__ __forceinline__ lds_void *lds_ptr(unsigned byte)
 {
@@ -489,9 +490,10 @@ __device__ __forceinline__ unsigned frag_offset(int first, int lane, int s)
 // columns, the K % BK tail is read straight from global memory after the last
 // slice, and stores outside C are skipped); a 16-byte chunk of an
 // MN-contiguous operand may straddle M or N (see the slice count below).
-template <class Cfg, bool BF, bool TA, bool TB, bool MASK, bool SPLIT>
+template <class Cfg, bool BF, bool TA, bool TB, bool MASK, bool SPLIT, bool CROWS>
 __global__ __launch_bounds__(Cfg::NT) void hgemm_dma_kernel(HgemmArgs p)
 {
+    static_assert(!CROWS || !MASK, "the epilogue by rows is for whole tiles");
     constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, S = Cfg::STAGES;
     constexpr bool A_KC = !TA, B_KC = TB;
     static_assert((A_KC || BM >= 128) && (B_KC || BN >= 128), "MN-contiguous slices need 16 chunks per row");
@@ -701,23 +703,27 @@ __global__ __launch_bounds__(Cfg::NT) void hgemm_dma_kernel(HgemmArgs p)
     step(t0, std::integral_constant<int, S - 2>{}, std::false_type{}, t0 >= 1);
     if constexpr (S >= 3) step(t0 + 1, std::integral_constant<int, S - 3>{}, std::false_type{}, false);
     if constexpr (S >= 4) step(t0 + 2, std::integral_constant<int, S - 4>{}, std::false_type{}, false);
-    // With beta != 0 the epilogue reads C one block row ahead of its stores
-    // (below).  Where no global read follows the last slice (no K tail) and
-    // the workgroup is the only one on its tile (no K split), the first block
-    // row's read is issued here, so that it is in flight during the last
-    // slice's MFMAs.
+    // CROWS (whole tiles, beta != 0): the epilogue runs by rows (below), C read
+    // and written in row segments of the wave tile, one 32-row block row
+    // ahead.  Where the workgroup is the only one on its tile (no K split),
+    // the first block row's read is issued here, so that it is in flight
+    // during the last slice's MFMAs.  In the row layout lane l covers columns
+    // 4*(l % LPR) .. +3 of row (l / LPR) + RPI*q of a block row, q = 0 .. NQ-1.
     const float alpha = p.alpha, beta = p.beta;
     auto col_of = [&](int jj, int g) -> long long { return n0 + wn * Cfg::TN + 32 * jj + 8 * g + 4 * lk; };
-    f32x4_t cb[2][Cfg::FN * 4];
+    constexpr int PITCH = Cfg::TN + 4;   // floats per staged row (the pad spreads 32 rows over the banks)
+    constexpr int LPR = Cfg::TN / 4, RPI = 64 / LPR, NQ = 32 / RPI;
+    static_assert(NQ == Cfg::FN * 4, "a block row holds as many quads in either layout");
+    f32x4_t cb[2][NQ];
     auto read_row = [&](int i, f32x4_t *dst) {
-        const long long row = m0 + wm * Cfg::TM + 32 * i + lr;
 #pragma unroll
-        for (int jj = 0; jj < Cfg::FN; ++jj)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) dst[jj * 4 + g] = load_row4<MASK>(C, ldc, row, col_of(jj, g), p.M, p.N);
+        for (int q = 0; q < NQ; ++q) {
+            const int r = q * RPI + lane / LPR, c = 4 * (lane % LPR);
+            dst[q] = load_row4<MASK>(C, ldc, m0 + wm * Cfg::TM + 32 * i + r, n0 + wn * Cfg::TN + c, p.M, p.N);
+        }
     };
-    const bool early_c = !MASK && !SPLIT && beta != 0.f;
-    if (early_c) read_row(0, cb[0]);
+    constexpr bool early_c = CROWS && !SPLIT;
+    if constexpr (early_c) read_row(0, cb[0]);
     {   // last slice: everything is resident
         const int slot = (nk - 1) % S;
 #pragma unroll
@@ -839,9 +845,11 @@ __global__ __launch_bounds__(Cfg::NT) void hgemm_dma_kernel(HgemmArgs p)
     auto quad = [&](int i, int jj, int g) -> f32x4_t {
         return {acc[i][jj][4 * g], acc[i][jj][4 * g + 1], acc[i][jj][4 * g + 2], acc[i][jj][4 * g + 3]};
     };
-    if (MASK || beta == 0.f) {
-        // (tiles at the edge of C keep the plain order: their masked reads need
-        // the registers that a read-ahead would take)
+    if constexpr (!CROWS) {
+        // Straight from the accumulators (beta == 0, or tiles at the edge of C,
+        // whose masked reads need the registers that a read-ahead would take;
+        // a separate instantiation keeps the beta == 0 kernels free of the
+        // by-rows code and its registers).
         auto plain = [&](auto with_c) {
 #pragma unroll
             for (int i = 0; i < Cfg::FM; ++i) {
@@ -859,21 +867,38 @@ __global__ __launch_bounds__(Cfg::NT) void hgemm_dma_kernel(HgemmArgs p)
         else
             plain(std::false_type{});
     } else {
-        // C is read one block row ahead: the reads of block row i+1 are issued
-        // before the stores of block row i, so they are in flight while block
-        // row i is combined and stored, and each wait covers one read latency
-        // instead of one per block row behind the previous stores.
-        if (!early_c) read_row(0, cb[0]);
+        // By rows.  Straight from the accumulators a 16-byte access covers four
+        // columns of each of 32 rows, 32 bytes per row and cache line; here
+        // each wave passes a block row through a private LDS area (the ring is
+        // free once every wave is past the barrier) and reads C and writes it
+        // back in whole row segments of its tile (TN/4 lanes per row, 128 or
+        // 256 contiguous bytes).  C is read one block row ahead: the reads of
+        // block row i+1 are issued before the stores of block row i, so they
+        // are in flight while block row i is combined and stored, and each
+        // wait covers one read latency instead of one per block row behind the
+        // previous stores (the vector-memory counter counts stores too).
+        if constexpr (!early_c) read_row(0, cb[0]);
+        static_assert(Cfg::NW * 32 * PITCH * 4 <= S * Cfg::STAGE_BYTES, "staging area exceeds the ring");
+        lds_barrier();
+        const unsigned stage = lds0 + wave * 32 * PITCH * 4;
 #pragma unroll
         for (int i = 0; i < Cfg::FM; ++i) {
             if (i + 1 < Cfg::FM) read_row(i + 1, cb[(i + 1) & 1]);
-            const long long row = m0 + wm * Cfg::TM + 32 * i + lr;
 #pragma unroll
             for (int jj = 0; jj < Cfg::FN; ++jj)
 #pragma unroll
                 for (int g = 0; g < 4; ++g)
-                    store_row4_c<MASK>(C, ldc, row, col_of(jj, g), quad(i, jj, g), cb[i & 1][jj * 4 + g], alpha, beta,
-                                       p.M, p.N);
+                    *(lds_f32x4 *)(uintptr_t)(stage + (lr * PITCH + 32 * jj + 8 * g + 4 * lk) * 4) = quad(i, jj, g);
+            // a wave's LDS accesses complete in order; this orders the compiler's too
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+            for (int q = 0; q < NQ; ++q) {
+                const int r = q * RPI + lane / LPR, c = 4 * (lane % LPR);
+                const f32x4_t v = *(const lds_f32x4 *)(uintptr_t)(stage + (r * PITCH + c) * 4);
+                store_row4_c<MASK>(C, ldc, m0 + wm * Cfg::TM + 32 * i + r, n0 + wn * Cfg::TN + c, v, cb[i & 1][q],
+                                   alpha, beta, p.M, p.N);
+            }
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         }
     }
 }
@@ -945,22 +970,22 @@ constexpr bool dma_orientation_ok(bool tA, bool tB)
     return (!tA || Cfg::BM >= 128) && (tB || Cfg::BN >= 128);
 }
 
-template <class Cfg, bool BF, bool MASK, bool SPLIT>
+template <class Cfg, bool BF, bool MASK, bool SPLIT, bool CROWS = false>
 void launch_dma_ops(const HgemmArgs &a, dim3 grid, bool tA, bool tB, hipStream_t stream)
 {
     const dim3 block(Cfg::NT);
     if (!tA && !tB) {
         if constexpr (dma_orientation_ok<Cfg>(false, false))
-            hipLaunchKernelGGL((hgemm_dma_kernel<Cfg, BF, false, false, MASK, SPLIT>), grid, block, 0, stream, a);
+            hipLaunchKernelGGL((hgemm_dma_kernel<Cfg, BF, false, false, MASK, SPLIT, CROWS>), grid, block, 0, stream, a);
     } else if (!tA) {
         if constexpr (dma_orientation_ok<Cfg>(false, true))
-            hipLaunchKernelGGL((hgemm_dma_kernel<Cfg, BF, false, true, MASK, SPLIT>), grid, block, 0, stream, a);
+            hipLaunchKernelGGL((hgemm_dma_kernel<Cfg, BF, false, true, MASK, SPLIT, CROWS>), grid, block, 0, stream, a);
     } else if (!tB) {
         if constexpr (dma_orientation_ok<Cfg>(true, false))
-            hipLaunchKernelGGL((hgemm_dma_kernel<Cfg, BF, true, false, MASK, SPLIT>), grid, block, 0, stream, a);
+            hipLaunchKernelGGL((hgemm_dma_kernel<Cfg, BF, true, false, MASK, SPLIT, CROWS>), grid, block, 0, stream, a);
     } else {
         if constexpr (dma_orientation_ok<Cfg>(true, true))
-            hipLaunchKernelGGL((hgemm_dma_kernel<Cfg, BF, true, true, MASK, SPLIT>), grid, block, 0, stream, a);
+            hipLaunchKernelGGL((hgemm_dma_kernel<Cfg, BF, true, true, MASK, SPLIT, CROWS>), grid, block, 0, stream, a);
     }
 }
 
@@ -1008,15 +1033,20 @@ hipError_t launch_dma(const GemmProblem &q, hipStream_t stream, int nsplit = 1, 
     a.ws_part = ws ? reinterpret_cast<float *>(static_cast<char *>(ws) + kCounterBytes) : nullptr;
     const dim3 grid(a.tiles_m * a.tiles_n * nsplit, 1, q.batch);
     const bool whole = q.M % Cfg::BM == 0 && q.N % Cfg::BN == 0 && q.K % Cfg::BK == 0;
+    const bool by_rows = q.beta != 0.f;   // epilogue by rows for whole tiles that read C
     if (nsplit > 1) {
         if constexpr (Cfg::SPLITS) {
-            if (whole)
+            if (whole && by_rows)
+                launch_dma_ops<Cfg, BF, false, true, true>(a, grid, q.transA, q.transB, stream);
+            else if (whole)
                 launch_dma_ops<Cfg, BF, false, true>(a, grid, q.transA, q.transB, stream);
             else
                 launch_dma_ops<Cfg, BF, true, true>(a, grid, q.transA, q.transB, stream);
         } else {
             return hipErrorInvalidValue;
         }
+    } else if (whole && by_rows) {
+        launch_dma_ops<Cfg, BF, false, false, true>(a, grid, q.transA, q.transB, stream);
     } else if (whole) {
         launch_dma_ops<Cfg, BF, false, false>(a, grid, q.transA, q.transB, stream);
     } else {
