@@ -39,7 +39,9 @@
 //     gfx950 form of the page's asynchronous double buffering): 256x256 tiles
 //     with two slots of 64 k, or 128x128 or 64x128 tiles with four.  Ragged M, N and K
 //     are handled by clamped slice loads, a K tail read from global memory and
-//     masked stores;
+//     masked stores.  Whole tiles with beta != 0 run an instantiation whose
+//     epilogue reads and writes C by rows of the wave tile, one block row
+//     ahead;
 //   * hgemm_mfma_kernel -- everything else: 128x128 (64x64 for small grids)
 //     tiles of four waves in a 2 x 2 grid, read into registers with 16-byte
 //     loads (row starts 4-byte aligned: CDNA's multi-dword global loads need
