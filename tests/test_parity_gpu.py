@@ -787,6 +787,9 @@ def test_hgemm_beta_read_ahead(M, N, K, tile, tA, tB):
     run_and_check("f16", M, N, K, 1.0, -0.5, kind_vals="int4", exact=True, sample=48, transA=tA, transB=tB,
                   seed=83)
     run_and_check("f16", M, N, K, 1.5, 2.0, sample=32, transA=tA, transB=tB, seed=84)
+    # C rows only 4-byte aligned (odd ldc): the row-segment reads and writes take any dword offset
+    run_and_check("f16", M, N, K, -0.75, 1.0, ldc=N + 1, kind_vals="int4", exact=True, sample=24, transA=tA,
+                  transB=tB, seed=86)
 
 
 def test_batched_beta_read_ahead_bits():
