@@ -64,26 +64,19 @@ __device__ __forceinline__ f32x4_t load_row4(const float *C, long long ldc, long
     return c;
 }
 
-// C[row][col..col+3] = alpha*acc + beta*c for c read by load_row4: the same
-// fma(beta, c, alpha*acc) as store_row4, so either gives the same bits.
-template <bool MASK>
-__device__ __forceinline__ void store_row4_c(float *C, long long ldc, long long row, long long col, f32x4_t acc,
-                                             f32x4_t c, float alpha, float beta, int M, int N)
+// For whole tiles that read C ahead of the stores: alpha*acc + beta*c for c
+// read by load_row4, the same fma(beta, c, alpha*acc) as store_row4, so either
+// path gives the same bits; and the 16-byte store of the result.
+__device__ __forceinline__ f32x4_t fma_row4(f32x4_t acc, f32x4_t c, float alpha, float beta)
 {
-    if (MASK && row >= M) return;
-    float *dst = C + row * ldc + col;
     f32x4_t v = alpha * acc;
 #pragma unroll
     for (int e = 0; e < 4; ++e) v[e] = __builtin_fmaf(beta, c[e], v[e]);
-    if (!MASK || col + 3 < N) {
-        *reinterpret_cast<f32x4_g *>(dst) = v;
-        return;
-    }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        if (col + e >= N) break;
-        dst[e] = v[e];
-    }
+    return v;
+}
+__device__ __forceinline__ void store_row4_v(float *C, long long ldc, long long row, long long col, f32x4_t v)
+{
+    *reinterpret_cast<f32x4_g *>(C + row * ldc + col) = v;
 }
 
 }  // namespace mi355gemm

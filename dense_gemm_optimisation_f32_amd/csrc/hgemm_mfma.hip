@@ -716,7 +716,7 @@ __global__ __launch_bounds__(Cfg::NT) void hgemm_dma_kernel(HgemmArgs p)
     constexpr int PITCH = Cfg::TN + 4;   // floats per staged row (the pad spreads 32 rows over the banks)
     constexpr int LPR = Cfg::TN / 4, RPI = 64 / LPR, NQ = 32 / RPI;
     static_assert(NQ == Cfg::FN * 4, "a block row holds as many quads in either layout");
-    f32x4_t cb[2][NQ];
+    f32x4_t cb[NQ];
     auto read_row = [&](int i, f32x4_t *dst) {
 #pragma unroll
         for (int q = 0; q < NQ; ++q) {
@@ -725,7 +725,7 @@ __global__ __launch_bounds__(Cfg::NT) void hgemm_dma_kernel(HgemmArgs p)
         }
     };
     constexpr bool early_c = CROWS && !SPLIT;
-    if constexpr (early_c) read_row(0, cb[0]);
+    if constexpr (early_c) read_row(0, cb);
     {   // last slice: everything is resident
         const int slot = (nk - 1) % S;
 #pragma unroll
@@ -875,17 +875,17 @@ __global__ __launch_bounds__(Cfg::NT) void hgemm_dma_kernel(HgemmArgs p)
         // free once every wave is past the barrier) and reads C and writes it
         // back in whole row segments of its tile (TN/4 lanes per row, 128 or
         // 256 contiguous bytes).  C is read one block row ahead: the reads of
-        // block row i+1 are issued before the stores of block row i, so they
-        // are in flight while block row i is combined and stored, and each
-        // wait covers one read latency instead of one per block row behind the
-        // previous stores (the vector-memory counter counts stores too).
-        if constexpr (!early_c) read_row(0, cb[0]);
+        // block row i+1 are issued as soon as block row i is combined, before
+        // its stores, so they are in flight while block row i is stored and
+        // block row i+1 staged, and each wait covers one read latency instead
+        // of one per block row behind the previous stores (the vector-memory
+        // counter counts stores too).
+        if constexpr (!early_c) read_row(0, cb);
         static_assert(Cfg::NW * 32 * PITCH * 4 <= S * Cfg::STAGE_BYTES, "staging area exceeds the ring");
         lds_barrier();
         const unsigned stage = lds0 + wave * 32 * PITCH * 4;
 #pragma unroll
         for (int i = 0; i < Cfg::FM; ++i) {
-            if (i + 1 < Cfg::FM) read_row(i + 1, cb[(i + 1) & 1]);
 #pragma unroll
             for (int jj = 0; jj < Cfg::FN; ++jj)
 #pragma unroll
@@ -893,14 +893,19 @@ __global__ __launch_bounds__(Cfg::NT) void hgemm_dma_kernel(HgemmArgs p)
                     *(lds_f32x4 *)(uintptr_t)(stage + (lr * PITCH + 32 * jj + 8 * g + 4 * lk) * 4) = quad(i, jj, g);
             // a wave's LDS accesses complete in order; this orders the compiler's too
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            f32x4_t v[NQ];
 #pragma unroll
             for (int q = 0; q < NQ; ++q) {
                 const int r = q * RPI + lane / LPR, c = 4 * (lane % LPR);
-                const f32x4_t v = *(const lds_f32x4 *)(uintptr_t)(stage + (r * PITCH + c) * 4);
-                store_row4_c<MASK>(C, ldc, m0 + wm * Cfg::TM + 32 * i + r, n0 + wn * Cfg::TN + c, v, cb[i & 1][q],
-                                   alpha, beta, p.M, p.N);
+                v[q] = fma_row4(*(const lds_f32x4 *)(uintptr_t)(stage + (r * PITCH + c) * 4), cb[q], alpha, beta);
             }
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            if (i + 1 < Cfg::FM) read_row(i + 1, cb);
+#pragma unroll
+            for (int q = 0; q < NQ; ++q) {
+                const int r = q * RPI + lane / LPR, c = 4 * (lane % LPR);
+                store_row4_v(C, ldc, m0 + wm * Cfg::TM + 32 * i + r, n0 + wn * Cfg::TN + c, v[q]);
+            }
         }
     }
 }
