@@ -776,7 +776,7 @@ def write_counters(name: str, csv_paths) -> int:
             # long launches only and the busy share below is a lower bound)
             gpu_cycles = m["GRBM_GUI_ACTIVE"] / 8
             parts.append(f"{gpu_cycles:.4g} GPU-active cycles" +
-                         (f", i.e. a mean shader clock of {gpu_cycles / d / 1e3:.2f} GHz;" if d >= 50 else ";"))
+                         (f", i.e. a mean shader clock of {gpu_cycles / d / 1e3:.2f} GHz;" if d >= 100 else ";"))
         if m.get("SQ_INSTS_MFMA"):
             parts.append(f"{m['SQ_VALU_MFMA_BUSY_CYCLES'] / m['SQ_INSTS_MFMA']:.1f} matrix-core cycles "
                          f"per MFMA instruction, {m['SQ_INSTS_MFMA']:.4g} MFMA instructions;")
