@@ -795,6 +795,9 @@ def test_hgemm_beta_read_ahead(M, N, K, tile, tA, tB):
 def test_batched_beta_read_ahead_bits():
     # the batched configuration's 256x256 tiles, beta = 1, int4 values
     batched_check(1024, 1024, 1024, 16, 1.0, 1.0, kind_vals="int4", exact=True, sample=16, seed=85)
+    # whole 128x128 tiles of transposed members, beta != 0, bf16 and fp16
+    batched_check(256, 384, 512, 3, 1.5, -0.5, transA=True, transB=True, seed=87)
+    batched_check(256, 384, 512, 3, 1.0, 2.0, kind_vals="int4", exact=True, transA=True, seed=88, fmt="bf16")
 
 
 # ------------------------------------------------------------------ bfloat16 inputs
