@@ -41,7 +41,8 @@
 //     are handled by clamped slice loads, a K tail read from global memory and
 //     masked stores.  Whole tiles with beta != 0 run an instantiation whose
 //     epilogue reads and writes C by rows of the wave tile, one block row
-//     ahead;
+//     ahead (on 256x256 tiles, block row 1 goes straight into the LDS slot
+//     that the K loop has finished with);
 //   * hgemm_mfma_kernel -- everything else: 128x128 (64x64 for small grids)
 //     tiles of four waves in a 2 x 2 grid, read into registers with 16-byte
 //     loads (row starts 4-byte aligned: CDNA's multi-dword global loads need
@@ -726,6 +727,29 @@ __global__ __launch_bounds__(Cfg::NT) void hgemm_dma_kernel(HgemmArgs p)
     };
     constexpr bool early_c = CROWS && !SPLIT;
     if constexpr (early_c) read_row(0, cb);
+    // CDMA: the 256x256 tile (two slots of 64 KB; eight waves, each with four
+    // block rows of 32 x 64 floats, 8 KB apiece).  Slot s splits into eight
+    // 8 KB wave areas: waves 0-3 in its A part, waves 4-7 in its B part.  The
+    // slot of slice nk-2 is free once every wave is past the K loop's last
+    // barrier (in the step on slice nk-2, after every wave's reads of that
+    // slice): C block row 1 of each wave tile is loaded into the wave's area
+    // there now, straight from global memory (eight direct-to-LDS loads, lane
+    // l covering columns 4*(l%16) .. +3 of row 4j + l/16), so that it arrives
+    // during the last slice's MFMAs together with block row 0's register read.
+    constexpr bool CDMA = early_c && S == 2 && Cfg::NW == 8 && Cfg::FM == 4 && Cfg::TN == 64 &&
+                          Cfg::A_BYTES == 8 * 4096 && Cfg::B_BYTES == 8 * 4096;
+    auto wave_area = [&](int slot) -> unsigned {
+        return uwave < 4 ? lds0 + slot * Cfg::A_BYTES + uwave * 8192
+                         : lds0 + S * Cfg::A_BYTES + slot * Cfg::B_BYTES + (uwave - 4) * 8192;
+    };
+    if constexpr (CDMA) {
+        const int uwm = uwave / Cfg::WN, uwn = uwave % Cfg::WN;
+        const unsigned dst = wave_area((nk - 2) % S);
+        const float *row1 = C + (m0 + uwm * Cfg::TM + 32) * ldc + n0 + uwn * Cfg::TN;
+        const unsigned voff = (unsigned)(((lane >> 4) * ldc + 4 * (lane & 15)) * 4);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) dma16(row1 + 4 * j * ldc, voff, dst + 1024 * j);
+    }
     {   // last slice: everything is resident
         const int slot = (nk - 1) % S;
 #pragma unroll
@@ -883,28 +907,87 @@ __global__ __launch_bounds__(Cfg::NT) void hgemm_dma_kernel(HgemmArgs p)
         if constexpr (!early_c) read_row(0, cb);
         static_assert(Cfg::NW * 32 * PITCH * 4 <= S * Cfg::STAGE_BYTES, "staging area exceeds the ring");
         lds_barrier();
-        const unsigned stage = lds0 + wave * 32 * PITCH * 4;
+        if constexpr (CDMA) {
+            // Staging in the wave's area of the last slice's slot: rows of 256
+            // bytes, 16-byte chunk k of row r at chunk k ^ (r % 16), so that the
+            // 16 lanes of a quarter-wave hit 16 different chunks when writing (one
+            // column chunk of 16 rows) and reading back (the 16 chunks of a row).
+            // Order of the four block rows: 0 from registers (read before the last
+            // slice), 1 from LDS, 2 and 3 from registers, each read issued while
+            // the block row before it is stored.
+            const unsigned stage = wave_area((nk - 1) % S), cdat = wave_area((nk - 2) % S);
+            auto stage_row = [&](int i) {
 #pragma unroll
-        for (int i = 0; i < Cfg::FM; ++i) {
+                for (int jj = 0; jj < Cfg::FN; ++jj)
 #pragma unroll
-            for (int jj = 0; jj < Cfg::FN; ++jj)
+                    for (int g = 0; g < 4; ++g) {
+                        const int k = 8 * jj + 2 * g + lk;
+                        *(lds_f32x4 *)(uintptr_t)(stage + lr * 256 + ((k ^ (lr & 15)) * 16)) = quad(i, jj, g);
+                    }
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            };
+            auto staged = [&](int q) -> f32x4_t {
+                const int r = 4 * q + (lane >> 4), c = lane & 15;
+                return *(const lds_f32x4 *)(uintptr_t)(stage + r * 256 + ((c ^ (r & 15)) * 16));
+            };
+            auto store_row = [&](int i, const f32x4_t *v) {
 #pragma unroll
-                for (int g = 0; g < 4; ++g)
-                    *(lds_f32x4 *)(uintptr_t)(stage + (lr * PITCH + 32 * jj + 8 * g + 4 * lk) * 4) = quad(i, jj, g);
-            // a wave's LDS accesses complete in order; this orders the compiler's too
+                for (int q = 0; q < 8; ++q)
+                    store_row4_v(C, ldc, m0 + wm * Cfg::TM + 32 * i + 4 * q + (lane >> 4), n0 + wn * Cfg::TN + 4 * (lane & 15),
+                                 v[q]);
+            };
+            f32x4_t v[8];
+            stage_row(0);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) v[q] = fma_row4(staged(q), cb[q], alpha, beta);
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-            f32x4_t v[NQ];
+            read_row(2, cb);
+            store_row(0, v);
+            // block row 1: its direct-to-LDS loads precede only the 8 reads and the
+            // 8 stores just issued (the count is kept in order, stores included)
+            stage_row(1);
+            wait_vmcnt<16>();
 #pragma unroll
-            for (int q = 0; q < NQ; ++q) {
-                const int r = q * RPI + lane / LPR, c = 4 * (lane % LPR);
-                v[q] = fma_row4(*(const lds_f32x4 *)(uintptr_t)(stage + (r * PITCH + c) * 4), cb[q], alpha, beta);
-            }
+            for (int q = 0; q < 8; ++q)
+                v[q] = fma_row4(staged(q), *(const lds_f32x4 *)(uintptr_t)(cdat + (4 * q + (lane >> 4)) * 256 + (lane & 15) * 16),
+                                alpha, beta);
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-            if (i + 1 < Cfg::FM) read_row(i + 1, cb);
+            store_row(1, v);
+            stage_row(2);
 #pragma unroll
-            for (int q = 0; q < NQ; ++q) {
-                const int r = q * RPI + lane / LPR, c = 4 * (lane % LPR);
-                store_row4_v(C, ldc, m0 + wm * Cfg::TM + 32 * i + r, n0 + wn * Cfg::TN + c, v[q]);
+            for (int q = 0; q < 8; ++q) v[q] = fma_row4(staged(q), cb[q], alpha, beta);
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            read_row(3, cb);
+            store_row(2, v);
+            stage_row(3);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) v[q] = fma_row4(staged(q), cb[q], alpha, beta);
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            store_row(3, v);
+        } else {
+            const unsigned stage = lds0 + wave * 32 * PITCH * 4;
+#pragma unroll
+            for (int i = 0; i < Cfg::FM; ++i) {
+#pragma unroll
+                for (int jj = 0; jj < Cfg::FN; ++jj)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g)
+                        *(lds_f32x4 *)(uintptr_t)(stage + (lr * PITCH + 32 * jj + 8 * g + 4 * lk) * 4) = quad(i, jj, g);
+                // a wave's LDS accesses complete in order; this orders the compiler's too
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                f32x4_t v[NQ];
+#pragma unroll
+                for (int q = 0; q < NQ; ++q) {
+                    const int r = q * RPI + lane / LPR, c = 4 * (lane % LPR);
+                    v[q] = fma_row4(*(const lds_f32x4 *)(uintptr_t)(stage + (r * PITCH + c) * 4), cb[q], alpha, beta);
+                }
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                if (i + 1 < Cfg::FM) read_row(i + 1, cb);
+#pragma unroll
+                for (int q = 0; q < NQ; ++q) {
+                    const int r = q * RPI + lane / LPR, c = 4 * (lane % LPR);
+                    store_row4_v(C, ldc, m0 + wm * Cfg::TM + 32 * i + r, n0 + wn * Cfg::TN + c, v[q]);
+                }
             }
         }
     }

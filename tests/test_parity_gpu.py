@@ -779,6 +779,7 @@ def test_hgemm_64x128_matches_128x128_bits(M, N, K):
 @pytest.mark.parametrize("tA,tB", [(False, False)] + OPS)
 @pytest.mark.parametrize("M,N,K,tile", [
     (4096, 4096, 128, "256x256"),
+    (4096, 4096, 192, "256x256, odd slice count"),
     (1536, 1536, 4096, "128x128"),
     (1024, 1024, 2048, "64x128 (128x128 when A is stored K x M)"),
 ])
@@ -790,6 +791,27 @@ def test_hgemm_beta_read_ahead(M, N, K, tile, tA, tB):
     # C rows only 4-byte aligned (odd ldc): the row-segment reads and writes take any dword offset
     run_and_check("f16", M, N, K, -0.75, 1.0, ldc=N + 1, kind_vals="int4", exact=True, sample=24, transA=tA,
                   transB=tB, seed=86)
+
+
+@pytest.mark.parametrize("tA,tB", [(False, False)] + OPS)
+@pytest.mark.parametrize("K", [128, 192])
+def test_hgemm_256_beta_every_element(K, tA, tB):
+    # Every element of a 4096x4096 C on 256x256 tiles (the block row that goes
+    # through the freed LDS slot included), int4 values: the beta != 0 result
+    # must equal the beta == 0 result plus beta*C exactly (all values are small
+    # integers and halves, so no step rounds).  The beta == 0 path is checked
+    # against the oracle by the other tests.
+    M = N = 4096
+    note(f"256x256 beta every element K={K} transA={int(tA)} transB={int(tB)}")
+    p = si.gemm_problem(M, N, K, in_dtype=np.float16, kind="int4", seed=89, transA=tA, transB=tB)
+    dA, dB, c0 = to_dev(p["A"]), to_dev(p["B"]), to_dev(p["C"])
+    d = torch.empty_like(c0)
+    c = c0.clone()
+    lda, ldb = p["lda"], p["ldb"]
+    dg.gemm_f16_f32acc_ex(int(tA), int(tB), M, N, K, 1.0, dA, lda, dB, ldb, 0.0, d, N)
+    dg.gemm_f16_f32acc_ex(int(tA), int(tB), M, N, K, 1.0, dA, lda, dB, ldb, -0.5, c, N)
+    torch.cuda.synchronize()
+    assert torch.equal(c, d + (-0.5) * c0)
 
 
 def test_batched_beta_read_ahead_bits():
