@@ -793,25 +793,55 @@ def test_hgemm_beta_read_ahead(M, N, K, tile, tA, tB):
                   transB=tB, seed=86)
 
 
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
 @pytest.mark.parametrize("tA,tB", [(False, False)] + OPS)
 @pytest.mark.parametrize("K", [128, 192])
-def test_hgemm_256_beta_every_element(K, tA, tB):
+def test_hgemm_256_beta_every_element(K, tA, tB, fmt):
     # Every element of a 4096x4096 C on 256x256 tiles (the block row that goes
     # through the freed LDS slot included), int4 values: the beta != 0 result
     # must equal the beta == 0 result plus beta*C exactly (all values are small
     # integers and halves, so no step rounds).  The beta == 0 path is checked
     # against the oracle by the other tests.
     M = N = 4096
-    note(f"256x256 beta every element K={K} transA={int(tA)} transB={int(tB)}")
-    p = si.gemm_problem(M, N, K, in_dtype=np.float16, kind="int4", seed=89, transA=tA, transB=tB)
+    note(f"256x256 beta every element {fmt} K={K} transA={int(tA)} transB={int(tB)}")
+    p = si.gemm_problem(M, N, K, in_dtype=IN_DTYPE[fmt], kind="int4", seed=89, transA=tA, transB=tB)
     dA, dB, c0 = to_dev(p["A"]), to_dev(p["B"]), to_dev(p["C"])
     d = torch.empty_like(c0)
     c = c0.clone()
     lda, ldb = p["lda"], p["ldb"]
-    dg.gemm_f16_f32acc_ex(int(tA), int(tB), M, N, K, 1.0, dA, lda, dB, ldb, 0.0, d, N)
-    dg.gemm_f16_f32acc_ex(int(tA), int(tB), M, N, K, 1.0, dA, lda, dB, ldb, -0.5, c, N)
+    fn = dg.gemm_bf16_f32acc_ex if fmt == "bf16" else dg.gemm_f16_f32acc_ex
+    fn(int(tA), int(tB), M, N, K, 1.0, dA, lda, dB, ldb, 0.0, d, N)
+    fn(int(tA), int(tB), M, N, K, 1.0, dA, lda, dB, ldb, -0.5, c, N)
     torch.cuda.synchronize()
     assert torch.equal(c, d + (-0.5) * c0)
+
+
+@pytest.mark.parametrize("nb,M,N,K", [(16, 1024, 1024, 1024), (12, 1024, 1024, 320)])
+def test_batched_256_beta_every_element(nb, M, N, K):
+    # The same on batched 256x256 tiles (member strides with a gap of 64
+    # elements), every element of every member, and the gaps left untouched
+    note(f"batched 256x256 beta every element batch={nb} M={M} N={N} K={K}")
+    probs = [si.gemm_problem(M, N, K, in_dtype=np.float16, kind="int4", seed=91, batch=b) for b in range(nb)]
+    sA, sB, sC = M * K + 64, K * N + 64, M * N + 64
+    A = np.zeros(sA * nb, np.float16)
+    B = np.zeros(sB * nb, np.float16)
+    C = np.zeros(sC * nb, np.float32)
+    for b, q in enumerate(probs):
+        A[b * sA: b * sA + M * K] = q["A"]
+        B[b * sB: b * sB + K * N] = q["B"]
+        C[b * sC: b * sC + M * N] = q["C"]
+    dA, dB, c0 = to_dev(A), to_dev(B), to_dev(C)
+    d = torch.zeros_like(c0)
+    c = c0.clone()
+    dg.gemm_batched_f16_f32acc(M, N, K, 1.0, dA, K, sA, dB, N, sB, 0.0, d, N, sC, nb)
+    dg.gemm_batched_f16_f32acc(M, N, K, 1.0, dA, K, sA, dB, N, sB, 2.0, c, N, sC, nb)
+    torch.cuda.synchronize()
+    for b in range(nb):
+        got = c[b * sC: b * sC + M * N]
+        want = d[b * sC: b * sC + M * N] + 2.0 * c0[b * sC: b * sC + M * N]
+        assert torch.equal(got, want), f"member {b}"
+        # the gaps between members are never written
+        assert torch.equal(c[b * sC + M * N: (b + 1) * sC], c0[b * sC + M * N: (b + 1) * sC])
 
 
 def test_batched_beta_read_ahead_bits():

@@ -54,6 +54,10 @@ def planner(tmp_path_factory):
     # the step's HGEMM and the batched configuration: 256x256 tiles, one round
     ((4096, 4096, 4096), ("dma256", 1)),
     ((1024, 1024, 1024, 16), ("dma256", 1)),
+    # the 256x256 tiles of the beta epilogue tests: two or three slices, batched
+    ((4096, 4096, 128), ("dma256", 1)),
+    ((4096, 4096, 192, 1, 1, 1), ("dma256", 1)),
+    ((1024, 1024, 320, 12), ("dma256", 1)),
     # HGEMM 2048^3: 256 tiles of 128^2 fill the CUs; no split
     ((2048, 2048, 2048), ("dma128", 1)),
     # one GPU's row share under an 8-way split: 64x128 tiles
