@@ -358,7 +358,12 @@ def main() -> int:
     ap.add_argument("--write-counters", nargs="+", metavar=("NAME", "CSV"),
                     help="turn rocprofv3 counter_collection.csv files of a --profile NAME run into "
                          "profiles/counters_NAME.md; uses no GPU")
+    ap.add_argument("--write-resources", action="store_true",
+                    help="write the compiler's register, scratch, LDS and occupancy figures of the "
+                         "profiled kernels to profiles/resources.md (runs hipcc; uses no GPU)")
     args = ap.parse_args()
+    if args.write_resources:
+        return write_resources()
     if args.write_traffic:
         return write_traffic(*args.write_traffic)
     if args.write_counters:
@@ -808,6 +813,71 @@ def write_counters(name: str, csv_paths) -> int:
         lines.append(" ".join(parts))
     fname = ("counters_sgemm4096x4096x1024_hgemm4096cube.md" if name == "step" else f"counters_{_slug(name)}.md")
     path = os.path.join(ROOT, "profiles", fname)
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(path)
+    return 0
+
+
+def write_resources() -> int:
+    """The compiler's resource usage (hipcc kernel-resource-usage remarks) of the kernels
+    that the committed counter summaries profile, and a summary over every kernel
+    instantiation, as profiles/resources.md."""
+    import glob
+
+    from dense_gemm_optimisation_f32_amd import build
+
+    recs = build.resource_usage()
+    by_name = {_short(r["kernel"]): r for r in recs}
+    # the kernels of each profiled configuration, as the counter summaries name them
+    used = {}
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "counters_*.md"))):
+        cfg = os.path.basename(path)[len("counters_"):-3]
+        for line in open(path):
+            m = re.match(r"- kernel \d+: `(.+)`$", line.strip())
+            if m:
+                used.setdefault(m.group(1).split("<mi355gemm::")[0], []).append(cfg)
+    lds_cu = 160 * 1024
+
+    def row(name, cfgs):
+        r = by_name.get(name)
+        if r is None:
+            return f"| `{name}` | {', '.join(cfgs)} | not found in the sources | | | | | | |"
+        lds = int(r.get("LDS Size [bytes/block]", 0))
+        wg_cu = lds_cu // lds if lds else "-"
+        return (f"| `{name}` | {', '.join(cfgs)} | {r['VGPRs']} | {r['AGPRs']} | {r['TotalSGPRs']} | "
+                f"{r['ScratchSize [bytes/lane]']} | {r['VGPRs Spill']} / {r['SGPRs Spill']} | "
+                f"{lds // 1024} KiB ({wg_cu}) | {r['Occupancy [waves/SIMD]']} |")
+
+    lines = ["# Compiler resource usage of the profiled kernels", "",
+             "Command (hipcc's kernel-resource-usage remarks on the committed sources; no GPU):", "",
+             "```", "python3 $R/bench.py --write-resources   # R = repository root", "```", "",
+             "Per kernel: architectural VGPRs and accumulation VGPRs (AGPRs) per lane, SGPRs, scratch "
+             "bytes per lane, spilled VGPRs / SGPRs, LDS per work-group (in brackets the work-groups "
+             "that fit in a CU's 160 KiB), and the waves per SIMD the registers allow (the compiler's "
+             "occupancy figure). The configurations are those of profiles/counters_*.md that launch the "
+             "kernel.", "",
+             "| kernel | profiled in | VGPRs | AGPRs | SGPRs | scratch (B/lane) | spills V / S | LDS per WG | "
+             "waves per SIMD |", "|---|---|---|---|---|---|---|---|---|"]
+    for name in sorted(used):
+        lines.append(row(name, sorted(set(used[name]))))
+    lines += ["", "Every kernel instantiation in the sources:", "",
+              "| source | kernels | max VGPRs | max AGPRs | with scratch | with VGPR spills | with SGPR spills |",
+              "|---|---|---|---|---|---|---|"]
+    for src in sorted({r["source"] for r in recs}):
+        rs = [r for r in recs if r["source"] == src]
+        lines.append(f"| {src} | {len(rs)} | {max(int(r['VGPRs']) for r in rs)} | "
+                     f"{max(int(r['AGPRs']) for r in rs)} | "
+                     f"{sum(int(r['ScratchSize [bytes/lane]']) > 0 for r in rs)} | "
+                     f"{sum(int(r['VGPRs Spill']) > 0 for r in rs)} | {sum(int(r['SGPRs Spill']) > 0 for r in rs)} |")
+    spilled = [r for r in recs if int(r["VGPRs Spill"]) > 0 or int(r["SGPRs Spill"]) > 0
+               or int(r["ScratchSize [bytes/lane]"]) > 0]
+    if spilled:
+        lines += ["", "Kernels with spills or scratch:", ""]
+        for r in spilled:
+            lines.append(f"- `{_short(r['kernel'])}`: VGPR spills {r['VGPRs Spill']}, SGPR spills "
+                         f"{r['SGPRs Spill']}, scratch {r['ScratchSize [bytes/lane]']} B/lane")
+    path = os.path.join(ROOT, "profiles", "resources.md")
     with open(path, "w") as f:
         f.write("\n".join(lines) + "\n")
     print(path)

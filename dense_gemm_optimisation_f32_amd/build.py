@@ -33,6 +33,41 @@ def sources() -> list[str]:
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
 
 
+def resource_usage() -> list[dict]:
+    """The compiler's resource usage of every kernel in the HIP sources, from hipcc's
+    kernel-resource-usage remarks (device code only, nothing written): per kernel its
+    demangled name and the remark fields as printed (VGPRs, AGPRs, TotalSGPRs,
+    "ScratchSize [bytes/lane]", "Occupancy [waves/SIMD]", "VGPRs Spill", "SGPRs Spill",
+    "LDS Size [bytes/block]")."""
+    import re
+
+    recs = []
+    for src in sorted(glob.glob(os.path.join(CSRC, "*.hip"))):
+        cmd = [HIPCC, *COMMON, "--cuda-device-only", "-Rpass-analysis=kernel-resource-usage", "-c", src,
+               "-o", os.devnull]
+        out = subprocess.run(cmd, capture_output=True, text=True)
+        if out.returncode != 0:
+            raise RuntimeError(f"hipcc failed on {src}:\n{out.stderr[-2000:]}")
+        cur = None
+        for line in out.stderr.splitlines():
+            m = re.search(r"remark: Function Name: (\S+)", line)
+            if m:
+                cur = {"symbol": m.group(1), "source": os.path.basename(src)}
+                recs.append(cur)
+                continue
+            m = re.search(r"remark:\s+(.+?): (\S+) \[-Rpass-analysis", line)
+            if m and cur is not None:
+                cur[m.group(1).strip()] = m.group(2)
+    filt = shutil.which("c++filt") or shutil.which("llvm-cxxfilt")
+    names = [r["symbol"] for r in recs]
+    if filt:
+        names = subprocess.run([filt], input="\n".join(names), capture_output=True, text=True,
+                               check=True).stdout.splitlines()
+    for r, n in zip(recs, names):
+        r["kernel"] = n
+    return recs
+
+
 def build(verbose: bool = False, extra: list[str] | None = None) -> str:
     """Compile every source and link the shared library; returns its path."""
     os.makedirs(BUILD_DIR, exist_ok=True)
